@@ -1,0 +1,486 @@
+"""Pins of the CPU oracle to things other than itself.
+
+Each ``pin_*`` function checks one part of the oracle against what the pages
+print, a closed form, a library routine, or brute force; the test functions
+call them, and ``test_planted_mistakes_are_caught`` plants plausible mistakes
+in the oracle (on the CPU) and checks that some pin fails for each.
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.moe_oracle as O
+from tests import _brute as B
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _close_at(printed, value, decimals):
+    """``value`` rounds to ``printed`` at the page's printed precision."""
+    return abs(value - printed) <= 0.5 * 10 ** (-decimals) + 1e-12
+
+
+# ---------------------------------------------------------------------------
+# pins
+# ---------------------------------------------------------------------------
+
+def pin_router_worked_example_skillsuites():
+    g = _golden("router_worked_example_skillsuites.json")
+    logits = np.array([g["logits"]])
+    scores = O.selection_scores(logits, "softmax")
+    idx = O.top_k_select(scores, g["top_k"])
+    assert [int(e) + 1 for e in idx[0]] == g["selected_1based"]
+    gates = O.gate_weights(logits, idx, "softmax")[0]
+    for p, v in zip(g["gates"], gates):
+        assert _close_at(p, v, g["gates_decimals"]), (p, v)
+    assert abs(gates.sum() - 1.0) < 1e-12
+    # the exponentials the page prints
+    for p, e in zip(g["exp_selected"], idx[0]):
+        assert _close_at(p, math.exp(g["logits"][e]), g["exp_decimals"])
+    # softmax over all eight (the contrast the page draws)
+    full = np.exp(logits[0] - logits[0].max())
+    full /= full.sum()
+    sel = full[idx[0]]
+    for p, v in zip(g["full_softmax_selected"], sel):
+        assert _close_at(p, v, g["full_softmax_decimals"]), (p, v)
+    assert _close_at(g["full_softmax_sum"], sel.sum(), g["full_softmax_decimals"])
+
+
+def _page12_logits(g):
+    total = g["exp_total"]
+    p3, p6 = g["probabilities"]
+    l = np.full(8, math.log((total - total * p3 - total * p6) / 6.0))
+    l[2] = math.log(p3 * total)
+    l[5] = math.log(p6 * total)
+    return l
+
+
+def pin_router_worked_example_ai_infra():
+    g = _golden("router_worked_example_ai_infra_part12.json")
+    logits = _page12_logits(g)[None, :]
+    assert _close_at(g["exp_total"], np.exp(logits).sum(), g["exp_total_decimals"])
+    idx = O.top_k_select(O.selection_scores(logits, "softmax"), g["top_k"])
+    assert [int(e) + 1 for e in idx[0]] == g["selected_1based"]
+    p = np.exp(logits[0]) / np.exp(logits[0]).sum()
+    for pr, v in zip(g["probabilities"], p[idx[0]]):
+        assert _close_at(pr, v, g["probabilities_decimals"])
+    assert _close_at(g["probability_sum"], p[idx[0]].sum(), g["probabilities_decimals"])
+    gates = O.gate_weights(logits, idx, "softmax")[0]
+    for pr, v in zip(g["mixing_weights"], gates):
+        assert _close_at(pr, v, g["mixing_weights_decimals"]), (pr, v)
+    # combine: the layer output is the gate-weighted sum of the two expert
+    # vectors; with the printed 2-decimal weights the result may differ by at
+    # most 0.005 * (|a| + |b|) per element.
+    e3 = np.array(g["expert_outputs"]["E3"])
+    e6 = np.array(g["expert_outputs"]["E6"])
+    y = np.stack([e3, e6])                     # rows in slot order
+    out = O.combine(y, gates[None, :], np.array([[0, 1]]))[0]
+    printed = g["mixing_weights"][0] * e3 + g["mixing_weights"][1] * e6
+    assert np.all(np.abs(out - printed) <= 0.005 * (np.abs(e3) + np.abs(e6)) + 1e-12)
+
+
+def pin_softmax_placement_equivalence(seed=0):
+    """Softmax over the selected logits == softmax over all, keep top-k,
+    renormalise (Chapter 19, 19.3.2)."""
+    rng = np.random.default_rng(seed)
+    for N, k in ((8, 2), (16, 4), (256, 8)):
+        logits = rng.normal(0, 2, size=(64, N))
+        idx = O.top_k_select(O.selection_scores(logits, "softmax"), k)
+        g = O.gate_weights(logits, idx, "softmax")
+        p = np.exp(logits - logits.max(axis=1, keepdims=True))
+        p /= p.sum(axis=1, keepdims=True)
+        ps = np.take_along_axis(p, idx, axis=1)
+        ref = ps / ps.sum(axis=1, keepdims=True)
+        assert np.max(np.abs(g - ref) / ref) <= 1e-12
+        # selected probabilities are the k largest
+        kth = np.sort(p, axis=1)[:, -k]
+        assert np.all(ps.min(axis=1) >= kth - 1e-15)
+
+
+def pin_brute_force_routing(seed=1):
+    rng = np.random.default_rng(seed)
+    for route in ("softmax", "sigmoid"):
+        for N, k in ((4, 2), (6, 3), (8, 2), (5, 5), (7, 1)):
+            logits = rng.normal(0, 1.5, size=(12, N))
+            logits[0, :] = 0.25                       # exact ties
+            logits[1, 1] = logits[1, 3]               # a pair tie
+            bias = rng.uniform(-0.1, 0.1, size=N) if route == "sigmoid" else None
+            sc = O.selection_scores(logits, route, bias)
+            idx = O.top_k_select(sc, k)
+            g = O.gate_weights(logits, idx, route)
+            for t in range(logits.shape[0]):
+                row = [float(v) for v in logits[t]]
+                if route == "softmax":
+                    sel, gb = B.route_softmax_all_renorm(row, k)
+                else:
+                    sel, gb = B.route_sigmoid_bias(row, k, [float(b) for b in bias])
+                assert list(idx[t]) == sel, (route, N, k, t, idx[t], sel)
+                assert np.allclose(g[t], gb, rtol=1e-12, atol=1e-15)
+
+
+def pin_sigmoid_invariants(seed=2):
+    rng = np.random.default_rng(seed)
+    T, N, k = 32, 16, 4
+    logits = rng.normal(0, 1, size=(T, N))
+    # (1) gates sum to one
+    bias = rng.uniform(-0.1, 0.1, N)
+    idx = O.top_k_select(O.selection_scores(logits, "sigmoid", bias), k)
+    g = O.gate_weights(logits, idx, "sigmoid")
+    assert np.allclose(g.sum(axis=1), 1.0, atol=1e-14)
+    # (2) the bias moves selection, never the weights: a bias that keeps the
+    # selection keeps the gates bit for bit
+    idx0 = O.top_k_select(O.selection_scores(logits, "sigmoid", None), k)
+    tiny = np.full(N, 1e-30)
+    idx1 = O.top_k_select(O.selection_scores(logits, "sigmoid", tiny), k)
+    assert np.array_equal(idx0, idx1)
+    g0 = O.gate_weights(logits, idx0, "sigmoid")
+    g1 = O.gate_weights(logits, idx1, "sigmoid")
+    assert np.array_equal(g0, g1)
+    # a big bias on expert 0 forces it in; its weight is its unbiased affinity
+    big = np.zeros(N)
+    big[0] = 10.0
+    idx2 = O.top_k_select(O.selection_scores(logits, "sigmoid", big), k)
+    assert np.all(idx2[:, 0] == 0)
+    g2 = O.gate_weights(logits, idx2, "sigmoid")
+    a = 1.0 / (1.0 + np.exp(-logits))
+    asel = np.take_along_axis(a, idx2, axis=1)
+    assert np.allclose(g2, asel / asel.sum(axis=1, keepdims=True), rtol=1e-13)
+    # (3) equal logits, zero bias -> uniform 1/k on the k lowest indices
+    eq = np.zeros((3, N))
+    idx3 = O.top_k_select(O.selection_scores(eq, "sigmoid", None), k)
+    assert np.array_equal(idx3, np.tile(np.arange(k), (3, 1)))
+    assert np.allclose(O.gate_weights(eq, idx3, "sigmoid"), 1.0 / k, atol=1e-15)
+    # (4) k = N, zero bias -> sigmoid / sum of sigmoids
+    idx4 = O.top_k_select(O.selection_scores(logits, "sigmoid", None), N)
+    g4 = O.gate_weights(logits, idx4, "sigmoid")
+    full = a / a.sum(axis=1, keepdims=True)
+    assert np.allclose(g4, np.take_along_axis(full, idx4, axis=1), rtol=1e-13)
+
+
+def pin_sigmoid_function():
+    z = np.array([-800.0, -30.0, -1.0, 0.0, 1.0, 30.0, 800.0])
+    s = O.sigmoid(z)
+    ref = [B.sig(float(v)) for v in z]
+    assert np.allclose(s, ref, rtol=1e-15, atol=0)
+    assert s[3] == 0.5 and np.all(np.isfinite(s))
+
+
+def pin_router_logits_brute(seed=3):
+    rng = np.random.default_rng(seed)
+    x = rng.normal(size=(5, 7))
+    w = rng.normal(size=(7, 4))
+    off = rng.normal(size=4)
+    got = O.router_logits(x, w, off)
+    ref = B.matvec_rows(x.tolist(), w.tolist())
+    ref = [[v + off[e] for e, v in enumerate(row)] for row in ref]
+    assert np.allclose(got, ref, rtol=1e-13, atol=1e-14)
+
+
+def pin_permutation(seed=4):
+    rng = np.random.default_rng(seed)
+    for T, N, k in ((1, 4, 2), (37, 8, 2), (64, 16, 4), (100, 256, 8), (5, 5, 5)):
+        idx = np.stack([rng.permutation(N)[:k] for _ in range(T)])
+        p = O.permute_assignments(idx, N)
+        assert p.counts.sum() == T * k
+        assert np.array_equal(p.counts, [sum(int(v == e) for v in idx.reshape(-1)) for e in range(N)])
+        assert p.offsets[0] == 0 and p.offsets[-1] == T * k
+        assert np.all(np.diff(p.offsets) == p.counts)
+        # bijection
+        assert np.array_equal(np.sort(p.inv_perm.reshape(-1)), np.arange(T * k))
+        # brute force: Python sorted() of (expert, token, slot)
+        keys = sorted((int(idx[t, i]), t, i) for t in range(T) for i in range(k))
+        assert [t for _, t, _ in keys] == list(p.perm_token)
+        assert [i for _, _, i in keys] == list(p.perm_slot)
+        for r, (e, t, i) in enumerate(keys):
+            assert p.inv_perm[t, i] == r
+            assert p.offsets[e] <= r < p.offsets[e + 1]
+    # empty experts are allowed
+    idx = np.zeros((10, 1), dtype=np.int64)
+    p = O.permute_assignments(idx, 3)
+    assert list(p.counts) == [10, 0, 0] and list(p.offsets) == [0, 10, 10, 10]
+
+
+def _tiny_layer(rng, T=4, d=8, N=4, k=2, d_ff=6, shared=False):
+    x = rng.normal(size=(T, d))
+    w_r = rng.normal(size=(d, N)) / math.sqrt(d)
+    experts = [(rng.normal(size=(d_ff, d)) / math.sqrt(d), rng.normal(size=(d_ff, d)) / math.sqrt(d),
+                rng.normal(size=(d, d_ff)) / math.sqrt(d_ff)) for _ in range(N)]
+    sh = None
+    if shared:
+        sh = (rng.normal(size=(d_ff, d)), rng.normal(size=(d_ff, d)), rng.normal(size=(d, d_ff)))
+    return x, w_r, experts, sh
+
+
+def pin_layer_brute_force(seed=5):
+    rng = np.random.default_rng(seed)
+    for route, shared in (("softmax", False), ("sigmoid", True), ("sigmoid", False)):
+        x, w_r, experts, sh = _tiny_layer(rng, shared=shared)
+        bias = rng.uniform(-0.1, 0.1, size=4) if route == "sigmoid" else None
+        off = rng.normal(size=4) * 0.3
+        out, _, _ = O.moe_forward(x, w_r, experts, 2, route, logit_offset=off,
+                                  select_bias=bias, shared=sh)
+        tolist = lambda m: np.asarray(m).tolist()
+        ref = B.moe_layer(tolist(x), tolist(w_r),
+                          [tuple(tolist(m) for m in ex) for ex in experts], 2, route,
+                          None if bias is None else tolist(bias),
+                          None if sh is None else tuple(tolist(m) for m in sh),
+                          offset=tolist(off))
+        assert np.allclose(out, ref, rtol=1e-10, atol=1e-12), (route, shared)
+
+
+def _dense_swiglu_torch(x, wg, wu, wd):
+    X = torch.from_numpy(np.asarray(x, dtype=np.float64))
+    g = X @ torch.from_numpy(wg).T
+    u = X @ torch.from_numpy(wu).T
+    return (torch.nn.functional.silu(g) * u @ torch.from_numpy(wd).T).numpy()
+
+
+def pin_identical_experts_equal_dense(seed=6):
+    """With every expert identical and gates summing to 1, the layer is the
+    dense FFN ("same scale a dense FFN would have produced"); checked against
+    torch's float64 silu + matmul at k = N and k < N, with a shared expert."""
+    rng = np.random.default_rng(seed)
+    T, d, d_ff = 24, 32, 48
+    x = rng.normal(size=(T, d))
+    W = (rng.normal(size=(d_ff, d)) / math.sqrt(d), rng.normal(size=(d_ff, d)) / math.sqrt(d),
+         rng.normal(size=(d, d_ff)) / math.sqrt(d_ff))
+    S = (rng.normal(size=(d_ff, d)) / math.sqrt(d), rng.normal(size=(d_ff, d)) / math.sqrt(d),
+         rng.normal(size=(d, d_ff)) / math.sqrt(d_ff))
+    dense = _dense_swiglu_torch(x, *W)
+    dense_s = _dense_swiglu_torch(x, *S)
+    for route in ("softmax", "sigmoid"):
+        for N, k in ((8, 8), (8, 2), (16, 5)):
+            w_r = rng.normal(size=(d, N))
+            bias = rng.uniform(-0.1, 0.1, N) if route == "sigmoid" else None
+            out, _, _ = O.moe_forward(x, w_r, [W] * N, k, route, select_bias=bias)
+            assert np.allclose(out, dense, rtol=1e-12, atol=1e-12)
+            out2, _, _ = O.moe_forward(x, w_r, [W] * N, k, route, select_bias=bias, shared=S)
+            assert np.allclose(out2, dense + dense_s, rtol=1e-12, atol=1e-12)
+
+
+def pin_distinct_experts_k_equals_n(seed=7):
+    """k = N with distinct experts: out = sum_e softmax(s)_e * FFN_e(x) over
+    all experts (no selection left), against torch float64."""
+    rng = np.random.default_rng(seed)
+    T, d, d_ff, N = 10, 16, 24, 4
+    x, w_r, experts, _ = _tiny_layer(rng, T, d, N, N, d_ff)
+    out, _, _ = O.moe_forward(x, w_r, experts, N, "softmax")
+    s = torch.from_numpy(x @ w_r)
+    p = torch.softmax(s, dim=1).numpy()
+    ref = sum(p[:, e:e + 1] * _dense_swiglu_torch(x, *experts[e]) for e in range(N))
+    assert np.allclose(out, ref, rtol=1e-12, atol=1e-12)
+
+
+def pin_token_independence_and_relabel(seed=8):
+    rng = np.random.default_rng(seed)
+    x, w_r, experts, sh = _tiny_layer(rng, T=16, d=12, N=6, k=3, d_ff=10, shared=True)
+    out, _, _ = O.moe_forward(x, w_r, experts, 3, "softmax", shared=sh)
+    pr = rng.permutation(16)
+    out_p, _, _ = O.moe_forward(x[pr], w_r, experts, 3, "softmax", shared=sh)
+    assert np.allclose(out_p, out[pr], rtol=1e-13, atol=1e-13)
+    pe = rng.permutation(6)
+    out_e, _, _ = O.moe_forward(x, w_r[:, pe], [experts[e] for e in pe], 3, "softmax", shared=sh)
+    assert np.allclose(out_e, out, rtol=1e-13, atol=1e-13)
+
+
+def pin_bf16_decoder():
+    codes = np.arange(65536, dtype=np.uint16)
+    got = O.bf16_bits_to_f64(codes)
+    ref = torch.from_numpy(codes.view(np.int16)).view(torch.bfloat16).double().numpy()
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    m = ~np.isnan(ref)
+    assert np.array_equal(got[m], ref[m])
+
+
+def pin_e4m3_decoder():
+    codes = np.arange(256, dtype=np.uint8)
+    got = O.e4m3_bits_to_f64(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).double().numpy()
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    m = ~np.isnan(ref)
+    assert np.array_equal(got[m], ref[m])
+    assert np.nanmax(got) == 448.0 and int(np.isnan(got).sum()) == 2
+
+
+def pin_fp8_block_dequant(seed=9):
+    rng = np.random.default_rng(seed)
+    R, C = 130, 260                              # ragged last blocks
+    q = rng.integers(0, 256, size=(R, C), dtype=np.uint8)
+    q[(q & 0x7F) == 0x7F] = 0x38                 # no NaN codes
+    sc = rng.uniform(0.5, 2.0, size=(2, 3)).astype(np.float32)
+    w = O.dequant_fp8_block(q, sc)
+    dec = torch.from_numpy(q).view(torch.float8_e4m3fn).double().numpy()
+    for r in (0, 1, 127, 128, 129):
+        for c in (0, 127, 128, 255, 256, 259):
+            assert w[r, c] == dec[r, c] * float(sc[r // 128, c // 128])
+    assert w[5, 5] == dec[5, 5] * float(sc[0, 0])
+    # code 0x38 is exactly 1.0
+    q1 = np.full((128, 128), 0x38, dtype=np.uint8)
+    assert np.all(O.dequant_fp8_block(q1, np.array([[3.0]], dtype=np.float32)) == 3.0)
+
+
+def pin_experts_touched():
+    g = _golden("experts_touched.json")
+    t = g["table_8_top2"]
+    for B_, read, pct in t["rows"]:
+        v = O.expected_experts_touched(t["n_experts"], t["top_k"], B_)
+        assert _close_at(read, v, t["decimals"]), (B_, read, v)
+        assert abs(100 * v / t["n_experts"] - pct) <= 0.5 + 1e-9 or pct == 100
+    f = g["fine_grained_256_top8_b64"]
+    v = O.expected_experts_touched(f["n_experts"], f["top_k"], f["batch"])
+    assert abs(v - f["approx"]) <= f["rel_tol"] * f["approx"]
+    s = g["share_woken_1_in_32"]
+    for B_, pct in s["rows_percent"]:
+        v = O.expected_experts_touched(s["n_experts"], s["top_k"], B_)
+        assert abs(100 * v / s["n_experts"] - pct) <= 0.5 + 1e-9, (B_, pct, v)
+
+
+def pin_touched_statistics(seed=10):
+    """Uniform random routing: the mean distinct-expert count over trials is
+    within 4 standard errors of the closed form."""
+    rng = np.random.default_rng(seed)
+    for N, k, Bt in ((8, 2, 4), (8, 2, 16), (256, 8, 64)):
+        trials = 4000
+        vals = np.empty(trials)
+        for i in range(trials):
+            idx = np.stack([rng.permutation(N)[:k] for _ in range(Bt)])
+            vals[i] = np.count_nonzero(O.expert_counts(idx, N))
+        mu = O.expected_experts_touched(N, k, Bt)
+        assert abs(vals.mean() - mu) <= 4 * vals.std() / math.sqrt(trials) + 1e-9
+
+
+ALL_PINS = [
+    pin_router_worked_example_skillsuites, pin_router_worked_example_ai_infra,
+    pin_softmax_placement_equivalence, pin_brute_force_routing,
+    pin_sigmoid_invariants, pin_sigmoid_function, pin_router_logits_brute,
+    pin_permutation, pin_layer_brute_force, pin_identical_experts_equal_dense,
+    pin_distinct_experts_k_equals_n, pin_token_independence_and_relabel,
+    pin_bf16_decoder, pin_e4m3_decoder, pin_fp8_block_dequant,
+    pin_experts_touched,
+]
+
+
+@pytest.mark.parametrize("pin", ALL_PINS + [pin_touched_statistics], ids=lambda f: f.__name__)
+def test_pin(pin):
+    pin()
+
+
+# ---------------------------------------------------------------------------
+# planted mistakes: each must make at least one pin fail
+# ---------------------------------------------------------------------------
+
+def _m_full_softmax_no_renorm(logits, idx, route):
+    p = np.exp(logits - logits.max(axis=1, keepdims=True))
+    p /= p.sum(axis=1, keepdims=True)
+    return np.take_along_axis(p, idx, axis=1)
+
+
+def _m_gates_from_biased(orig):
+    def f(logits, idx, route):
+        if route == "sigmoid":
+            a = O.sigmoid(np.take_along_axis(logits, idx, axis=1)) + 0.05 * (idx == 0)
+            return a / a.sum(axis=1, keepdims=True)
+        return orig(logits, idx, route)
+    return f
+
+
+def _m_topk_smallest(scores, k):
+    return np.argsort(np.asarray(scores, dtype=np.float32), axis=1, kind="stable")[:, :k]
+
+
+def _m_topk_ties_high(scores, k):
+    s = np.asarray(scores, dtype=np.float32)
+    N = s.shape[1]
+    order = np.argsort(-s[:, ::-1], axis=1, kind="stable")
+    return (N - 1 - order)[:, :k]
+
+
+def _m_silu_on_up(X, wg, wu, wd):
+    g = X @ wg.T
+    u = X @ wu.T
+    return (g * O.sigmoid(u) * u) @ wd.T
+
+
+def _m_down_transposed(X, wg, wu, wd):
+    h = O.silu(X @ wg.T) * (X @ wu.T)
+    return h @ wd.reshape(wd.shape[1], wd.shape[0])
+
+
+def _m_combine_drop_shared(y, g, inv, ys=None):
+    return _orig_combine(y, g, inv, None)
+
+
+def _m_combine_slot_swap(y, g, inv, ys=None):
+    return _orig_combine(y, g[:, ::-1], inv, ys)
+
+
+def _m_perm_unstable(idx, n):
+    p = _orig_perm(idx, n)
+    T, k = np.asarray(idx).shape
+    # reverse token order inside each expert
+    for e in range(n):
+        lo, hi = p.offsets[e], p.offsets[e + 1]
+        p.perm_token[lo:hi] = p.perm_token[lo:hi][::-1].copy()
+    return p
+
+
+def _m_bf16_truncate_sign(bits):
+    return np.abs(_orig_bf16(bits))
+
+
+def _m_e4m3_bias8(bits):
+    return _orig_e4m3(bits) / 2.0
+
+
+def _m_touched_linear(N, k, b):
+    return min(N, k * b)
+
+
+def _m_logits_no_offset(x, w, off=None):
+    return _orig_logits(x, w, None)
+
+
+_orig_perm = O.permute_assignments
+_orig_bf16 = O.bf16_bits_to_f64
+_orig_e4m3 = O.e4m3_bits_to_f64
+_orig_logits = O.router_logits
+_orig_combine = O.combine
+
+MUTATIONS = {
+    "gates_softmax_all_no_renormalise": ("gate_weights", lambda: _m_full_softmax_no_renorm),
+    "gates_from_biased_scores": ("gate_weights", lambda: _m_gates_from_biased(O.gate_weights)),
+    "topk_picks_smallest": ("top_k_select", lambda: _m_topk_smallest),
+    "topk_ties_to_higher_index": ("top_k_select", lambda: _m_topk_ties_high),
+    "silu_on_up_branch": ("swiglu_expert", lambda: _m_silu_on_up),
+    "down_projection_transposed": ("swiglu_expert", lambda: _m_down_transposed),
+    "combine_drops_shared": ("combine", lambda: _m_combine_drop_shared),
+    "combine_swaps_slots": ("combine", lambda: _m_combine_slot_swap),
+    "permutation_not_token_ordered": ("permute_assignments", lambda: _m_perm_unstable),
+    "bf16_decoder_loses_sign": ("bf16_bits_to_f64", lambda: _m_bf16_truncate_sign),
+    "e4m3_decoder_wrong_bias": ("e4m3_bits_to_f64", lambda: _m_e4m3_bias8),
+    "experts_touched_linear": ("expected_experts_touched", lambda: _m_touched_linear),
+    "router_drops_offset": ("router_logits", lambda: _m_logits_no_offset),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_planted_mistakes_are_caught(name, monkeypatch):
+    attr, make = MUTATIONS[name]
+    monkeypatch.setattr(O, attr, make())
+    failed = []
+    for pin in ALL_PINS:
+        try:
+            pin()
+        except (AssertionError, ValueError, IndexError):
+            failed.append(pin.__name__)
+    assert failed, f"planted mistake {name} passed every pin"

@@ -1,0 +1,227 @@
+"""Benchmark of the MoE FFN layer forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config I]
+
+A step is one pass of the whole hot path over one batch already resident in
+HBM: router (logits + top-k), permute, expert gate/up + SwiGLU, expert down,
+combine, each through its C-ABI entry point on torch's current stream, with a
+HIP event after each so every stage is timed inside the timed region.  The
+default workload is the Mixtral-8x7B-shaped decode layer (T=16, d=4096, 8
+experts top-2, d_ff=14336, bf16).  Prints one JSON line.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0            # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2500.0        # dense bf16 MFMA
+PEAK_FP32_VALU_TFLOPS = 78.6     # 256 CU x 64 lanes x 2 flop x 2.4 GHz, no packed math
+METRIC = "MoE-layer tokens/sec at 1 GPU; decode HBM GB/s and prefill TFLOP/s vs roofline"
+STAGES = ["router", "permute", "gate_up", "down", "combine"]
+
+
+def accounting(cfg, touched: int):
+    """Algorithmic bytes and flops of each stage (each weight byte of a
+    touched expert counted once; activations in and out once)."""
+    T, k, N, d, f = cfg.T, cfg.top_k, cfg.n_experts, cfg.d_model, cfg.d_ff
+    wb = {"f32": 4, "bf16": 2, "fp8": 1}[cfg.w_dtype]
+    ab = 4 if cfg.act_dtype == "f32" else 2
+    sh = cfg.n_shared
+    rows = T * k + sh * T
+    mats = touched + sh
+    sc13 = 2 * (f // 128) * (d // 128) * 4 if cfg.w_dtype == "fp8" else 0
+    sc2 = (f // 128) * (d // 128) * 4 if cfg.w_dtype == "fp8" else 0
+    st = {
+        "router": dict(bytes=T * d * ab + d * N * 4 + T * k * 8, flops=2 * T * d * N),
+        "permute": dict(bytes=T * k * 4 + (2 * N + 1) * 4 + 2 * T * k * 4, flops=0),
+        "gate_up": dict(bytes=mats * (2 * f * d * wb + sc13) + rows * d * ab + rows * f * ab,
+                        flops=2 * rows * d * 2 * f),
+        "down": dict(bytes=mats * (d * f * wb + sc2) + rows * f * ab + rows * d * ab,
+                     flops=2 * rows * f * d),
+        "combine": dict(bytes=rows * d * ab + T * d * ab + T * k * 8, flops=2 * T * k * d),
+    }
+    layer = dict(bytes=mats * (3 * f * d * wb + sc13 + sc2) + d * N * 4 + 2 * T * d * ab,
+                 flops=sum(v["flops"] for v in st.values()))
+    return st, layer
+
+
+def roofline_for(cfg, stage: dict, ms: float):
+    flops, byts = stage["flops"], stage["bytes"]
+    if cfg.w_dtype == "f32":
+        peak_f = PEAK_FP32_VALU_TFLOPS
+    else:
+        peak_f = PEAK_BF16_TFLOPS
+    ai = flops / max(byts, 1)
+    ridge = peak_f * 1e12 / (PEAK_HBM_GBS * 1e9)
+    if ai < ridge:
+        ach = byts / (ms * 1e-3) / 1e9
+        return {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(ach / PEAK_HBM_GBS, 4)}
+    ach = flops / (ms * 1e-3) / 1e12
+    bound = "alu" if cfg.w_dtype == "f32" else "mfma"
+    return {"bound": bound, "achieved": round(ach, 1), "peak": peak_f, "unit": "TFLOP/s",
+            "frac": round(ach / peak_f, 4)}
+
+
+def cpu_baseline(cfg, x_cpu, n_tokens: int):
+    """Time the CPU oracle (as it stands) on a bounded sample of the same
+    workload: the first n_tokens tokens, weights decoded from their stored
+    bits inside the timed region."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import oracle.moe_oracle as O
+    from mixture_experts_ffn_09_amd import workloads as W
+    from tests import _harness as Hh
+
+    xs = x_cpu[:n_tokens]
+    w_r, off, bias = Hh.oracle_router(cfg)
+    R = O.route_tokens(Hh.x_f64(cfg, xs), w_r, cfg.top_k, cfg.route, off, bias)
+    need = sorted(set(int(e) for e in R.idx.reshape(-1))) + ([cfg.n_experts] if cfg.n_shared else [])
+    stored = {e: W.make_expert(cfg, e) for e in need}      # generation is not timed
+
+    def expert(e):
+        w = stored[e]
+        return tuple(Hh.decode_weight(cfg, w, kk) for kk in ("gate", "up", "down"))
+
+    t0 = time.perf_counter()
+    xo = Hh.x_f64(cfg, xs)
+    O.moe_forward(xo, w_r, expert, cfg.top_k, cfg.route, off, bias,
+                  expert(cfg.n_experts) if cfg.n_shared else None)
+    secs = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    return {"value": round(n_tokens / secs, 3), "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"first {n_tokens} of {cfg.T} tokens, {len(need)} experts decoded from "
+                      f"stored bits, float64 NumPy, {secs:.2f} s"}
+
+
+CPU_SAMPLE = {0: 64, 1: 16, 2: 16, 3: 4, 4: 8}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=1, help="workload index (1 = Mixtral decode)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    a = ap.parse_args()
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(the design for sharding is described in the docs)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from mixture_experts_ffn_09_amd import moe, workloads as W
+    from mixture_experts_ffn_09_amd.layer import build_device_layer
+
+    cfg = W.CONFIGS[a.config]
+    print(f"[bench] building {cfg.name}", file=sys.stderr, flush=True)
+    L = build_device_layer(cfg)
+    x_cpu = W.make_x(cfg)
+    x = x_cpu.to("cuda")
+    T, k, N, d, f = cfg.T, cfg.top_k, cfg.n_experts, cfg.d_model, cfg.d_ff
+    adt = x.dtype
+    s = L.shape_for(T)
+    ws = L.workspace()
+    rb = L.routing_buffers()
+    routing = moe.make_routing(**rb)
+    h = torch.empty(T * k, f, dtype=adt, device="cuda")
+    y = torch.empty(T * k, d, dtype=adt, device="cuda")
+    h_sh = torch.empty(T, f, dtype=adt, device="cuda") if cfg.n_shared else None
+    y_sh = torch.empty(T, d, dtype=adt, device="cuda") if cfg.n_shared else None
+    out = torch.empty_like(x)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        moe.moe_router_topk(s, x, L.weights, rb["topk_idx"], rb["topk_w"], ws)
+        if ev is not None:
+            ev[1].record()
+        moe.moe_permute(s, rb["topk_idx"], None, routing)
+        if ev is not None:
+            ev[2].record()
+        moe.moe_expert_gate_up(s, x, None, rb["perm_token"], rb["offsets"], L.weights, h, h_sh)
+        if ev is not None:
+            ev[3].record()
+        moe.moe_expert_down(s, h, h_sh, rb["offsets"], L.weights, y, y_sh)
+        if ev is not None:
+            ev[4].record()
+        moe.moe_combine(s, y, y_sh, rb["inv_perm"], rb["topk_w"], out)
+        if ev is not None:
+            ev[5].record()
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(a.steps)]
+    print(f"[bench] timing {a.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(a.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / a.steps
+    stage_ms = {name: sum(ev[j].elapsed_time(ev[j + 1]) for ev in events) / a.steps
+                for j, name in enumerate(STAGES)}
+
+    # cross-check: the same work through the single moe_layer_forward call
+    torch.cuda.synchronize()
+    t2 = time.perf_counter()
+    for _ in range(a.steps):
+        moe.moe_layer_forward(s, L.weights, x, out, ws)
+    torch.cuda.synchronize()
+    fused_ms = (time.perf_counter() - t2) * 1e3 / a.steps
+
+    counts = rb["counts"].cpu()
+    touched = int((counts > 0).sum())
+    st, layer = accounting(cfg, touched)
+    stages = {}
+    for name in STAGES:
+        r = roofline_for(cfg, st[name], stage_ms[name])
+        stages[name] = {"ms": round(stage_ms[name], 4), "bytes": st[name]["bytes"],
+                        "flops": st[name]["flops"], "bound": r["bound"], "frac": r["frac"],
+                        "achieved": r["achieved"], "unit": r["unit"]}
+    dom = "gate_up"
+    roof = roofline_for(cfg, st[dom], stage_ms[dom])
+    roof["traffic"] = None
+    roof["kernel"] = "ffn_stream_kernel (gate/up + SwiGLU)"
+    layer_gbs = layer["bytes"] / (ms_step * 1e-3) / 1e9
+    layer_tflops = layer["flops"] / (ms_step * 1e-3) / 1e12
+
+    rec = {
+        "metric": METRIC, "value": round(T / (ms_step * 1e-3), 2), "unit": "tokens/s",
+        "n_gpus": 1, "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": {"f32": "f32", "bf16": "bf16", "fp8": "fp8-e4m3 weights, bf16 activations"}[cfg.w_dtype],
+        "data": "synthetic (seeded random weights and inputs)",
+        "config": {"workload": cfg.name, "T": T, "d_model": d, "n_experts": N, "top_k": k,
+                   "d_ff": f, "n_shared": cfg.n_shared, "route": cfg.route,
+                   "weights": cfg.w_dtype, "experts_touched": touched,
+                   "max_over_mean_load": round(float(counts.max()) / max(1e-9, float(counts.float().mean())), 3)},
+        "roofline": roof,
+        "layer": {"algorithmic_bytes": layer["bytes"], "flops": layer["flops"],
+                  "hbm_GBps": round(layer_gbs, 1), "hbm_frac": round(layer_gbs / PEAK_HBM_GBS, 4),
+                  "TFLOPs": round(layer_tflops, 2),
+                  "single_call_ms_per_step": round(fused_ms, 4)},
+        "stages": stages,
+    }
+    if not a.no_cpu_baseline:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        rec["cpu_baseline"] = cpu_baseline(cfg, x_cpu, min(T, CPU_SAMPLE.get(a.config, 8)))
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,208 @@
+/*
+ * moe_ffn.h - C ABI of the MI355X (gfx950) token-choice sparse MoE FFN
+ * layer forward.
+ *
+ * The layer (the pages cited below are "Mixture of Experts for LLM
+ * Inference" [MoE-LLM], "AI Infrastructure series - Part 12 of 24" [AIS-12],
+ * "Chapter 19: Mixture-of-Experts Models" [CH19] and "Mixture of Experts
+ * Explained" [MoE-EXP]):
+ *
+ *   s      = x @ W_router (+ logit_offset)            router logits
+ *   select top-k experts per token (softmax: by logit; sigmoid: by
+ *          sigmoid(s) + select_bias, the bias used for selection only)
+ *   g      = softmax over the k selected logits  |  sigmoid(s_sel)/sum
+ *   out[t] = sum_i g[t,i] * FFN_{idx[t,i]}(x[t])  (+ FFN_shared(x[t]))
+ *   FFN(x) = W_down (silu(W_gate x) * (W_up x))    (SwiGLU expert)
+ *
+ * Conventions for every entry point:
+ *   - Pointers are DEVICE pointers unless stated otherwise, owned by the
+ *     caller.  The library never allocates device memory; scratch space is
+ *     the caller's workspace, sized by moe_workspace_bytes().
+ *   - Calls are asynchronous on `stream`; results are valid once the stream
+ *     has synchronised.  No entry point copies device data to the host or
+ *     synchronises the stream.
+ *   - Arguments are checked on the host before any HIP call; a bad argument
+ *     returns an error status and launches nothing.  A failed launch returns
+ *     MOE_ERR_HIP; moe_last_error() then gives the HIP message (per thread).
+ *   - Row-major layouts; experts are numbered 0..N-1.  Expert ids and token
+ *     indices are int32.  Entry points hold no state and may be called from
+ *     several host threads.
+ *   - Supported types: x/out float32 or bfloat16; expert weights float32
+ *     (with float32 activations), bfloat16, or OCP FP8 E4M3 with one float32
+ *     scale per 128x128 block (both with bfloat16 activations).  The router
+ *     weight, offset and bias are always float32.
+ *   - Shape limits (else MOE_ERR_UNSUPPORTED): N <= 512, k <= 64;
+ *     n_shared in {0,1}; bfloat16 weights need d_model % 32 == 0 and
+ *     d_ff % 32 == 0; FP8 weights need d_model % 128 == 0 and
+ *     d_ff % 128 == 0; bfloat16 activations need d_model % 8 == 0.
+ *     float32 weights need n_tokens * top_k <= 1048560.  Invalid values
+ *     (k < 1, k > N, negative sizes, ...) are MOE_ERR_INVALID_ARG.
+ *     n_tokens == 0 is a valid no-op.
+ */
+#ifndef MOE_FFN_H
+#define MOE_FFN_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1,         /* null pointer, bad value              */
+  MOE_ERR_UNSUPPORTED = 2,         /* valid but outside the limits above   */
+  MOE_ERR_WORKSPACE_TOO_SMALL = 3, /* ws_bytes < moe_workspace_bytes()     */
+  MOE_ERR_HIP = 4                  /* a HIP call failed; see last_error    */
+} moe_status_t;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype_t;
+
+/* softmax over the top-k logits ([CH19] 19.3.2; [MoE-EXP] "The router, with
+ * real numbers"), or sigmoid affinities with a selection-only per-expert
+ * bias and renormalised selected affinities ([AIS-12] worked example,
+ * DeepSeek-V3 paragraph; [MoE-LLM] "DeepSeek-style bias controller";
+ * [CH19] 19.3.4). */
+typedef enum { MOE_ROUTE_SOFTMAX_TOPK = 0, MOE_ROUTE_SIGMOID_BIAS = 1 } moe_route_t;
+
+typedef struct {
+  int32_t n_tokens;   /* T  >= 0                                          */
+  int32_t d_model;    /* d  >= 1                                          */
+  int32_t n_experts;  /* N  routed experts                                */
+  int32_t top_k;      /* k                                                */
+  int32_t d_ff;       /* expert hidden width                              */
+  int32_t n_shared;   /* 0 or 1 always-on shared expert ([MoE-LLM]
+                         "Shared experts"; [AIS-12] "What is a shared
+                         expert?")                                         */
+  int32_t route;      /* moe_route_t                                      */
+  int32_t act_dtype;  /* MOE_F32 | MOE_BF16 : x, out                       */
+  int32_t w_dtype;    /* MOE_F32 | MOE_BF16 | MOE_FP8_E4M3 : expert weights */
+} moe_shape_t;
+
+/* Device pointers to the layer's parameters.  Expert weights are in the
+ * packed layout written by moe_pack_weights(); scales stay in their natural
+ * [E][rows/128][cols/128] float32 layout. */
+typedef struct {
+  const float* w_router;     /* [d][N]                                    */
+  const float* logit_offset; /* [N] added to the logits, or NULL          */
+  const float* select_bias;  /* [N] selection-only bias (sigmoid), or NULL */
+  const void* w13;           /* packed gate+up of the N routed experts     */
+  const void* w2;            /* packed down of the N routed experts        */
+  const float* w13_scale;    /* FP8: [N][2][d_ff/128][d/128] gate, up      */
+  const float* w2_scale;     /* FP8: [N][d/128][d_ff/128]                  */
+  const void* w13_shared;    /* packed gate+up of the shared expert / NULL */
+  const void* w2_shared;     /* packed down of the shared expert / NULL    */
+  const float* w13_shared_scale; /* FP8 scales of the shared expert / NULL */
+  const float* w2_shared_scale;
+} moe_weights_t;
+
+/* Routing results (all device pointers; each may be NULL in
+ * moe_layer_forward when the caller does not want it back). */
+typedef struct {
+  int32_t* topk_idx;   /* [T][k] expert ids, best first                    */
+  float* topk_w;       /* [T][k] gates, rows sum to 1                      */
+  int32_t* counts;     /* [N] assignments per expert                       */
+  int32_t* offsets;    /* [N+1] exclusive prefix sum of counts             */
+  int32_t* perm_token; /* [T*k] token of each expert-contiguous row        */
+  int32_t* inv_perm;   /* [T][k] row of each (token, slot)                 */
+} moe_routing_t;
+
+/* Bytes of one packed expert-weight buffer for `n_mats` experts:
+ * which = 0 -> gate+up (w13), which = 1 -> down (w2).  0 on a bad shape. */
+size_t moe_packed_weight_bytes(const moe_shape_t* s, int which, int n_mats);
+
+/* Repack expert weights from [out][in] row-major into the kernels' layout
+ * (run once, not part of the forward).  which = 0: src_a = W_gate
+ * [n_mats][d_ff][d], src_b = W_up [n_mats][d_ff][d]; which = 1: src_a =
+ * W_down [n_mats][d][d_ff], src_b = NULL.  Elements are of s->w_dtype (FP8:
+ * uint8 E4M3 codes).  dst must hold moe_packed_weight_bytes(s, which,
+ * n_mats) bytes and must not overlap the sources.  Each expert is a
+ * separately addressed block, so an unselected expert's bytes are never
+ * read ([MoE-EXP] "Why heads cannot be sparsified the same way"). */
+moe_status_t moe_pack_weights(const moe_shape_t* s, int which, int n_mats,
+                              const void* src_a, const void* src_b, void* dst,
+                              hipStream_t stream);
+
+/* Workspace bytes moe_layer_forward / moe_grouped_ffn / moe_router_topk need
+ * for this shape (0 when n_tokens == 0); each of them checks ws_bytes against
+ * it.  Returns (size_t)-1 on a bad shape.  Layout (256-byte aligned pieces):
+ * logits [T][N] f32, topk idx/w, counts, offsets, perm_token, inv_perm,
+ * H [T*k][d_ff] and H_shared [T][d_ff], Y [T*k][d] and Y_shared [T][d]
+ * (H, Y in the activation type). */
+size_t moe_workspace_bytes(const moe_shape_t* s);
+
+/* a1+a2: router logits, selection and gates ([MoE-LLM] "Opening the
+ * router"; [CH19] 19.3.2; [AIS-12] worked example).  x: [T][d] act_dtype.
+ * Writes topk_idx [T][k] (descending selection score, exact ties to the
+ * lower index) and topk_w [T][k].  Uses w->w_router, w->logit_offset and
+ * (sigmoid only) w->select_bias; ws holds the [T][N] float32 logits. */
+moe_status_t moe_router_topk(const moe_shape_t* s, const void* x,
+                             const moe_weights_t* w, int32_t* topk_idx,
+                             float* topk_w, void* ws, size_t ws_bytes,
+                             hipStream_t stream);
+
+/* a3+a4: per-expert counts, offsets, and the stable expert-contiguous
+ * permutation of (token, slot) assignments, ordered by (expert, token)
+ * ([CH19] 19.6.3 "Route and pack").  Ids outside [0, N) are not counted and
+ * get inv_perm = -1.  If x_perm is not NULL, also gathers x_perm[r] =
+ * x[perm_token[r]] ([T*k][d] act_dtype; x is then required). */
+moe_status_t moe_permute(const moe_shape_t* s, const int32_t* topk_idx,
+                         const void* x, moe_routing_t* out, void* x_perm,
+                         hipStream_t stream);
+
+/* a5+a6: every routed expert's SwiGLU FFN on its rows, and the shared
+ * expert on all T tokens.  Rows of expert e are r in
+ * [offsets[e], offsets[e+1]); row r reads x_perm[r] when x_perm is not NULL,
+ * else x[perm_token[r]].  Writes y_perm [T*k][d] (row r = FFN_e of its
+ * token) and, when n_shared == 1, y_shared [T][d]; both act_dtype.
+ * offsets/perm_token are device arrays as written by moe_permute. */
+moe_status_t moe_grouped_ffn(const moe_shape_t* s, const void* x,
+                             const void* x_perm, const int32_t* perm_token,
+                             const int32_t* offsets, const moe_weights_t* w,
+                             void* y_perm, void* y_shared, void* ws,
+                             size_t ws_bytes, hipStream_t stream);
+
+/* a5 alone: H = silu(X W_gate^T) * (X W_up^T) for every routed expert's rows
+ * (the SwiGLU in the GEMM epilogue) and, when n_shared == 1, for all T tokens
+ * of the shared expert.  Inputs as in moe_grouped_ffn.  h: [T*k][d_ff],
+ * h_shared: [T][d_ff] (act_dtype). */
+moe_status_t moe_expert_gate_up(const moe_shape_t* s, const void* x,
+                                const void* x_perm, const int32_t* perm_token,
+                                const int32_t* offsets, const moe_weights_t* w,
+                                void* h, void* h_shared, hipStream_t stream);
+
+/* a6 alone: y = H W_down^T per routed expert's rows (and the shared
+ * expert's).  h / h_shared as written by moe_expert_gate_up. */
+moe_status_t moe_expert_down(const moe_shape_t* s, const void* h,
+                             const void* h_shared, const int32_t* offsets,
+                             const moe_weights_t* w, void* y_perm,
+                             void* y_shared, hipStream_t stream);
+
+/* a7: out[t] = sum_{i<k} topk_w[t,i] * y_perm[inv_perm[t,i]] (+ y_shared[t])
+ * in that fixed order with float32 accumulation and one rounding per output
+ * element: deterministic, no atomics ([MoE-LLM] "The MoE change is
+ * surprisingly local"; [CH19] 19.3.2).  y_shared may be NULL. */
+moe_status_t moe_combine(const moe_shape_t* s, const void* y_perm,
+                         const void* y_shared, const int32_t* inv_perm,
+                         const float* topk_w, void* out, hipStream_t stream);
+
+/* The whole layer forward: router, permute, grouped FFN, combine.  x and
+ * out: [T][d] act_dtype (must not overlap).  routing_out may be NULL, and
+ * any of its members may be NULL.  ws: moe_workspace_bytes(s) bytes. */
+moe_status_t moe_layer_forward(const moe_shape_t* s, const moe_weights_t* w,
+                               const void* x, void* out,
+                               moe_routing_t* routing_out, void* ws,
+                               size_t ws_bytes, hipStream_t stream);
+
+/* Static description of a status code. */
+const char* moe_status_string(moe_status_t st);
+
+/* Message of the last MOE_ERR_HIP / argument error on this host thread. */
+const char* moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_FFN_H */

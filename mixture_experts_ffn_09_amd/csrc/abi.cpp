@@ -1,0 +1,374 @@
+// C ABI of the MoE FFN library: argument checks (all on the host, before any
+// HIP call), workspace carving, and kernel orchestration.  See moe_ffn.h.
+
+#include "moe_ffn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "kernels.h"
+
+namespace {
+
+constexpr int kMaxExperts = 512;
+constexpr int kMaxTopK = 64;
+
+thread_local char g_err[512] = "";
+
+moe_status_t fail(moe_status_t st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+moe_status_t hip_fail(const char* where, hipError_t e) {
+  return fail(MOE_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+#define HIP_TRY(where, expr)                     \
+  do {                                           \
+    hipError_t e_ = (expr);                      \
+    if (e_ != hipSuccess) return hip_fail(where, e_); \
+  } while (0)
+
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+int act_size(const moe_shape_t* s) { return s->act_dtype == MOE_F32 ? 4 : 2; }
+
+int w_size(const moe_shape_t* s) {
+  return s->w_dtype == MOE_F32 ? 4 : (s->w_dtype == MOE_BF16 ? 2 : 1);
+}
+
+moe_status_t check_shape(const moe_shape_t* s) {
+  if (!s) return fail(MOE_ERR_INVALID_ARG, "shape is NULL");
+  if (s->n_tokens < 0) return fail(MOE_ERR_INVALID_ARG, "n_tokens < 0");
+  if (s->d_model < 1 || s->d_ff < 1) return fail(MOE_ERR_INVALID_ARG, "d_model, d_ff must be >= 1");
+  if (s->n_experts < 1) return fail(MOE_ERR_INVALID_ARG, "n_experts must be >= 1");
+  if (s->top_k < 1 || s->top_k > s->n_experts)
+    return fail(MOE_ERR_INVALID_ARG, "need 1 <= top_k <= n_experts");
+  if (s->n_shared != 0 && s->n_shared != 1) return fail(MOE_ERR_INVALID_ARG, "n_shared must be 0 or 1");
+  if (s->route != MOE_ROUTE_SOFTMAX_TOPK && s->route != MOE_ROUTE_SIGMOID_BIAS)
+    return fail(MOE_ERR_INVALID_ARG, "unknown route %d", s->route);
+  if (s->act_dtype != MOE_F32 && s->act_dtype != MOE_BF16)
+    return fail(MOE_ERR_INVALID_ARG, "act_dtype must be MOE_F32 or MOE_BF16");
+  if (s->w_dtype != MOE_F32 && s->w_dtype != MOE_BF16 && s->w_dtype != MOE_FP8_E4M3)
+    return fail(MOE_ERR_INVALID_ARG, "unknown w_dtype %d", s->w_dtype);
+  if (s->n_experts > kMaxExperts) return fail(MOE_ERR_UNSUPPORTED, "n_experts > %d", kMaxExperts);
+  if (s->top_k > kMaxTopK) return fail(MOE_ERR_UNSUPPORTED, "top_k > %d", kMaxTopK);
+  if ((s->act_dtype == MOE_F32) != (s->w_dtype == MOE_F32))
+    return fail(MOE_ERR_UNSUPPORTED, "float32 activations pair with float32 weights only");
+  if (s->w_dtype == MOE_BF16 && (s->d_model % 32 || s->d_ff % 32))
+    return fail(MOE_ERR_UNSUPPORTED, "bfloat16 weights need d_model %% 32 == 0 and d_ff %% 32 == 0");
+  if (s->w_dtype == MOE_FP8_E4M3 && (s->d_model % 128 || s->d_ff % 128))
+    return fail(MOE_ERR_UNSUPPORTED, "FP8 weights need d_model %% 128 == 0 and d_ff %% 128 == 0");
+  const long long tk = (long long)s->n_tokens * s->top_k;
+  if (tk > INT_MAX / 2) return fail(MOE_ERR_UNSUPPORTED, "n_tokens * top_k too large");
+  if (s->act_dtype == MOE_F32 && (tk + 15) / 16 > 65535)
+    return fail(MOE_ERR_UNSUPPORTED, "float32 path: n_tokens * top_k > %d", 16 * 65535);
+  return MOE_OK;
+}
+
+struct WsLayout {
+  size_t logits, idx, w, counts, offsets, perm, inv, H, H_sh, Y, Y_sh, total;
+};
+
+WsLayout ws_layout(const moe_shape_t* s) {
+  WsLayout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off += align256(bytes);
+    return o;
+  };
+  const size_t T = s->n_tokens, k = s->top_k, N = s->n_experts, d = s->d_model, f = s->d_ff;
+  const size_t es = act_size(s), sh = s->n_shared;
+  L.logits = take(T * N * 4);
+  L.idx = take(T * k * 4);
+  L.w = take(T * k * 4);
+  L.counts = take(N * 4);
+  L.offsets = take((N + 1) * 4);
+  L.perm = take(T * k * 4);
+  L.inv = take(T * k * 4);
+  L.H = take(T * k * f * es);
+  L.H_sh = take(sh * T * f * es);
+  L.Y = take(T * k * d * es);
+  L.Y_sh = take(sh * T * d * es);
+  L.total = off;
+  return L;
+}
+
+moe_status_t check_ws(const moe_shape_t* s, void* ws, size_t ws_bytes) {
+  const size_t need = ws_layout(s).total;
+  if (!ws) return fail(MOE_ERR_INVALID_ARG, "workspace is NULL");
+  if (ws_bytes < need)
+    return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", ws_bytes, need);
+  return MOE_OK;
+}
+
+moe_status_t check_weights(const moe_shape_t* s, const moe_weights_t* w, bool router, bool ffn) {
+  if (!w) return fail(MOE_ERR_INVALID_ARG, "weights is NULL");
+  if (router) {
+    if (!w->w_router) return fail(MOE_ERR_INVALID_ARG, "w_router is NULL");
+    if (w->select_bias && s->route != MOE_ROUTE_SIGMOID_BIAS)
+      return fail(MOE_ERR_INVALID_ARG, "select_bias belongs to the sigmoid router");
+  }
+  if (ffn) {
+    if (!w->w13 || !w->w2) return fail(MOE_ERR_INVALID_ARG, "w13 / w2 is NULL");
+    if (s->w_dtype == MOE_FP8_E4M3 && (!w->w13_scale || !w->w2_scale))
+      return fail(MOE_ERR_INVALID_ARG, "FP8 weights need w13_scale and w2_scale");
+    if (s->n_shared) {
+      if (!w->w13_shared || !w->w2_shared)
+        return fail(MOE_ERR_INVALID_ARG, "n_shared == 1 needs w13_shared / w2_shared");
+      if (s->w_dtype == MOE_FP8_E4M3 && (!w->w13_shared_scale || !w->w2_shared_scale))
+        return fail(MOE_ERR_INVALID_ARG, "FP8 shared expert needs its scales");
+    }
+  }
+  return MOE_OK;
+}
+
+moe_status_t run_router(const moe_shape_t* s, const void* x, const moe_weights_t* w,
+                        int32_t* idx, float* gw, float* logits, hipStream_t st) {
+  HIP_TRY("router_logits",
+          launch_router_logits(x, s->act_dtype == MOE_BF16, w->w_router, w->logit_offset, logits,
+                               s->n_tokens, s->d_model, s->n_experts, st));
+  HIP_TRY("router_topk", launch_router_topk(logits,
+                                            s->route == MOE_ROUTE_SIGMOID_BIAS ? w->select_bias
+                                                                               : nullptr,
+                                            s->route == MOE_ROUTE_SIGMOID_BIAS, s->n_tokens,
+                                            s->n_experts, s->top_k, idx, gw, st));
+  return MOE_OK;
+}
+
+moe_status_t run_ffn(const moe_shape_t* s, const void* x, const void* x_rows,
+                     const int32_t* perm, const int32_t* offsets, const moe_weights_t* w,
+                     void* H, void* H_sh, void* y, void* y_sh, int pass, hipStream_t st) {
+  if (s->w_dtype == MOE_F32) {
+    FfnF32Args a{};
+    a.x_rows = static_cast<const float*>(x_rows);
+    a.perm_token = perm;
+    a.x_sh = static_cast<const float*>(x);
+    a.offsets = offsets;
+    a.T = s->n_tokens;
+    a.N = s->n_experts;
+    a.n_shared = s->n_shared;
+    a.d = s->d_model;
+    a.d_ff = s->d_ff;
+    a.max_rows = s->n_tokens * s->top_k;
+    a.w13 = static_cast<const float*>(w->w13);
+    a.w2 = static_cast<const float*>(w->w2);
+    a.w13_sh = static_cast<const float*>(w->w13_shared);
+    a.w2_sh = static_cast<const float*>(w->w2_shared);
+    a.H = static_cast<float*>(H);
+    a.H_sh = static_cast<float*>(H_sh);
+    a.Y = static_cast<float*>(y);
+    a.Y_sh = static_cast<float*>(y_sh);
+    HIP_TRY("ffn_f32", launch_ffn_f32(a, pass, st));
+    return MOE_OK;
+  }
+  FfnArgs a{};
+  a.x_rows = static_cast<const uint16_t*>(x_rows);
+  a.perm_token = perm;
+  a.x_sh = static_cast<const uint16_t*>(x);
+  a.offsets = offsets;
+  a.T = s->n_tokens;
+  a.N = s->n_experts;
+  a.n_shared = s->n_shared;
+  a.d = s->d_model;
+  a.d_ff = s->d_ff;
+  a.fp8 = s->w_dtype == MOE_FP8_E4M3;
+  a.w13 = w->w13;
+  a.w2 = w->w2;
+  a.s13 = w->w13_scale;
+  a.s2 = w->w2_scale;
+  a.w13_sh = w->w13_shared;
+  a.w2_sh = w->w2_shared;
+  a.s13_sh = w->w13_shared_scale;
+  a.s2_sh = w->w2_shared_scale;
+  a.H = static_cast<uint16_t*>(H);
+  a.H_sh = static_cast<uint16_t*>(H_sh);
+  a.Y = static_cast<uint16_t*>(y);
+  a.Y_sh = static_cast<uint16_t*>(y_sh);
+  HIP_TRY("ffn", launch_ffn_lowp(a, pass, st));
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(moe_status_t st) {
+  switch (st) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported shape or type";
+    case MOE_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case MOE_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char* moe_last_error(void) { return g_err; }
+
+size_t moe_packed_weight_bytes(const moe_shape_t* s, int which, int n_mats) {
+  if (check_shape(s) != MOE_OK || (which != 0 && which != 1) || n_mats < 1) return 0;
+  const size_t per = (size_t)s->d_model * s->d_ff * w_size(s) * (which == 0 ? 2 : 1);
+  return per * (size_t)n_mats;
+}
+
+moe_status_t moe_pack_weights(const moe_shape_t* s, int which, int n_mats, const void* src_a,
+                              const void* src_b, void* dst, hipStream_t stream) {
+  moe_status_t st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (which != 0 && which != 1) return fail(MOE_ERR_INVALID_ARG, "which must be 0 or 1");
+  if (n_mats < 1) return fail(MOE_ERR_INVALID_ARG, "n_mats must be >= 1");
+  if (!src_a || !dst) return fail(MOE_ERR_INVALID_ARG, "src_a / dst is NULL");
+  if ((which == 0) != (src_b != nullptr))
+    return fail(MOE_ERR_INVALID_ARG, "src_b is W_up for which == 0 and NULL for which == 1");
+  const int rows = which == 0 ? s->d_ff : s->d_model;
+  const int cols = which == 0 ? s->d_model : s->d_ff;
+  HIP_TRY("pack", launch_pack(src_a, src_b, dst, n_mats, rows, cols, w_size(s), stream));
+  return MOE_OK;
+}
+
+size_t moe_workspace_bytes(const moe_shape_t* s) {
+  if (check_shape(s) != MOE_OK) return (size_t)-1;
+  if (s->n_tokens == 0) return 0;
+  return ws_layout(s).total;
+}
+
+moe_status_t moe_router_topk(const moe_shape_t* s, const void* x, const moe_weights_t* w,
+                             int32_t* topk_idx, float* topk_w, void* ws, size_t ws_bytes,
+                             hipStream_t stream) {
+  moe_status_t st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (s->n_tokens == 0) return MOE_OK;
+  if ((st = check_weights(s, w, true, false)) != MOE_OK) return st;
+  if (!x || !topk_idx || !topk_w) return fail(MOE_ERR_INVALID_ARG, "x / topk_idx / topk_w is NULL");
+  if ((st = check_ws(s, ws, ws_bytes)) != MOE_OK) return st;
+  const WsLayout L = ws_layout(s);
+  return run_router(s, x, w, topk_idx, topk_w,
+                    reinterpret_cast<float*>(static_cast<char*>(ws) + L.logits), stream);
+}
+
+moe_status_t moe_permute(const moe_shape_t* s, const int32_t* topk_idx, const void* x,
+                         moe_routing_t* out, void* x_perm, hipStream_t stream) {
+  moe_status_t st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (!out || !out->counts || !out->offsets || !out->perm_token || !out->inv_perm)
+    return fail(MOE_ERR_INVALID_ARG, "routing counts / offsets / perm_token / inv_perm is NULL");
+  if (!topk_idx) return fail(MOE_ERR_INVALID_ARG, "topk_idx is NULL");
+  if (x_perm && !x) return fail(MOE_ERR_INVALID_ARG, "x_perm needs x");
+  // T == 0 still yields well-defined (zero) counts and offsets
+  HIP_TRY("permute", launch_permute(topk_idx, s->n_tokens, s->top_k, s->n_experts, out->counts,
+                                    out->offsets, out->perm_token, out->inv_perm, stream));
+  if (x_perm && s->n_tokens > 0)
+    HIP_TRY("gather", launch_gather_rows(x, out->perm_token, x_perm, s->n_tokens * s->top_k,
+                                         s->d_model * act_size(s), stream));
+  return MOE_OK;
+}
+
+moe_status_t moe_grouped_ffn(const moe_shape_t* s, const void* x, const void* x_perm,
+                             const int32_t* perm_token, const int32_t* offsets,
+                             const moe_weights_t* w, void* y_perm, void* y_shared, void* ws,
+                             size_t ws_bytes, hipStream_t stream) {
+  moe_status_t st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (s->n_tokens == 0) return MOE_OK;
+  if ((st = check_weights(s, w, false, true)) != MOE_OK) return st;
+  if (!offsets || !y_perm) return fail(MOE_ERR_INVALID_ARG, "offsets / y_perm is NULL");
+  if (!x_perm && (!x || !perm_token))
+    return fail(MOE_ERR_INVALID_ARG, "without x_perm, x and perm_token are required");
+  if (s->n_shared && (!x || !y_shared))
+    return fail(MOE_ERR_INVALID_ARG, "the shared expert needs x and y_shared");
+  if ((st = check_ws(s, ws, ws_bytes)) != MOE_OK) return st;
+  const WsLayout L = ws_layout(s);
+  char* b = static_cast<char*>(ws);
+  return run_ffn(s, x, x_perm ? x_perm : x, x_perm ? nullptr : perm_token, offsets, w, b + L.H,
+                 b + L.H_sh, y_perm, y_shared, 3, stream);
+}
+
+moe_status_t moe_expert_gate_up(const moe_shape_t* s, const void* x, const void* x_perm,
+                                const int32_t* perm_token, const int32_t* offsets,
+                                const moe_weights_t* w, void* h, void* h_shared,
+                                hipStream_t stream) {
+  moe_status_t st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (s->n_tokens == 0) return MOE_OK;
+  if ((st = check_weights(s, w, false, true)) != MOE_OK) return st;
+  if (!offsets || !h) return fail(MOE_ERR_INVALID_ARG, "offsets / h is NULL");
+  if (!x_perm && (!x || !perm_token))
+    return fail(MOE_ERR_INVALID_ARG, "without x_perm, x and perm_token are required");
+  if (s->n_shared && (!x || !h_shared))
+    return fail(MOE_ERR_INVALID_ARG, "the shared expert needs x and h_shared");
+  return run_ffn(s, x, x_perm ? x_perm : x, x_perm ? nullptr : perm_token, offsets, w, h,
+                 h_shared, nullptr, nullptr, 1, stream);
+}
+
+moe_status_t moe_expert_down(const moe_shape_t* s, const void* h, const void* h_shared,
+                             const int32_t* offsets, const moe_weights_t* w, void* y_perm,
+                             void* y_shared, hipStream_t stream) {
+  moe_status_t st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (s->n_tokens == 0) return MOE_OK;
+  if ((st = check_weights(s, w, false, true)) != MOE_OK) return st;
+  if (!offsets || !h || !y_perm) return fail(MOE_ERR_INVALID_ARG, "offsets / h / y_perm is NULL");
+  if (s->n_shared && (!h_shared || !y_shared))
+    return fail(MOE_ERR_INVALID_ARG, "the shared expert needs h_shared and y_shared");
+  return run_ffn(s, nullptr, nullptr, nullptr, offsets, w, const_cast<void*>(h),
+                 const_cast<void*>(h_shared), y_perm, y_shared, 2, stream);
+}
+
+moe_status_t moe_combine(const moe_shape_t* s, const void* y_perm, const void* y_shared,
+                         const int32_t* inv_perm, const float* topk_w, void* out,
+                         hipStream_t stream) {
+  moe_status_t st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (s->n_tokens == 0) return MOE_OK;
+  if (!y_perm || !inv_perm || !topk_w || !out)
+    return fail(MOE_ERR_INVALID_ARG, "y_perm / inv_perm / topk_w / out is NULL");
+  if (s->n_shared && !y_shared) return fail(MOE_ERR_INVALID_ARG, "n_shared == 1 needs y_shared");
+  HIP_TRY("combine", launch_combine(y_perm, s->n_shared ? y_shared : nullptr, inv_perm, topk_w,
+                                    out, s->n_tokens, s->top_k, s->d_model,
+                                    s->act_dtype == MOE_BF16, stream));
+  return MOE_OK;
+}
+
+moe_status_t moe_layer_forward(const moe_shape_t* s, const moe_weights_t* w, const void* x,
+                               void* out, moe_routing_t* r, void* ws, size_t ws_bytes,
+                               hipStream_t stream) {
+  moe_status_t st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (s->n_tokens == 0) return MOE_OK;
+  if ((st = check_weights(s, w, true, true)) != MOE_OK) return st;
+  if (!x || !out) return fail(MOE_ERR_INVALID_ARG, "x / out is NULL");
+  if (x == out) return fail(MOE_ERR_INVALID_ARG, "x and out must not overlap");
+  if ((st = check_ws(s, ws, ws_bytes)) != MOE_OK) return st;
+  const WsLayout L = ws_layout(s);
+  char* b = static_cast<char*>(ws);
+  int32_t* idx = (r && r->topk_idx) ? r->topk_idx : reinterpret_cast<int32_t*>(b + L.idx);
+  float* gw = (r && r->topk_w) ? r->topk_w : reinterpret_cast<float*>(b + L.w);
+  int32_t* counts = (r && r->counts) ? r->counts : reinterpret_cast<int32_t*>(b + L.counts);
+  int32_t* offs = (r && r->offsets) ? r->offsets : reinterpret_cast<int32_t*>(b + L.offsets);
+  int32_t* perm = (r && r->perm_token) ? r->perm_token : reinterpret_cast<int32_t*>(b + L.perm);
+  int32_t* inv = (r && r->inv_perm) ? r->inv_perm : reinterpret_cast<int32_t*>(b + L.inv);
+
+  if ((st = run_router(s, x, w, idx, gw, reinterpret_cast<float*>(b + L.logits), stream)) != MOE_OK)
+    return st;
+  HIP_TRY("permute", launch_permute(idx, s->n_tokens, s->top_k, s->n_experts, counts, offs, perm,
+                                    inv, stream));
+  if ((st = run_ffn(s, x, x, perm, offs, w, b + L.H, b + L.H_sh, b + L.Y, b + L.Y_sh, 3,
+                    stream)) != MOE_OK)
+    return st;
+  HIP_TRY("combine", launch_combine(b + L.Y, s->n_shared ? b + L.Y_sh : nullptr, inv, gw, out,
+                                    s->n_tokens, s->top_k, s->d_model, s->act_dtype == MOE_BF16,
+                                    stream));
+  return MOE_OK;
+}
+
+}  // extern "C"

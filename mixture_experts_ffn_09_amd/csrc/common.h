@@ -1,0 +1,58 @@
+// Shared device helpers of the gfx950 MoE FFN kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float floatx4_t;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float floatx16_t;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4_t;
+typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2_t;
+
+#define MOE_WAVE 64
+#define MOE_MAX_EXPERTS 1024
+#define MOE_FP8_BLOCK 128
+
+// bfloat16 <-> float32.  bf16 is the top half of a binary32 word.
+__device__ __forceinline__ float bf16_to_f32(uint32_t b16) {
+  return __uint_as_float(b16 << 16);
+}
+
+// Round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+}
+
+// Logistic function in float32 (no overflow: exp of a non-positive value).
+__device__ __forceinline__ float sigmoid_f32(float z) {
+  float e = __expf(-fabsf(z));
+  float p = 1.0f / (1.0f + e);
+  return z >= 0.0f ? p : e * p;
+}
+
+__device__ __forceinline__ float silu_f32(float z) { return z * sigmoid_f32(z); }
+
+// Two OCP E4M3 codes (the low or high 16 bits of `w`) -> two bf16 in one
+// dword.  E4M3 values are exact in bf16, so the conversion is exact.
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w) {
+  typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
+  bf16x2_t v = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI);
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ floatx4_t mfma16x16x32(const u32x4_t& a, const u32x4_t& b,
+                                                  floatx4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+__host__ __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }

@@ -1,0 +1,81 @@
+// Host-side launchers of the gfx950 kernels (each returns the launch
+// status; none synchronises).  Pointers are device pointers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+// Router logits s[T][N] = x[T][d] @ W[d][N] (+ offset[N]) in float32.
+// act_bf16: x is bfloat16 (else float32).
+hipError_t launch_router_logits(const void* x, bool act_bf16, const float* w_router,
+                                const float* offset, float* logits, int T, int d, int N,
+                                hipStream_t st);
+
+// Top-k selection and gates from float32 logits (one wave per token).
+hipError_t launch_router_topk(const float* logits, const float* select_bias, int sigmoid,
+                              int T, int N, int k, int32_t* topk_idx, float* topk_w,
+                              hipStream_t st);
+
+// Counts, offsets and the stable (expert, token) permutation.
+hipError_t launch_permute(const int32_t* topk_idx, int T, int k, int N, int32_t* counts,
+                          int32_t* offsets, int32_t* perm_token, int32_t* inv_perm,
+                          hipStream_t st);
+
+// x_perm[r] = x[perm_token[r]] for r < rows (row_bytes per row).
+hipError_t launch_gather_rows(const void* x, const int32_t* perm_token, void* x_perm,
+                              int rows, int row_bytes, hipStream_t st);
+
+// Expert FFN.  Routed expert e owns rows [offsets[e], offsets[e+1]); its
+// input row r is x_rows[perm_token[r]] (perm_token given) or x_rows[r]
+// (x_rows already expert-contiguous).  The shared expert (n_shared == 1)
+// reads x_sh[t] for t < T.  Outputs: H / Y (routed, row r), H_sh / Y_sh
+// (shared, row t).
+struct FfnArgs {
+  const uint16_t* x_rows;
+  const int32_t* perm_token;
+  const uint16_t* x_sh;
+  const int32_t* offsets;
+  int T, N, n_shared, d, d_ff;
+  bool fp8;
+  const void* w13;
+  const void* w2;
+  const float* s13;
+  const float* s2;
+  const void* w13_sh;
+  const void* w2_sh;
+  const float* s13_sh;
+  const float* s2_sh;
+  uint16_t* H;
+  uint16_t* H_sh;
+  uint16_t* Y;
+  uint16_t* Y_sh;
+};
+// pass: 1 = gate/up + SwiGLU only, 2 = down only, 3 = both.
+hipError_t launch_ffn_lowp(const FfnArgs& a, int pass, hipStream_t st);
+
+// Float32 expert FFN (float32 activations and weights), same row scheme.
+struct FfnF32Args {
+  const float* x_rows;
+  const int32_t* perm_token;
+  const float* x_sh;
+  const int32_t* offsets;
+  int T, N, n_shared, d, d_ff, max_rows;
+  const float* w13;           // [N][2][d_ff][d]
+  const float* w2;            // [N][d][d_ff]
+  const float* w13_sh;
+  const float* w2_sh;
+  float* H;
+  float* H_sh;
+  float* Y;
+  float* Y_sh;
+};
+hipError_t launch_ffn_f32(const FfnF32Args& a, int pass, hipStream_t st);
+
+// out[t] = sum_i g[t,i] * Y[inv[t,i]] (+ Ys[t]).
+hipError_t launch_combine(const void* y_perm, const void* y_shared, const int32_t* inv_perm,
+                          const float* topk_w, void* out, int T, int k, int d, bool act_bf16,
+                          hipStream_t st);
+
+// Weight repack (see moe_pack_weights).  esize: 4 (f32), 2 (bf16), 1 (fp8).
+hipError_t launch_pack(const void* src_a, const void* src_b, void* dst, int n_mats, int rows,
+                       int cols, int esize, hipStream_t st);

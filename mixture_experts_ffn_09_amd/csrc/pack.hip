@@ -1,0 +1,77 @@
+// One-time repack of expert weights from [out][in] row-major into the
+// streaming kernels' block layout.
+//
+// A block covers 16 output rows and one K step (32 inputs for bf16, 64 for
+// FP8) and is 1 KB: 64 lanes x 16 bytes, lane l holding row l % 16 and the
+// 8 (bf16) or 2 x 8 (FP8: k-steps 2s and 2s+1 of 32) consecutive inputs
+// starting at 8 * (l / 16) - exactly its MFMA B operand.  Blocks are ordered
+// (expert, row block, K step, matrix) with matrix = gate, up for the fused
+// gate/up weight, so one row block's stream along K is contiguous.
+
+#include "common.h"
+#include "kernels.h"
+
+namespace {
+
+__global__ __launch_bounds__(256) void pack_kernel(const uint8_t* __restrict__ a,
+                                                   const uint8_t* __restrict__ b,
+                                                   uint8_t* __restrict__ dst, int n_mats,
+                                                   int rows, int cols, int esize, int nh,
+                                                   size_t total_chunks) {
+  const size_t c = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (c >= total_chunks) return;
+  const int lane = (int)(c & 63);
+  size_t blk = c >> 6;
+  const int ksteps = esize == 2 ? cols / 32 : cols / 64;
+  const int h = (int)(blk % nh);
+  blk /= nh;
+  const int ks = (int)(blk % ksteps);
+  blk /= ksteps;
+  const int nb = (int)(blk % (rows / 16));
+  const size_t e = blk / (rows / 16);
+  const uint8_t* src = (h ? b : a) + e * (size_t)rows * cols * esize;
+  const int row = nb * 16 + (lane & 15);
+  uint8_t* out = dst + c * 16;
+  if (esize == 2) {
+    const int col = ks * 32 + (lane >> 4) * 8;
+    *reinterpret_cast<uint4*>(out) =
+        *reinterpret_cast<const uint4*>(src + ((size_t)row * cols + col) * 2);
+  } else {
+    const int col = ks * 64 + (lane >> 4) * 8;
+    const uint8_t* s = src + (size_t)row * cols + col;
+    *reinterpret_cast<uint2*>(out) = *reinterpret_cast<const uint2*>(s);
+    *reinterpret_cast<uint2*>(out + 8) = *reinterpret_cast<const uint2*>(s + 32);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_pack(const void* src_a, const void* src_b, void* dst, int n_mats, int rows,
+                       int cols, int esize, hipStream_t st) {
+  const int nh = src_b ? 2 : 1;
+  const size_t bytes = (size_t)n_mats * nh * rows * cols * esize;
+  if (esize == 4) {
+    // float32 weights keep the natural layout: gate block then up block
+    const size_t one = (size_t)rows * cols * 4;
+    for (int e = 0; e < n_mats; ++e) {
+      hipError_t r = hipMemcpyAsync(static_cast<uint8_t*>(dst) + (size_t)e * nh * one,
+                                    static_cast<const uint8_t*>(src_a) + (size_t)e * one, one,
+                                    hipMemcpyDeviceToDevice, st);
+      if (r != hipSuccess) return r;
+      if (nh == 2) {
+        r = hipMemcpyAsync(static_cast<uint8_t*>(dst) + (size_t)e * nh * one + one,
+                           static_cast<const uint8_t*>(src_b) + (size_t)e * one, one,
+                           hipMemcpyDeviceToDevice, st);
+        if (r != hipSuccess) return r;
+      }
+    }
+    return hipSuccess;
+  }
+  const size_t chunks = bytes / 16;
+  const size_t grid = (chunks + 255) / 256;
+  pack_kernel<<<dim3((unsigned)grid), 256, 0, st>>>(static_cast<const uint8_t*>(src_a),
+                                                    static_cast<const uint8_t*>(src_b),
+                                                    static_cast<uint8_t*>(dst), n_mats, rows,
+                                                    cols, esize, nh, chunks);
+  return hipGetLastError();
+}

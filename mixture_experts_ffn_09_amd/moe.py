@@ -1,0 +1,199 @@
+"""ctypes binding of ``libmoe_ffn.so`` (C ABI in ``include/moe_ffn.h``).
+
+Argument marshalling only: every step of the layer runs in the HIP library.
+Tensors are torch tensors used as device memory; calls go to the current
+torch CUDA (HIP) stream.  A missing library raises; there is no fallback.
+Function names match the C entry points.
+"""
+
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.environ.get("MOE_FFN_LIB", os.path.join(_HERE, "libmoe_ffn.so"))
+
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE_TOO_SMALL, MOE_ERR_HIP = range(5)
+MOE_F32, MOE_BF16, MOE_FP8_E4M3 = range(3)
+MOE_ROUTE_SOFTMAX_TOPK, MOE_ROUTE_SIGMOID_BIAS = range(2)
+
+DTYPE_CODES = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8": MOE_FP8_E4M3}
+ROUTE_CODES = {"softmax": MOE_ROUTE_SOFTMAX_TOPK, "sigmoid": MOE_ROUTE_SIGMOID_BIAS}
+
+EXPORTS = ["moe_packed_weight_bytes", "moe_pack_weights", "moe_workspace_bytes",
+           "moe_router_topk", "moe_permute", "moe_grouped_ffn", "moe_expert_gate_up",
+           "moe_expert_down", "moe_combine", "moe_layer_forward", "moe_status_string",
+           "moe_last_error"]
+
+
+class MoEError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"[{status}] {message}")
+        self.status = status
+
+
+class Shape(C.Structure):
+    _fields_ = [("n_tokens", C.c_int32), ("d_model", C.c_int32), ("n_experts", C.c_int32),
+                ("top_k", C.c_int32), ("d_ff", C.c_int32), ("n_shared", C.c_int32),
+                ("route", C.c_int32), ("act_dtype", C.c_int32), ("w_dtype", C.c_int32)]
+
+
+class Weights(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in (
+        "w_router", "logit_offset", "select_bias", "w13", "w2", "w13_scale", "w2_scale",
+        "w13_shared", "w2_shared", "w13_shared_scale", "w2_shared_scale")]
+
+
+class Routing(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in (
+        "topk_idx", "topk_w", "counts", "offsets", "perm_token", "inv_perm")]
+
+
+_lib = None
+
+
+def lib() -> C.CDLL:
+    """Open the HIP library once; raise if it is not built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built: run python -m mixture_experts_ffn_09_amd.build")
+        L = C.CDLL(LIB_PATH)
+        P, S, I = C.c_void_p, C.POINTER(Shape), C.c_int
+        L.moe_packed_weight_bytes.argtypes = [S, I, I]
+        L.moe_packed_weight_bytes.restype = C.c_size_t
+        L.moe_pack_weights.argtypes = [S, I, I, P, P, P, P]
+        L.moe_workspace_bytes.argtypes = [S]
+        L.moe_workspace_bytes.restype = C.c_size_t
+        L.moe_router_topk.argtypes = [S, P, C.POINTER(Weights), P, P, P, C.c_size_t, P]
+        L.moe_permute.argtypes = [S, P, P, C.POINTER(Routing), P, P]
+        L.moe_grouped_ffn.argtypes = [S, P, P, P, P, C.POINTER(Weights), P, P, P, C.c_size_t, P]
+        L.moe_expert_gate_up.argtypes = [S, P, P, P, P, C.POINTER(Weights), P, P, P]
+        L.moe_expert_down.argtypes = [S, P, P, P, C.POINTER(Weights), P, P, P]
+        L.moe_combine.argtypes = [S, P, P, P, P, P, P]
+        L.moe_layer_forward.argtypes = [S, C.POINTER(Weights), P, P, C.POINTER(Routing), P,
+                                        C.c_size_t, P]
+        for f in ("moe_pack_weights", "moe_router_topk", "moe_permute", "moe_grouped_ffn",
+                  "moe_expert_gate_up", "moe_expert_down", "moe_combine", "moe_layer_forward"):
+            getattr(L, f).restype = C.c_int
+        L.moe_status_string.argtypes = [C.c_int]
+        L.moe_status_string.restype = C.c_char_p
+        L.moe_last_error.argtypes = []
+        L.moe_last_error.restype = C.c_char_p
+        _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != MOE_OK:
+        L = lib()
+        raise MoEError(status, f"{L.moe_status_string(status).decode()}: {L.moe_last_error().decode()}")
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("expected a torch tensor")
+    if not t.is_cuda:
+        raise ValueError("tensors passed to the MoE library must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to the MoE library must be contiguous")
+    return t.data_ptr()
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def make_shape(T: int, d_model: int, n_experts: int, top_k: int, d_ff: int, n_shared: int = 0,
+               route: str = "softmax", act_dtype: str = "bf16", w_dtype: str = "bf16") -> Shape:
+    return Shape(T, d_model, n_experts, top_k, d_ff, n_shared, ROUTE_CODES[route],
+                 DTYPE_CODES[act_dtype], DTYPE_CODES[w_dtype])
+
+
+def make_weights(**tensors) -> Weights:
+    """Weights struct from device tensors (keys are the C field names)."""
+    w = Weights()
+    for k, v in tensors.items():
+        setattr(w, k, _ptr(v))
+    w._keep = tensors  # keep the tensors alive with the struct
+    return w
+
+
+def make_routing(**tensors) -> Routing:
+    r = Routing()
+    for k, v in tensors.items():
+        setattr(r, k, _ptr(v))
+    r._keep = tensors
+    return r
+
+
+def moe_packed_weight_bytes(shape: Shape, which: int, n_mats: int) -> int:
+    return int(lib().moe_packed_weight_bytes(C.byref(shape), which, n_mats))
+
+
+def moe_workspace_bytes(shape: Shape) -> int:
+    v = int(lib().moe_workspace_bytes(C.byref(shape)))
+    if v == C.c_size_t(-1).value:
+        raise MoEError(MOE_ERR_INVALID_ARG, lib().moe_last_error().decode())
+    return v
+
+
+def moe_pack_weights(shape: Shape, which: int, n_mats: int, src_a: torch.Tensor,
+                     src_b: Optional[torch.Tensor], dst: torch.Tensor):
+    _check(lib().moe_pack_weights(C.byref(shape), which, n_mats, _ptr(src_a), _ptr(src_b),
+                                  _ptr(dst), _stream()))
+
+
+def moe_router_topk(shape: Shape, x: torch.Tensor, weights: Weights, topk_idx: torch.Tensor,
+                    topk_w: torch.Tensor, ws: torch.Tensor):
+    _check(lib().moe_router_topk(C.byref(shape), _ptr(x), C.byref(weights), _ptr(topk_idx),
+                                 _ptr(topk_w), _ptr(ws), ws.numel() * ws.element_size(),
+                                 _stream()))
+
+
+def moe_permute(shape: Shape, topk_idx: torch.Tensor, x: Optional[torch.Tensor],
+                routing: Routing, x_perm: Optional[torch.Tensor] = None):
+    _check(lib().moe_permute(C.byref(shape), _ptr(topk_idx), _ptr(x), C.byref(routing),
+                             _ptr(x_perm), _stream()))
+
+
+def moe_grouped_ffn(shape: Shape, x: Optional[torch.Tensor], x_perm: Optional[torch.Tensor],
+                    perm_token: Optional[torch.Tensor], offsets: torch.Tensor, weights: Weights,
+                    y_perm: torch.Tensor, y_shared: Optional[torch.Tensor], ws: torch.Tensor):
+    _check(lib().moe_grouped_ffn(C.byref(shape), _ptr(x), _ptr(x_perm), _ptr(perm_token),
+                                 _ptr(offsets), C.byref(weights), _ptr(y_perm), _ptr(y_shared),
+                                 _ptr(ws), ws.numel() * ws.element_size(), _stream()))
+
+
+def moe_expert_gate_up(shape: Shape, x: Optional[torch.Tensor], x_perm: Optional[torch.Tensor],
+                       perm_token: Optional[torch.Tensor], offsets: torch.Tensor,
+                       weights: Weights, h: torch.Tensor, h_shared: Optional[torch.Tensor]):
+    _check(lib().moe_expert_gate_up(C.byref(shape), _ptr(x), _ptr(x_perm), _ptr(perm_token),
+                                    _ptr(offsets), C.byref(weights), _ptr(h), _ptr(h_shared),
+                                    _stream()))
+
+
+def moe_expert_down(shape: Shape, h: torch.Tensor, h_shared: Optional[torch.Tensor],
+                    offsets: torch.Tensor, weights: Weights, y_perm: torch.Tensor,
+                    y_shared: Optional[torch.Tensor]):
+    _check(lib().moe_expert_down(C.byref(shape), _ptr(h), _ptr(h_shared), _ptr(offsets),
+                                 C.byref(weights), _ptr(y_perm), _ptr(y_shared), _stream()))
+
+
+def moe_combine(shape: Shape, y_perm: torch.Tensor, y_shared: Optional[torch.Tensor],
+                inv_perm: torch.Tensor, topk_w: torch.Tensor, out: torch.Tensor):
+    _check(lib().moe_combine(C.byref(shape), _ptr(y_perm), _ptr(y_shared), _ptr(inv_perm),
+                             _ptr(topk_w), _ptr(out), _stream()))
+
+
+def moe_layer_forward(shape: Shape, weights: Weights, x: torch.Tensor, out: torch.Tensor,
+                      ws: torch.Tensor, routing: Optional[Routing] = None):
+    _check(lib().moe_layer_forward(C.byref(shape), C.byref(weights), _ptr(x), _ptr(out),
+                                   C.byref(routing) if routing is not None else None, _ptr(ws),
+                                   ws.numel() * ws.element_size(), _stream()))

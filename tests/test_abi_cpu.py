@@ -1,0 +1,161 @@
+"""The C ABI without a GPU: the library loads, exports what the header
+declares, and rejects bad arguments on the host before any HIP call."""
+
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from mixture_experts_ffn_09_amd import moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_ffn.h")
+
+FAKE = C.c_void_p(0x1000)  # never dereferenced: every call below fails validation first
+
+
+def _lib():
+    if not os.path.exists(moe.LIB_PATH):
+        pytest.fail("libmoe_ffn.so is not built (python -m mixture_experts_ffn_09_amd.build)")
+    return moe.lib()
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_header_declares_the_entry_points():
+    names = _declared()
+    for n in ("moe_router_topk", "moe_permute", "moe_grouped_ffn", "moe_combine",
+              "moe_layer_forward"):
+        assert n in names
+    assert set(names) == set(moe.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = _lib()
+    for n in _declared():
+        assert hasattr(L, n), n
+
+
+def shape(**kw):
+    base = dict(T=16, d_model=4096, n_experts=8, top_k=2, d_ff=14336)
+    base.update({k: v for k, v in kw.items() if k in base})
+    rest = {k: v for k, v in kw.items() if k not in base}
+    return moe.make_shape(base["T"], base["d_model"], base["n_experts"], base["top_k"],
+                          base["d_ff"], **rest)
+
+
+def _status(fn, *args):
+    return getattr(_lib(), fn)(*args)
+
+
+def test_status_strings():
+    L = _lib()
+    assert L.moe_status_string(0) == b"ok"
+    assert L.moe_status_string(3) == b"workspace too small"
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(top_k=0), moe.MOE_ERR_INVALID_ARG),
+    (dict(top_k=9), moe.MOE_ERR_INVALID_ARG),
+    (dict(T=-1), moe.MOE_ERR_INVALID_ARG),
+    (dict(d_model=0), moe.MOE_ERR_INVALID_ARG),
+    (dict(n_experts=600, top_k=8), moe.MOE_ERR_UNSUPPORTED),
+    (dict(n_experts=100, top_k=65), moe.MOE_ERR_UNSUPPORTED),
+    (dict(d_model=4016), moe.MOE_ERR_UNSUPPORTED),                  # bf16 needs % 32
+    (dict(w_dtype="fp8", d_ff=14336 + 64), moe.MOE_ERR_UNSUPPORTED),  # fp8 needs % 128
+    (dict(act_dtype="f32", w_dtype="bf16"), moe.MOE_ERR_UNSUPPORTED),
+    (dict(act_dtype="bf16", w_dtype="f32"), moe.MOE_ERR_UNSUPPORTED),
+    (dict(n_shared=2), moe.MOE_ERR_INVALID_ARG),
+])
+def test_bad_shapes_are_rejected(kw, code):
+    s = shape(**kw)
+    w = moe.Weights(w_router=FAKE.value, w13=FAKE.value, w2=FAKE.value)
+    st = _status("moe_layer_forward", C.byref(s), C.byref(w), FAKE, C.c_void_p(0x2000), None,
+                 FAKE, C.c_size_t(1 << 40), None)
+    assert st == code, (kw, st, _lib().moe_last_error())
+    assert _lib().moe_workspace_bytes(C.byref(s)) == C.c_size_t(-1).value
+
+
+def test_null_shape_and_pointers():
+    assert _status("moe_layer_forward", None, None, None, None, None, None, 0, None) == \
+        moe.MOE_ERR_INVALID_ARG
+    s = shape()
+    w = moe.Weights(w_router=FAKE.value, w13=FAKE.value, w2=FAKE.value)
+    ws = C.c_size_t(moe.moe_workspace_bytes(s))
+    # null x
+    assert _status("moe_layer_forward", C.byref(s), C.byref(w), None, FAKE, None, FAKE, ws,
+                   None) == moe.MOE_ERR_INVALID_ARG
+    # null router weight
+    w2 = moe.Weights(w13=FAKE.value, w2=FAKE.value)
+    assert _status("moe_layer_forward", C.byref(s), C.byref(w2), FAKE, C.c_void_p(0x2000), None,
+                   FAKE, ws, None) == moe.MOE_ERR_INVALID_ARG
+    # x == out
+    assert _status("moe_layer_forward", C.byref(s), C.byref(w), FAKE, FAKE, None, FAKE, ws,
+                   None) == moe.MOE_ERR_INVALID_ARG
+    # selection bias with the softmax router
+    w3 = moe.Weights(w_router=FAKE.value, w13=FAKE.value, w2=FAKE.value, select_bias=FAKE.value)
+    assert _status("moe_router_topk", C.byref(s), FAKE, C.byref(w3), FAKE, FAKE, FAKE, ws,
+                   None) == moe.MOE_ERR_INVALID_ARG
+    # shared expert without its weights
+    s_sh = shape(n_shared=1, route="sigmoid")
+    assert _status("moe_grouped_ffn", C.byref(s_sh), FAKE, None, FAKE, FAKE, C.byref(w), FAKE,
+                   FAKE, FAKE, C.c_size_t(1 << 40), None) == moe.MOE_ERR_INVALID_ARG
+    # fp8 without scales
+    s8 = shape(w_dtype="fp8")
+    assert _status("moe_grouped_ffn", C.byref(s8), FAKE, None, FAKE, FAKE, C.byref(w), FAKE,
+                   None, FAKE, C.c_size_t(1 << 40), None) == moe.MOE_ERR_INVALID_ARG
+    # permute without outputs
+    r = moe.Routing()
+    assert _status("moe_permute", C.byref(s), FAKE, None, C.byref(r), None, None) == \
+        moe.MOE_ERR_INVALID_ARG
+    # pack: src_b must be given exactly for the gate/up weight
+    assert _status("moe_pack_weights", C.byref(s), 0, 1, FAKE, None, FAKE, None) == \
+        moe.MOE_ERR_INVALID_ARG
+    assert _status("moe_pack_weights", C.byref(s), 1, 1, FAKE, FAKE, FAKE, None) == \
+        moe.MOE_ERR_INVALID_ARG
+    assert _status("moe_pack_weights", C.byref(s), 2, 1, FAKE, None, FAKE, None) == \
+        moe.MOE_ERR_INVALID_ARG
+
+
+def test_workspace_too_small():
+    s = shape()
+    w = moe.Weights(w_router=FAKE.value, w13=FAKE.value, w2=FAKE.value)
+    need = moe.moe_workspace_bytes(s)
+    st = _status("moe_layer_forward", C.byref(s), C.byref(w), FAKE, C.c_void_p(0x2000), None,
+                 FAKE, C.c_size_t(need - 1), None)
+    assert st == moe.MOE_ERR_WORKSPACE_TOO_SMALL
+    assert b"needed" in _lib().moe_last_error()
+
+
+def test_workspace_size_formula():
+    s = shape(T=100, n_experts=256, top_k=8, d_model=7168, d_ff=2048, n_shared=1, route="sigmoid")
+    a = lambda v: (v + 255) // 256 * 256
+    T, k, N, d, f = 100, 8, 256, 7168, 2048
+    want = (a(T * N * 4) + 2 * a(T * k * 4) + a(N * 4) + a((N + 1) * 4) + 2 * a(T * k * 4)
+            + a(T * k * f * 2) + a(T * f * 2) + a(T * k * d * 2) + a(T * d * 2))
+    assert moe.moe_workspace_bytes(s) == want
+    assert moe.moe_packed_weight_bytes(s, 0, 3) == 3 * 2 * d * f * 2
+    assert moe.moe_packed_weight_bytes(s, 1, 1) == d * f * 2
+    s8 = shape(w_dtype="fp8")
+    assert moe.moe_packed_weight_bytes(s8, 1, 2) == 2 * 4096 * 14336
+
+
+def test_zero_tokens_needs_no_device():
+    s = shape(T=0)
+    assert moe.moe_workspace_bytes(s) == 0
+    w = moe.Weights()
+    assert _status("moe_layer_forward", C.byref(s), C.byref(w), None, None, None, None, 0,
+                   None) == moe.MOE_OK
+    assert _status("moe_combine", C.byref(s), None, None, None, None, None, None) == moe.MOE_OK
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(moe, "_lib", None)
+    monkeypatch.setattr(moe, "LIB_PATH", str(tmp_path / "nope.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        moe.lib()

@@ -151,10 +151,10 @@ def main():
         moe.moe_permute(s, rb["topk_idx"], None, routing)
         if ev is not None:
             ev[2].record()
-        moe.moe_expert_gate_up(s, x, None, rb["perm_token"], rb["offsets"], L.weights, h, h_sh)
+        moe.moe_expert_gate_up(s, x, None, rb["perm_token"], rb["offsets"], L.weights, h, h_sh, ws)
         if ev is not None:
             ev[3].record()
-        moe.moe_expert_down(s, h, h_sh, rb["offsets"], L.weights, y, y_sh)
+        moe.moe_expert_down(s, h, h_sh, rb["offsets"], L.weights, y, y_sh, ws)
         if ev is not None:
             ev[4].record()
         moe.moe_combine(s, y, y_sh, rb["inv_perm"], rb["topk_w"], out)

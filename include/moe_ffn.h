@@ -128,9 +128,11 @@ moe_status_t moe_pack_weights(const moe_shape_t* s, int which, int n_mats,
 /* Workspace bytes moe_layer_forward / moe_grouped_ffn / moe_router_topk need
  * for this shape (0 when n_tokens == 0); each of them checks ws_bytes against
  * it.  Returns (size_t)-1 on a bad shape.  Layout (256-byte aligned pieces):
- * logits [T][N] f32, topk idx/w, counts, offsets, perm_token, inv_perm,
- * H [T*k][d_ff] and H_shared [T][d_ff], Y [T*k][d] and Y_shared [T][d]
- * (H, Y in the activation type). */
+ * router partial logits [S][T][N] f32 (S >= 1 K-splits), topk idx/w,
+ * counts, offsets, perm_token, inv_perm, an 8 KB tile schedule, H [T*k][d_ff]
+ * and H_shared [T][d_ff], Y [T*k][d] and Y_shared [T][d] (H, Y in the
+ * activation type).  moe_expert_gate_up / moe_expert_down use only the
+ * schedule piece but check ws_bytes against the full size. */
 size_t moe_workspace_bytes(const moe_shape_t* s);
 
 /* a1+a2: router logits, selection and gates ([MoE-LLM] "Opening the
@@ -171,14 +173,16 @@ moe_status_t moe_grouped_ffn(const moe_shape_t* s, const void* x,
 moe_status_t moe_expert_gate_up(const moe_shape_t* s, const void* x,
                                 const void* x_perm, const int32_t* perm_token,
                                 const int32_t* offsets, const moe_weights_t* w,
-                                void* h, void* h_shared, hipStream_t stream);
+                                void* h, void* h_shared, void* ws,
+                                size_t ws_bytes, hipStream_t stream);
 
 /* a6 alone: y = H W_down^T per routed expert's rows (and the shared
  * expert's).  h / h_shared as written by moe_expert_gate_up. */
 moe_status_t moe_expert_down(const moe_shape_t* s, const void* h,
                              const void* h_shared, const int32_t* offsets,
                              const moe_weights_t* w, void* y_perm,
-                             void* y_shared, hipStream_t stream);
+                             void* y_shared, void* ws, size_t ws_bytes,
+                             hipStream_t stream);
 
 /* a7: out[t] = sum_{i<k} topk_w[t,i] * y_perm[inv_perm[t,i]] (+ y_shared[t])
  * in that fixed order with float32 accumulation and one rounding per output

@@ -75,7 +75,7 @@ moe_status_t check_shape(const moe_shape_t* s) {
 }
 
 struct WsLayout {
-  size_t logits, idx, w, counts, offsets, perm, inv, H, H_sh, Y, Y_sh, total;
+  size_t logits, idx, w, counts, offsets, perm, inv, sched, H, H_sh, Y, Y_sh, total;
 };
 
 WsLayout ws_layout(const moe_shape_t* s) {
@@ -88,13 +88,14 @@ WsLayout ws_layout(const moe_shape_t* s) {
   };
   const size_t T = s->n_tokens, k = s->top_k, N = s->n_experts, d = s->d_model, f = s->d_ff;
   const size_t es = act_size(s), sh = s->n_shared;
-  L.logits = take(T * N * 4);
+  L.logits = take((size_t)router_splits(s->n_tokens, s->n_experts, s->d_model) * T * N * 4);
   L.idx = take(T * k * 4);
   L.w = take(T * k * 4);
   L.counts = take(N * 4);
   L.offsets = take((N + 1) * 4);
   L.perm = take(T * k * 4);
   L.inv = take(T * k * 4);
+  L.sched = take(2048 * 4);
   L.H = take(T * k * f * es);
   L.H_sh = take(sh * T * f * es);
   L.Y = take(T * k * d * es);
@@ -134,20 +135,21 @@ moe_status_t check_weights(const moe_shape_t* s, const moe_weights_t* w, bool ro
 
 moe_status_t run_router(const moe_shape_t* s, const void* x, const moe_weights_t* w,
                         int32_t* idx, float* gw, float* logits, hipStream_t st) {
-  HIP_TRY("router_logits",
-          launch_router_logits(x, s->act_dtype == MOE_BF16, w->w_router, w->logit_offset, logits,
-                               s->n_tokens, s->d_model, s->n_experts, st));
-  HIP_TRY("router_topk", launch_router_topk(logits,
-                                            s->route == MOE_ROUTE_SIGMOID_BIAS ? w->select_bias
-                                                                               : nullptr,
-                                            s->route == MOE_ROUTE_SIGMOID_BIAS, s->n_tokens,
-                                            s->n_experts, s->top_k, idx, gw, st));
+  HIP_TRY("router_logits", launch_router_logits(x, s->act_dtype == MOE_BF16, w->w_router, logits,
+                                                s->n_tokens, s->d_model, s->n_experts, st));
+  HIP_TRY("router_topk",
+          launch_router_topk(logits, router_splits(s->n_tokens, s->n_experts, s->d_model),
+                             w->logit_offset,
+                             s->route == MOE_ROUTE_SIGMOID_BIAS ? w->select_bias : nullptr,
+                             s->route == MOE_ROUTE_SIGMOID_BIAS, s->n_tokens, s->n_experts,
+                             s->top_k, idx, gw, st));
   return MOE_OK;
 }
 
 moe_status_t run_ffn(const moe_shape_t* s, const void* x, const void* x_rows,
                      const int32_t* perm, const int32_t* offsets, const moe_weights_t* w,
-                     void* H, void* H_sh, void* y, void* y_sh, int pass, hipStream_t st) {
+                     void* H, void* H_sh, void* y, void* y_sh, void* sched, int pass,
+                     hipStream_t st) {
   if (s->w_dtype == MOE_F32) {
     FfnF32Args a{};
     a.x_rows = static_cast<const float*>(x_rows);
@@ -177,11 +179,13 @@ moe_status_t run_ffn(const moe_shape_t* s, const void* x, const void* x_rows,
   a.x_sh = static_cast<const uint16_t*>(x);
   a.offsets = offsets;
   a.T = s->n_tokens;
+  a.k = s->top_k;
   a.N = s->n_experts;
   a.n_shared = s->n_shared;
   a.d = s->d_model;
   a.d_ff = s->d_ff;
   a.fp8 = s->w_dtype == MOE_FP8_E4M3;
+  a.sched = static_cast<int32_t*>(sched);
   a.w13 = w->w13;
   a.w2 = w->w2;
   a.s13 = w->w13_scale;
@@ -290,13 +294,13 @@ moe_status_t moe_grouped_ffn(const moe_shape_t* s, const void* x, const void* x_
   const WsLayout L = ws_layout(s);
   char* b = static_cast<char*>(ws);
   return run_ffn(s, x, x_perm ? x_perm : x, x_perm ? nullptr : perm_token, offsets, w, b + L.H,
-                 b + L.H_sh, y_perm, y_shared, 3, stream);
+                 b + L.H_sh, y_perm, y_shared, b + L.sched, 3, stream);
 }
 
 moe_status_t moe_expert_gate_up(const moe_shape_t* s, const void* x, const void* x_perm,
                                 const int32_t* perm_token, const int32_t* offsets,
-                                const moe_weights_t* w, void* h, void* h_shared,
-                                hipStream_t stream) {
+                                const moe_weights_t* w, void* h, void* h_shared, void* ws,
+                                size_t ws_bytes, hipStream_t stream) {
   moe_status_t st = check_shape(s);
   if (st != MOE_OK) return st;
   if (s->n_tokens == 0) return MOE_OK;
@@ -306,13 +310,15 @@ moe_status_t moe_expert_gate_up(const moe_shape_t* s, const void* x, const void*
     return fail(MOE_ERR_INVALID_ARG, "without x_perm, x and perm_token are required");
   if (s->n_shared && (!x || !h_shared))
     return fail(MOE_ERR_INVALID_ARG, "the shared expert needs x and h_shared");
+  if ((st = check_ws(s, ws, ws_bytes)) != MOE_OK) return st;
   return run_ffn(s, x, x_perm ? x_perm : x, x_perm ? nullptr : perm_token, offsets, w, h,
-                 h_shared, nullptr, nullptr, 1, stream);
+                 h_shared, nullptr, nullptr, static_cast<char*>(ws) + ws_layout(s).sched, 1,
+                 stream);
 }
 
 moe_status_t moe_expert_down(const moe_shape_t* s, const void* h, const void* h_shared,
                              const int32_t* offsets, const moe_weights_t* w, void* y_perm,
-                             void* y_shared, hipStream_t stream) {
+                             void* y_shared, void* ws, size_t ws_bytes, hipStream_t stream) {
   moe_status_t st = check_shape(s);
   if (st != MOE_OK) return st;
   if (s->n_tokens == 0) return MOE_OK;
@@ -320,8 +326,10 @@ moe_status_t moe_expert_down(const moe_shape_t* s, const void* h, const void* h_
   if (!offsets || !h || !y_perm) return fail(MOE_ERR_INVALID_ARG, "offsets / h / y_perm is NULL");
   if (s->n_shared && (!h_shared || !y_shared))
     return fail(MOE_ERR_INVALID_ARG, "the shared expert needs h_shared and y_shared");
+  if ((st = check_ws(s, ws, ws_bytes)) != MOE_OK) return st;
   return run_ffn(s, nullptr, nullptr, nullptr, offsets, w, const_cast<void*>(h),
-                 const_cast<void*>(h_shared), y_perm, y_shared, 2, stream);
+                 const_cast<void*>(h_shared), y_perm, y_shared,
+                 static_cast<char*>(ws) + ws_layout(s).sched, 2, stream);
 }
 
 moe_status_t moe_combine(const moe_shape_t* s, const void* y_perm, const void* y_shared,
@@ -362,8 +370,8 @@ moe_status_t moe_layer_forward(const moe_shape_t* s, const moe_weights_t* w, con
     return st;
   HIP_TRY("permute", launch_permute(idx, s->n_tokens, s->top_k, s->n_experts, counts, offs, perm,
                                     inv, stream));
-  if ((st = run_ffn(s, x, x, perm, offs, w, b + L.H, b + L.H_sh, b + L.Y, b + L.Y_sh, 3,
-                    stream)) != MOE_OK)
+  if ((st = run_ffn(s, x, x, perm, offs, w, b + L.H, b + L.H_sh, b + L.Y, b + L.Y_sh,
+                    b + L.sched, 3, stream)) != MOE_OK)
     return st;
   HIP_TRY("combine", launch_combine(b + L.Y, s->n_shared ? b + L.Y_sh : nullptr, inv, gw, out,
                                     s->n_tokens, s->top_k, s->d_model, s->act_dtype == MOE_BF16,

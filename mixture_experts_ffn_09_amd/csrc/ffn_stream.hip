@@ -35,7 +35,7 @@ struct StreamParams {
   const int32_t* perm;        // null: a is already expert-contiguous
   const uint16_t* a_sh;       // shared-expert activations, row t
   const int32_t* offsets;     // [N+1]
-  int T, N;
+  int T, N, g0;
   int K;       // reduction length
   int n_out;   // output width
   const uint8_t* w;           // packed routed weights
@@ -57,16 +57,22 @@ __device__ __forceinline__ void fp8_block_to_bf16(const u32x4_t& q, u32x4_t& lo,
   hi[3] = e4m3x2_to_bf16x2<true>(q[3]);
 }
 
-// GATED: pass 1 (gate+up, SwiGLU) else pass 2 (down).
-template <int P, int MB, bool FP8, bool GATED>
+// GATED: pass 1 (gate+up, SwiGLU) else pass 2 (down).  One wave owns one
+// 16-row output block and walks K with a ring of D K-steps of loads in
+// flight (each step: NH weight blocks of 1 KB plus MB activation fragments).
+// Activation rows past the group's end are clamped to its last row: row m of
+// an MFMA result depends only on row m of A, and those rows are not stored.
+template <int MB, int D, bool FP8, bool GATED>
 __global__ __launch_bounds__(256) void ffn_stream_kernel(StreamParams p) {
-  constexpr int NH = GATED ? 2 : 1;  // weight blocks per output block
+  constexpr int NH = GATED ? 2 : 1;
+  constexpr int AF = FP8 ? 2 : 1;  // activation fragments per K step
+  static_assert(!FP8 || D % 2 == 0, "FP8 needs an even ring depth");
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int g = blockIdx.y;
+  const int g = p.g0 + blockIdx.y;
   const int NB = p.n_out / 16;
-  const int nb0 = (blockIdx.x * SW_WAVES + wave) * P;
-  if (nb0 >= NB) return;
+  const int nb = blockIdx.x * SW_WAVES + wave;
+  if (nb >= NB) return;
 
   const bool shared = g >= p.N;
   int row_base, rows;
@@ -80,164 +86,157 @@ __global__ __launch_bounds__(256) void ffn_stream_kernel(StreamParams p) {
   if (rows <= 0) return;
   uint16_t* out = shared ? p.out_sh : p.out;
 
-  // per-expert packed bytes and scale counts
   const size_t wbytes = (size_t)NH * p.n_out * p.K * (FP8 ? 1 : 2);
   const uint8_t* W = shared ? p.w_sh : p.w + (size_t)g * wbytes;
-  const int KS = FP8 ? p.K / 64 : p.K / 32;     // K steps of one 1 KB block
-  const int SK = p.K / MOE_FP8_BLOCK;           // scale columns
-  const int SR = p.n_out / MOE_FP8_BLOCK;       // scale rows per matrix
+  const int KS = FP8 ? p.K / 64 : p.K / 32;
+  const uint8_t* Wnb = W + (size_t)nb * KS * NH * 1024 + lane * 16;
+  const int SK = p.K / MOE_FP8_BLOCK;
+  const int SR = p.n_out / MOE_FP8_BLOCK;
   const float* S = nullptr;
-  if (FP8) S = shared ? p.s_sh : p.s + (size_t)g * NH * SR * SK;
+  if (FP8) S = (shared ? p.s_sh : p.s + (size_t)g * NH * SR * SK) + (size_t)((nb * 16) / MOE_FP8_BLOCK) * SK;
 
-  const int lrow = lane & 15;   // A row / B column within a block
+  const int lrow = lane & 15;
   const int lk = (lane >> 4) * 8;
 
   for (int m0 = 0; m0 < rows; m0 += 16 * MB) {
-    // activation row pointers of this lane, one per 16-row block
     const uint16_t* arow[MB];
-    bool av[MB];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
-      int r = m0 + mb * 16 + lrow;
-      av[mb] = r < rows;
-      const uint16_t* ptr = p.a;
-      if (av[mb]) {
-        if (shared)
-          ptr = p.a_sh + (size_t)r * p.K;
-        else if (p.perm)
-          ptr = p.a + (size_t)p.perm[row_base + r] * p.K;
-        else
-          ptr = p.a + (size_t)(row_base + r) * p.K;
-      }
+      const int r = min(m0 + mb * 16 + lrow, rows - 1);
+      const uint16_t* ptr;
+      if (shared)
+        ptr = p.a_sh + (size_t)r * p.K;
+      else if (p.perm)
+        ptr = p.a + (size_t)p.perm[row_base + r] * p.K;
+      else
+        ptr = p.a + (size_t)(row_base + r) * p.K;
       arow[mb] = ptr + lk;
     }
 
-    floatx4_t acc[P][NH][MB];
+    floatx4_t acc[NH][MB];
+    floatx4_t part[NH][MB];
 #pragma unroll
-    for (int i = 0; i < P; ++i)
+    for (int h = 0; h < NH; ++h)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        acc[h][mb] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+        part[h][mb] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+      }
+
+    u32x4_t bq[D][NH];
+    u32x4_t aq[D][MB][AF];
+    auto load_step = [&](int u, int ks) {
 #pragma unroll
       for (int h = 0; h < NH; ++h)
+        bq[u][h] = *reinterpret_cast<const u32x4_t*>(Wnb + ((size_t)ks * NH + h) * 1024);
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) acc[i][h][mb] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int f = 0; f < AF; ++f)
+          aq[u][mb][f] = *reinterpret_cast<const u32x4_t*>(arow[mb] + ks * (32 * AF) + f * 32);
+    };
+#pragma unroll
+    for (int u = 0; u < D; ++u) load_step(u, min(u, KS - 1));
+    // keep the ring: the scheduler must not sink loads next to their use
+    __builtin_amdgcn_sched_barrier(0);
 
-    const u32x4_t zero4 = {0u, 0u, 0u, 0u};
-
-    if (!FP8) {
-#pragma unroll 4
-      for (int ks = 0; ks < KS; ++ks) {
-        u32x4_t b[P][NH];
+    for (int ks0 = 0; ks0 < KS; ks0 += D) {
 #pragma unroll
-        for (int i = 0; i < P; ++i)
+      for (int u = 0; u < D; ++u) {
+        const int ks = ks0 + u;  // KS is a multiple of D: no bounds branch
+        {
+          if (!FP8) {
 #pragma unroll
-          for (int h = 0; h < NH; ++h) {
-            const size_t blk = ((size_t)(nb0 + i) * KS + ks) * NH + h;
-            b[i][h] = (nb0 + i < NB)
-                          ? *reinterpret_cast<const u32x4_t*>(W + blk * 1024 + lane * 16)
-                          : zero4;
-          }
-        u32x4_t a[MB];
+            for (int h = 0; h < NH; ++h)
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-          a[mb] = av[mb] ? *reinterpret_cast<const u32x4_t*>(arow[mb] + ks * 32) : zero4;
-#pragma unroll
-        for (int i = 0; i < P; ++i)
-#pragma unroll
-          for (int h = 0; h < NH; ++h)
-#pragma unroll
-            for (int mb = 0; mb < MB; ++mb)
-              acc[i][h][mb] = mfma16x16x32(a[mb], b[i][h], acc[i][h][mb]);
-      }
-    } else {
-      // FP8: K in chunks of 128 (two 1 KB steps of 64); per chunk a fresh
-      // partial sum is scaled by its block scale and added.
-      for (int kc = 0; kc < SK; ++kc) {
-        floatx4_t part[P][NH][MB];
-#pragma unroll
-        for (int i = 0; i < P; ++i)
-#pragma unroll
-          for (int h = 0; h < NH; ++h)
-#pragma unroll
-            for (int mb = 0; mb < MB; ++mb) part[i][h][mb] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const int ks = kc * 2 + half;
-          u32x4_t b[P][NH];
-#pragma unroll
-          for (int i = 0; i < P; ++i)
-#pragma unroll
-            for (int h = 0; h < NH; ++h) {
-              const size_t blk = ((size_t)(nb0 + i) * KS + ks) * NH + h;
-              b[i][h] = (nb0 + i < NB)
-                            ? *reinterpret_cast<const u32x4_t*>(W + blk * 1024 + lane * 16)
-                            : zero4;
-            }
-          u32x4_t a0[MB], a1[MB];
-#pragma unroll
-          for (int mb = 0; mb < MB; ++mb) {
-            a0[mb] = av[mb] ? *reinterpret_cast<const u32x4_t*>(arow[mb] + ks * 64) : zero4;
-            a1[mb] = av[mb] ? *reinterpret_cast<const u32x4_t*>(arow[mb] + ks * 64 + 32) : zero4;
-          }
-#pragma unroll
-          for (int i = 0; i < P; ++i)
+              for (int mb = 0; mb < MB; ++mb)
+                acc[h][mb] = mfma16x16x32(aq[u][mb][0], bq[u][h], acc[h][mb]);
+          } else {
 #pragma unroll
             for (int h = 0; h < NH; ++h) {
               u32x4_t blo, bhi;
-              fp8_block_to_bf16(b[i][h], blo, bhi);
+              fp8_block_to_bf16(bq[u][h], blo, bhi);
 #pragma unroll
               for (int mb = 0; mb < MB; ++mb) {
-                part[i][h][mb] = mfma16x16x32(a0[mb], blo, part[i][h][mb]);
-                part[i][h][mb] = mfma16x16x32(a1[mb], bhi, part[i][h][mb]);
+                part[h][mb] = mfma16x16x32(aq[u][mb][0], blo, part[h][mb]);
+                part[h][mb] = mfma16x16x32(aq[u][mb][AF - 1], bhi, part[h][mb]);
               }
             }
-        }
+            // every second 64-wide step closes a 128-wide scale block (D is
+            // even and ks0 a multiple of D, so ks and u have the same parity)
+            if (u & 1) {
+              const int kc = ks >> 1;
 #pragma unroll
-        for (int i = 0; i < P; ++i)
+              for (int h = 0; h < NH; ++h) {
+                const float sc = S[(size_t)h * SR * SK + kc];
 #pragma unroll
-          for (int h = 0; h < NH; ++h) {
-            const int srow = ((nb0 + i) * 16) / MOE_FP8_BLOCK;
-            const float sc = (nb0 + i < NB) ? S[((size_t)h * SR + srow) * SK + kc] : 0.f;
+                for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
-            for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-              for (int e = 0; e < 4; ++e) acc[i][h][mb][e] += sc * part[i][h][mb][e];
+                  for (int e = 0; e < 4; ++e) acc[h][mb][e] += sc * part[h][mb][e];
+                  part[h][mb] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+                }
+              }
+            }
           }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        load_step(u, min(ks + D, KS - 1));
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
 
     // epilogue: lane holds rows 4*(lane/16)+e of column lane%16
+    const int n = nb * 16 + lrow;
 #pragma unroll
-    for (int i = 0; i < P; ++i) {
-      const int n = (nb0 + i) * 16 + lrow;
-      if (nb0 + i >= NB) continue;
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = m0 + mb * 16 + (lane >> 4) * 4 + e;
-          if (r >= rows) continue;
-          float v;
-          if (GATED)
-            v = silu_f32(acc[i][0][mb][e]) * acc[i][NH - 1][mb][e];
-          else
-            v = acc[i][0][mb][e];
-          out[(size_t)(row_base + r) * p.n_out + n] = (uint16_t)f32_to_bf16(v);
-        }
-    }
+      for (int e = 0; e < 4; ++e) {
+        const int r = m0 + mb * 16 + (lane >> 4) * 4 + e;
+        if (r >= rows) continue;
+        float v;
+        if (GATED)
+          v = silu_f32(acc[0][mb][e]) * acc[NH - 1][mb][e];
+        else
+          v = acc[0][mb][e];
+        out[(size_t)(row_base + r) * p.n_out + n] = (uint16_t)f32_to_bf16(v);
+      }
   }
 }
 
-template <int P, int MB, bool FP8, bool GATED>
-hipError_t launch_stream(const StreamParams& sp, int groups, hipStream_t st) {
+template <int MB, int D, bool FP8, bool GATED>
+hipError_t launch_stream_d(const StreamParams& sp, int groups, hipStream_t st) {
   const int NB = sp.n_out / 16;
-  dim3 grid(ceil_div(NB, SW_WAVES * P), groups);
-  ffn_stream_kernel<P, MB, FP8, GATED><<<grid, SW_WAVES * 64, 0, st>>>(sp);
+  dim3 grid(ceil_div(NB, SW_WAVES), groups);
+  ffn_stream_kernel<MB, D, FP8, GATED><<<grid, SW_WAVES * 64, 0, st>>>(sp);
   return hipGetLastError();
+}
+
+// The ring depth must divide the number of K steps.
+template <int MB, int DMAX, bool FP8, bool GATED>
+hipError_t launch_stream(const StreamParams& sp, int groups, hipStream_t st) {
+  const int KS = FP8 ? sp.K / 64 : sp.K / 32;
+  if (DMAX >= 8 && KS % 8 == 0) return launch_stream_d<MB, (DMAX >= 8 ? 8 : DMAX), FP8, GATED>(sp, groups, st);
+  if (DMAX >= 4 && KS % 4 == 0) return launch_stream_d<MB, (DMAX >= 4 ? 4 : DMAX), FP8, GATED>(sp, groups, st);
+  if (KS % 2 == 0) return launch_stream_d<MB, 2, FP8, GATED>(sp, groups, st);
+  // FP8 K is a multiple of 128, so KS is even there
+  return launch_stream_d<MB, (FP8 ? 2 : 1), FP8, GATED>(sp, groups, st);
 }
 
 }  // namespace
 
-hipError_t launch_ffn_lowp(const FfnArgs& a, int pass, hipStream_t st) {
-  const int groups = a.N + a.n_shared;
+template <int MB>
+static hipError_t stream_pass(bool fp8, bool gated, const StreamParams& sp, int groups,
+                              hipStream_t st) {
+  if (fp8)
+    return gated ? launch_stream<MB, 4, true, true>(sp, groups, st)
+                 : launch_stream<MB, 4, true, false>(sp, groups, st);
+  return gated ? launch_stream<MB, 8, false, true>(sp, groups, st)
+               : launch_stream<MB, 8, false, false>(sp, groups, st);
+}
+
+hipError_t launch_ffn_stream(const FfnArgs& a, int pass, int g0, int g1, int rows_hint,
+                             hipStream_t st) {
+  if (g1 <= g0) return hipSuccess;
   StreamParams up{};
   up.a = a.x_rows;
   up.perm = a.perm_token;
@@ -245,6 +244,7 @@ hipError_t launch_ffn_lowp(const FfnArgs& a, int pass, hipStream_t st) {
   up.offsets = a.offsets;
   up.T = a.T;
   up.N = a.N;
+  up.g0 = g0;
   up.K = a.d;
   up.n_out = a.d_ff;
   up.w = static_cast<const uint8_t*>(a.w13);
@@ -267,14 +267,50 @@ hipError_t launch_ffn_lowp(const FfnArgs& a, int pass, hipStream_t st) {
   dn.out = a.Y;
   dn.out_sh = a.Y_sh;
 
+  const int groups = g1 - g0;
+  // rows held per pass: 16 * MB (a group with more rows takes more passes)
   hipError_t e = hipSuccess;
-  if (pass & 1) {
-    e = a.fp8 ? launch_stream<2, 2, true, true>(up, groups, st)
-              : launch_stream<2, 2, false, true>(up, groups, st);
-    if (e != hipSuccess) return e;
+  for (int ps = 1; ps <= 2 && e == hipSuccess; ++ps) {
+    if (!(pass & ps)) continue;
+    const StreamParams& sp = ps == 1 ? up : dn;
+    if (rows_hint <= 16)
+      e = stream_pass<1>(a.fp8, ps == 1, sp, groups, st);
+    else if (rows_hint <= 32)
+      e = stream_pass<2>(a.fp8, ps == 1, sp, groups, st);
+    else
+      e = stream_pass<4>(a.fp8, ps == 1, sp, groups, st);
   }
-  if (pass & 2)
-    e = a.fp8 ? launch_stream<2, 2, true, false>(dn, groups, st)
-              : launch_stream<2, 2, false, false>(dn, groups, st);
+  return e;
+}
+
+hipError_t launch_ffn_lowp(const FfnArgs& a, int pass, hipStream_t st) {
+  const bool gemm_ok = gemm_shape_ok(a.d, a.d_ff);
+  const int avg = (int)(((long long)a.T * a.k + a.N - 1) / a.N);  // rows per routed expert
+  const bool routed_gemm = gemm_ok && avg >= 64;
+  const bool shared_gemm = gemm_ok && a.n_shared && a.T >= 64;
+  hipError_t e = hipSuccess;
+  // Run pass by pass so the down projection always sees complete H rows.
+  for (int ps = 1; ps <= 2; ++ps) {
+    if (!(pass & ps)) continue;
+    if (routed_gemm && shared_gemm) {
+      // one launch over routed + shared groups: their tiles share the machine
+      e = launch_ffn_gemm(a, ps, 0, a.N + 1, gemm_row_tile(avg, a.fp8),
+                          a.T * a.k + a.T, a.sched, st);
+      if (e != hipSuccess) return e;
+      continue;
+    }
+    if (routed_gemm)
+      e = launch_ffn_gemm(a, ps, 0, a.N, gemm_row_tile(avg, a.fp8), a.T * a.k, a.sched, st);
+    else
+      e = launch_ffn_stream(a, ps, 0, a.N, avg, st);
+    if (e != hipSuccess) return e;
+    if (a.n_shared) {
+      if (shared_gemm)
+        e = launch_ffn_gemm(a, ps, a.N, a.N + 1, gemm_row_tile(a.T, a.fp8), a.T, a.sched, st);
+      else
+        e = launch_ffn_stream(a, ps, a.N, a.N + 1, a.T, st);
+      if (e != hipSuccess) return e;
+    }
+  }
   return e;
 }

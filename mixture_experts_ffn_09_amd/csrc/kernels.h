@@ -5,16 +5,17 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-// Router logits s[T][N] = x[T][d] @ W[d][N] (+ offset[N]) in float32.
-// act_bf16: x is bfloat16 (else float32).
+// Router logits x[T][d] @ W[d][N] in float32 as router_splits() partial
+// sums over K: partial[S][T][N].  act_bf16: x is bfloat16 (else float32).
+int router_splits(int T, int N, int d);
 hipError_t launch_router_logits(const void* x, bool act_bf16, const float* w_router,
-                                const float* offset, float* logits, int T, int d, int N,
-                                hipStream_t st);
+                                float* partial, int T, int d, int N, hipStream_t st);
 
-// Top-k selection and gates from float32 logits (one wave per token).
-hipError_t launch_router_topk(const float* logits, const float* select_bias, int sigmoid,
-                              int T, int N, int k, int32_t* topk_idx, float* topk_w,
-                              hipStream_t st);
+// Sums the S partials (+ offset[N]), selects the top k and writes the gates
+// (one wave per token).
+hipError_t launch_router_topk(const float* partial, int S, const float* offset,
+                              const float* select_bias, int sigmoid, int T, int N, int k,
+                              int32_t* topk_idx, float* topk_w, hipStream_t st);
 
 // Counts, offsets and the stable (expert, token) permutation.
 hipError_t launch_permute(const int32_t* topk_idx, int T, int k, int N, int32_t* counts,
@@ -35,8 +36,9 @@ struct FfnArgs {
   const int32_t* perm_token;
   const uint16_t* x_sh;
   const int32_t* offsets;
-  int T, N, n_shared, d, d_ff;
+  int T, k, N, n_shared, d, d_ff;
   bool fp8;
+  int32_t* sched;             // 2048 int32 of scratch for the GEMM tile schedule
   const void* w13;
   const void* w2;
   const float* s13;
@@ -50,8 +52,20 @@ struct FfnArgs {
   uint16_t* Y;
   uint16_t* Y_sh;
 };
-// pass: 1 = gate/up + SwiGLU only, 2 = down only, 3 = both.
+// pass: 1 = gate/up + SwiGLU only, 2 = down only, 3 = both.  Picks, per group
+// range, the weight-streaming kernel (few rows per expert) or the tiled
+// GEMM (many rows).
 hipError_t launch_ffn_lowp(const FfnArgs& a, int pass, hipStream_t st);
+
+// Streaming kernel over groups [g0, g1).
+hipError_t launch_ffn_stream(const FfnArgs& a, int pass, int g0, int g1, int rows_hint,
+                             hipStream_t st);
+// Tiled GEMM over groups [g0, g1) with row tile bm; max_rows bounds the total
+// rows of those groups.
+bool gemm_shape_ok(int d, int d_ff);
+int gemm_row_tile(int avg_rows, bool fp8);
+hipError_t launch_ffn_gemm(const FfnArgs& a, int pass, int g0, int g1, int bm, int max_rows,
+                           int32_t* sched, hipStream_t st);
 
 // Float32 expert FFN (float32 activations and weights), same row scheme.
 struct FfnF32Args {

@@ -72,8 +72,9 @@ def lib() -> C.CDLL:
         L.moe_router_topk.argtypes = [S, P, C.POINTER(Weights), P, P, P, C.c_size_t, P]
         L.moe_permute.argtypes = [S, P, P, C.POINTER(Routing), P, P]
         L.moe_grouped_ffn.argtypes = [S, P, P, P, P, C.POINTER(Weights), P, P, P, C.c_size_t, P]
-        L.moe_expert_gate_up.argtypes = [S, P, P, P, P, C.POINTER(Weights), P, P, P]
-        L.moe_expert_down.argtypes = [S, P, P, P, C.POINTER(Weights), P, P, P]
+        L.moe_expert_gate_up.argtypes = [S, P, P, P, P, C.POINTER(Weights), P, P, P,
+                                         C.c_size_t, P]
+        L.moe_expert_down.argtypes = [S, P, P, P, C.POINTER(Weights), P, P, P, C.c_size_t, P]
         L.moe_combine.argtypes = [S, P, P, P, P, P, P]
         L.moe_layer_forward.argtypes = [S, C.POINTER(Weights), P, P, C.POINTER(Routing), P,
                                         C.c_size_t, P]
@@ -173,17 +174,19 @@ def moe_grouped_ffn(shape: Shape, x: Optional[torch.Tensor], x_perm: Optional[to
 
 def moe_expert_gate_up(shape: Shape, x: Optional[torch.Tensor], x_perm: Optional[torch.Tensor],
                        perm_token: Optional[torch.Tensor], offsets: torch.Tensor,
-                       weights: Weights, h: torch.Tensor, h_shared: Optional[torch.Tensor]):
+                       weights: Weights, h: torch.Tensor, h_shared: Optional[torch.Tensor],
+                       ws: torch.Tensor):
     _check(lib().moe_expert_gate_up(C.byref(shape), _ptr(x), _ptr(x_perm), _ptr(perm_token),
                                     _ptr(offsets), C.byref(weights), _ptr(h), _ptr(h_shared),
-                                    _stream()))
+                                    _ptr(ws), ws.numel() * ws.element_size(), _stream()))
 
 
 def moe_expert_down(shape: Shape, h: torch.Tensor, h_shared: Optional[torch.Tensor],
                     offsets: torch.Tensor, weights: Weights, y_perm: torch.Tensor,
-                    y_shared: Optional[torch.Tensor]):
+                    y_shared: Optional[torch.Tensor], ws: torch.Tensor):
     _check(lib().moe_expert_down(C.byref(shape), _ptr(h), _ptr(h_shared), _ptr(offsets),
-                                 C.byref(weights), _ptr(y_perm), _ptr(y_shared), _stream()))
+                                 C.byref(weights), _ptr(y_perm), _ptr(y_shared), _ptr(ws),
+                                 ws.numel() * ws.element_size(), _stream()))
 
 
 def moe_combine(shape: Shape, y_perm: torch.Tensor, y_shared: Optional[torch.Tensor],

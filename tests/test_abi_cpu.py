@@ -132,13 +132,33 @@ def test_workspace_too_small():
     assert b"needed" in _lib().moe_last_error()
 
 
-def test_workspace_size_formula():
-    s = shape(T=100, n_experts=256, top_k=8, d_model=7168, d_ff=2048, n_shared=1, route="sigmoid")
+def _router_splits(T, N, d):
+    """Number of K-splits of the router logits (restated from the library's
+    sizing rule: ~1024 workgroups, at least 256 of K per split)."""
+    cdiv = lambda a, b: -(-a // b)
+    tiles = cdiv(T, 256) if N <= 8 else cdiv(T, 32) * cdiv(N, 64)
+    S = max(1, 1024 // tiles)
+    S = min(S, cdiv(d, 256))
+    KC = cdiv(cdiv(d, S), 32) * 32
+    return cdiv(d, KC)
+
+
+@pytest.mark.parametrize("T,N,k,d,f,sh", [(100, 256, 8, 7168, 2048, 1), (16, 8, 2, 4096, 14336, 0),
+                                          (8192, 8, 2, 4096, 14336, 0)])
+def test_workspace_size_formula(T, N, k, d, f, sh):
+    s = shape(T=T, n_experts=N, top_k=k, d_model=d, d_ff=f, n_shared=sh,
+              route="sigmoid" if sh else "softmax")
     a = lambda v: (v + 255) // 256 * 256
-    T, k, N, d, f = 100, 8, 256, 7168, 2048
-    want = (a(T * N * 4) + 2 * a(T * k * 4) + a(N * 4) + a((N + 1) * 4) + 2 * a(T * k * 4)
-            + a(T * k * f * 2) + a(T * f * 2) + a(T * k * d * 2) + a(T * d * 2))
+    S = _router_splits(T, N, d)
+    want = (a(S * T * N * 4) + 2 * a(T * k * 4) + a(N * 4) + a((N + 1) * 4) + 2 * a(T * k * 4)
+            + a(2048 * 4) + a(T * k * f * 2) + a(sh * T * f * 2) + a(T * k * d * 2)
+            + a(sh * T * d * 2))
     assert moe.moe_workspace_bytes(s) == want
+
+
+def test_packed_sizes():
+    s = shape(T=100, n_experts=256, top_k=8, d_model=7168, d_ff=2048, n_shared=1, route="sigmoid")
+    d, f = 7168, 2048
     assert moe.moe_packed_weight_bytes(s, 0, 3) == 3 * 2 * d * f * 2
     assert moe.moe_packed_weight_bytes(s, 1, 1) == d * f * 2
     s8 = shape(w_dtype="fp8")

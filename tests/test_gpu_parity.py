@@ -33,6 +33,13 @@ SMALL = {
                                       zipf_c=6.0),
     "fp8_rows_over_64": H.small_config(C[4], 107, T=200, d_model=256, d_ff=256, n_experts=8,
                                        top_k=2),
+    # tiled-GEMM path: 256-row tiles with a ragged last tile
+    "gemm_bm256_ragged": H.small_config(C[2], 108, T=600, d_model=256, d_ff=256, n_experts=4),
+    # routed and shared experts in one GEMM launch (128-row tiles)
+    "gemm_routed_plus_shared": H.small_config(C[3], 109, T=160, d_model=256, d_ff=128,
+                                              n_experts=16),
+    # FP8 weights through the GEMM path (routed + shared)
+    "gemm_fp8": H.small_config(C[4], 110, T=256, d_model=256, d_ff=256, n_experts=8, top_k=4),
 }
 
 
@@ -131,7 +138,16 @@ def test_stages_through_abi_match_layer_forward():
     y3 = torch.empty_like(y)
     ys3 = torch.empty_like(ys)
     moe.moe_grouped_ffn(s, xd, None, rb["perm_token"], rb["offsets"], L.weights, y3, ys3, ws)
+    # and the two per-row entry points
+    h4 = torch.empty(cfg.T * cfg.top_k, cfg.d_ff, dtype=xd.dtype, device="cuda")
+    hs4 = torch.empty(cfg.T, cfg.d_ff, dtype=xd.dtype, device="cuda")
+    y4 = torch.empty_like(y)
+    ys4 = torch.empty_like(ys)
+    moe.moe_expert_gate_up(s, xd, None, rb["perm_token"], rb["offsets"], L.weights, h4, hs4, ws)
+    moe.moe_expert_down(s, h4, hs4, rb["offsets"], L.weights, y4, ys4, ws)
     torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), y4.view(torch.int16))
+    assert torch.equal(ys.view(torch.int16), ys4.view(torch.int16))
     assert torch.equal(x_perm, xd[rb["perm_token"].long()])
     assert torch.equal(out2.view(torch.int16), out.view(torch.int16))
     assert torch.equal(y.view(torch.int16), y3.view(torch.int16))

@@ -8,16 +8,17 @@
 // local": each expert is a full FFN; "Mixture of Experts Explained", "The
 // slot it replaces": three matrices.)
 //
-// Tiling for gfx950: a 256-thread workgroup computes BM rows x 128 weight
-// rows (pass 1: 64 gate/up pairs) with 2 x 2 waves, each wave (BM/2) x 64
-// with v_mfma_f32_16x16x32_bf16.  Activation tiles go through LDS, written in
-// MFMA-fragment order (every 1 KB is one A operand: lane l holds row l % 16,
-// k = 8 * (l / 16) + j), so both the LDS writes and the operand reads are
-// contiguous 16-byte accesses.  Weights are pre-packed in the same fragment
-// order, so each wave loads its B operands straight from global memory into
-// registers, one fully coalesced 1 KB per fragment.  Two LDS stages of 64 K
-// each; the next stage's activations and weights are loaded while the
-// current one is multiplied.
+// Tiling for gfx950: a 512-thread workgroup (8 waves, two per SIMD, so one
+// wave's LDS or barrier wait is covered by the other's MFMAs) computes BM
+// rows x 256 weight rows (pass 1: 128 gate/up pairs) with 2 x 4 waves, each
+// wave (BM/2) x 64 with v_mfma_f32_16x16x32_bf16.  Both operands reach LDS through direct
+// global-to-LDS loads (global_load_lds_dwordx4: each lane's 16 bytes land at
+// lane * 16 of a 1 KB block), so no registers are spent on staging.  Every
+// 1 KB in LDS is one MFMA operand (lane l holds row l % 16, k = 8 * (l / 16)
+// + j): the activation copy picks its global addresses to produce that order
+// and the weights are pre-packed in it, so operand reads are contiguous
+// ds_read_b128.  Two 64-K stages: the copy of stage kt+1 is in flight while
+// stage kt is multiplied.
 //
 // Tile order: workgroup ids are spread over the 8 XCDs round-robin, so the
 // linear tile index is remapped to give each XCD a contiguous range, and the
@@ -31,7 +32,7 @@
 
 namespace {
 
-constexpr int GM_BN = 128;    // weight rows per workgroup tile
+constexpr int GM_BN = 256;    // weight rows per workgroup tile
 constexpr int GM_BK = 64;     // K per LDS stage
 constexpr int GM_GN = 8;      // weight tiles per tile-order group
 constexpr int NXCD = 8;
@@ -97,19 +98,48 @@ __global__ __launch_bounds__(1024) void tile_schedule_kernel(GemmParams p, int b
   if (i == 0) tiles[0] = 0;
 }
 
+// s_waitcnt vmcnt(N) leaving the other counters untouched (gfx9 encoding:
+// vmcnt low bits 3:0 and high bits 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier without the release/acquire fences of __syncthreads():
+// those would wait for every outstanding global-to-LDS copy (vmcnt(0)) and
+// drain the ring.  The copies are ordered by explicit wait_vmcnt() instead;
+// the empty asm statements keep the compiler from moving memory accesses
+// across the barrier.
+__device__ __forceinline__ void barrier_no_fence() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 template <int BM, bool GATED, bool FP8>
-__global__ __launch_bounds__(256, 1) void ffn_gemm_kernel(GemmParams p) {
+__global__ __launch_bounds__(512, 1) void ffn_gemm_kernel(GemmParams p) {
+  constexpr int NS = 2;               // LDS stages in the ring
+  constexpr int NWN = 4;              // wave grid 2 x 4 (8 waves, two per SIMD)
   constexpr int MBW = BM / 32;        // 16-row blocks per wave (wave tile BM/2 rows)
-  constexpr int NBW = 4;              // 16-row weight blocks per wave
-  constexpr int AFR = BM / 16;        // A fragments per 32-K step
-  constexpr int ACH = AFR * 64 / 256; // 16-byte A chunks per thread per 32-K step
+  constexpr int NBW = 4;              // 16-row weight blocks per wave (wave tile 64 wide)
+  constexpr int AFR = BM / 16;        // activation fragments per 32-K step
+  constexpr int WBL = NWN * NBW;      // weight blocks per tile (GM_BN / 16)
   constexpr int NH = GATED ? 2 : 1;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2][2][AFR * 1024];  // [buf][kstep]
+  // per stage: activations [2 K steps][AFR] KB, weights [2][WBL] KB (FP8:
+  // [WBL] KB, one 16-byte lane chunk holds both K steps)
+  constexpr int A_BYTES = 2 * AFR * 1024;
+  constexpr int B_FRAGS = FP8 ? WBL : 2 * WBL;
+  constexpr int STAGE = A_BYTES + B_FRAGS * 1024;
+  constexpr int A_PER_WAVE = 2 * AFR / 8;
+  constexpr int B_PER_WAVE = B_FRAGS / 8;
+  static_assert(GM_BN == WBL * 16, "tile width");
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[NS * STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / NWN, wn = wave % NWN;
 
   // ---- tile index: XCD remap, then groups of GM_GN weight tiles
   const int ngroups = p.g1 - p.g0;
@@ -122,8 +152,7 @@ __global__ __launch_bounds__(256, 1) void ffn_gemm_kernel(GemmParams p) {
   const int rr = L - blk * MT * GM_GN;
   const int mt = rr / gw;
   const int nt = blk * GM_GN + rr % gw;
-  // group of row tile mt (binary search over the tile starts)
-  int lo = 0, hi = ngroups - 1;
+  int lo = 0, hi = ngroups - 1;  // group of row tile mt
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
     if (p.tiles[mid] <= mt) lo = mid; else hi = mid - 1;
@@ -135,39 +164,39 @@ __global__ __launch_bounds__(256, 1) void ffn_gemm_kernel(GemmParams p) {
   const bool shared = g >= p.N;
   uint16_t* out = shared ? p.out_sh : p.out;
 
-  const int KT = p.K / GM_BK;    // LDS stages
-  // packed weight K steps: 32 wide (bf16) or 64 wide (FP8, two MFMA steps)
-  const int KS = FP8 ? p.K / 64 : p.K / 32;
-  // weights: this wave's 4 blocks per K step
+  const int KT = p.K / GM_BK;                 // LDS stages over K
+  const int KS = FP8 ? p.K / 64 : p.K / 32;   // packed weight K steps
   const size_t wbytes = (size_t)NH * p.n_out * p.K * (FP8 ? 1 : 2);
   const uint8_t* W = shared ? p.w_sh : p.w + (size_t)g * wbytes;
-  const uint8_t* wptr[NBW];
-  int srow[NBW];
-#pragma unroll
-  for (int j = 0; j < NBW; ++j) {
-    if (GATED) {
-      const int pb = nt * 4 + wn * 2 + (j >> 1);   // gate/up pair block
-      wptr[j] = W + (((size_t)pb * KS) * 2 + (j & 1)) * 1024 + lane * 16;
-      srow[j] = (j & 1) * (p.n_out / MOE_FP8_BLOCK) + (pb * 16) / MOE_FP8_BLOCK;
-    } else {
-      const int nb = nt * 8 + wn * 4 + j;
-      wptr[j] = W + ((size_t)nb * KS) * 1024 + lane * 16;
-      srow[j] = (nb * 16) / MOE_FP8_BLOCK;
-    }
-  }
-  const size_t wstep = (size_t)NH * 1024;  // bytes between K steps of one block
-  const int SK = p.K / MOE_FP8_BLOCK;
-  const float* S = nullptr;
-  if (FP8) S = shared ? p.s_sh : p.s + (size_t)g * NH * (p.n_out / MOE_FP8_BLOCK) * SK;
+  const size_t wstep = (size_t)NH * 1024;     // bytes between K steps of one block
 
-  // activations: this thread's ACH 16-byte chunks per 32-K step
-  const uint16_t* arow[ACH];
+  // Weight block jb of the tile: gated -> pair nt*8 + jb/2, gate (even) or
+  // up (odd); down -> row block nt*16 + jb.
+  auto block_offset = [&](int jb) -> size_t {
+    if (GATED) {
+      const int pb = nt * (WBL / 2) + (jb >> 1);
+      return (((size_t)pb * KS) * 2 + (jb & 1)) * 1024;
+    }
+    return ((size_t)(nt * WBL + jb) * KS) * 1024;
+  };
+  const uint8_t* bsrc[B_PER_WAVE];
+  int bdst[B_PER_WAVE], bks[B_PER_WAVE];
 #pragma unroll
-  for (int c = 0; c < ACH; ++c) {
-    const int chunk = tid + 256 * c;
-    const int fr = chunk >> 6, l = chunk & 63;
-    int r = m0 + fr * 16 + (l & 15);
-    r = min(r, rows - 1);  // rows past the end only feed rows that are not stored
+  for (int i = 0; i < B_PER_WAVE; ++i) {
+    const int q = wave * B_PER_WAVE + i;
+    const int jb = FP8 ? q : (q >> 1);
+    const int sb = FP8 ? 0 : (q & 1);
+    bsrc[i] = W + block_offset(jb) + lane * 16;
+    bks[i] = sb;
+    bdst[i] = A_BYTES + (FP8 ? jb : (sb * WBL + jb)) * 1024;
+  }
+  const uint16_t* asrc[A_PER_WAVE];
+  int adst[A_PER_WAVE];
+#pragma unroll
+  for (int i = 0; i < A_PER_WAVE; ++i) {
+    const int q = wave * A_PER_WAVE + i;
+    const int mb = q >> 1, sa = q & 1;
+    const int r = min(m0 + mb * 16 + (lane & 15), rows - 1);  // rows past the end are not stored
     const uint16_t* ptr;
     if (shared)
       ptr = p.a_sh + (size_t)r * p.K;
@@ -175,11 +204,38 @@ __global__ __launch_bounds__(256, 1) void ffn_gemm_kernel(GemmParams p) {
       ptr = p.a + (size_t)p.perm[row_base + r] * p.K;
     else
       ptr = p.a + (size_t)(row_base + r) * p.K;
-    arow[c] = ptr + (l >> 4) * 8;
+    asrc[i] = ptr + (lane >> 4) * 8 + sa * 32;
+    adst[i] = (sa * AFR + mb) * 1024;
   }
+  auto issue_stage = [&](int kt) {
+    uint8_t* base = lds + (kt % NS) * STAGE;
+#pragma unroll
+    for (int i = 0; i < A_PER_WAVE; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(asrc[i] + kt * GM_BK),
+                                       (void*)(base + adst[i]), 16, 0, 0);
+#pragma unroll
+    for (int i = 0; i < B_PER_WAVE; ++i)
+      __builtin_amdgcn_global_load_lds(
+          (const void*)(bsrc[i] + (size_t)(FP8 ? kt : kt * 2 + bks[i]) * wstep),
+          (void*)(base + bdst[i]), 16, 0, 0);
+  };
+
+  // FP8 scales of this wave's blocks
+  int srow[NBW];
+#pragma unroll
+  for (int j = 0; j < NBW; ++j) {
+    const int jb = wn * NBW + j;
+    if (GATED)
+      srow[j] = (jb & 1) * (p.n_out / MOE_FP8_BLOCK) + ((nt * (WBL / 2) + (jb >> 1)) * 16) / MOE_FP8_BLOCK;
+    else
+      srow[j] = ((nt * WBL + jb) * 16) / MOE_FP8_BLOCK;
+  }
+  const int SK = p.K / MOE_FP8_BLOCK;
+  const float* S = nullptr;
+  if (FP8) S = shared ? p.s_sh : p.s + (size_t)g * NH * (p.n_out / MOE_FP8_BLOCK) * SK;
 
   floatx4_t acc[MBW][NBW];
-  floatx4_t part[FP8 ? MBW : 1][NBW];  // FP8: sum over the current 128-K scale block
+  floatx4_t part[FP8 ? MBW : 1][NBW];
 #pragma unroll
   for (int i = 0; i < MBW; ++i)
 #pragma unroll
@@ -189,96 +245,62 @@ __global__ __launch_bounds__(256, 1) void ffn_gemm_kernel(GemmParams p) {
 #pragma unroll
     for (int j = 0; j < NBW; ++j) part[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
-  u32x4_t ga[2][ACH];      // staged activations of the next stage (2 K steps)
-  u32x4_t gb[2][2][NBW];   // weights: [stage parity][K step][block]
-
-  auto load_a = [&](int kt) {
-#pragma unroll
-    for (int s = 0; s < 2; ++s)
-#pragma unroll
-      for (int c = 0; c < ACH; ++c)
-        ga[s][c] = *reinterpret_cast<const u32x4_t*>(arow[c] + kt * GM_BK + s * 32);
-  };
-  auto store_a = [&](int buf) {
-#pragma unroll
-    for (int s = 0; s < 2; ++s)
-#pragma unroll
-      for (int c = 0; c < ACH; ++c)
-        *reinterpret_cast<u32x4_t*>(&lds[buf][s][(tid + 256 * c) * 16]) = ga[s][c];
-  };
-  auto load_b = [&](int par, int kt) {
-#pragma unroll
-    for (int s = 0; s < (FP8 ? 1 : 2); ++s)
+  issue_stage(0);
+  wait_vmcnt<0>();
+  barrier_no_fence();
+  for (int kt = 0; kt < KT; ++kt) {
+    // the other buffer was last read in stage kt-1, before the barrier below
+    if (kt + 1 < KT) issue_stage(kt + 1);
+    const uint8_t* base = lds + (kt % NS) * STAGE;
+    u32x4_t bq[NBW];
+    if (FP8) {
 #pragma unroll
       for (int j = 0; j < NBW; ++j)
-        gb[par][s][j] = *reinterpret_cast<const u32x4_t*>(
-            wptr[j] + (size_t)(FP8 ? kt : kt * 2 + s) * wstep);
-  };
-  auto compute = [&](int buf, int par) {
+        bq[j] = *reinterpret_cast<const u32x4_t*>(base + A_BYTES + (wn * NBW + j) * 1024 + lane * 16);
+    }
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      u32x4_t af[MBW];
+    for (int s2 = 0; s2 < 2; ++s2) {
+      u32x4_t af[MBW], bf[NBW];
 #pragma unroll
       for (int i = 0; i < MBW; ++i)
-        af[i] = *reinterpret_cast<const u32x4_t*>(&lds[buf][s][((wm * MBW + i) * 64 + lane) * 16]);
-      if (!FP8) {
+        af[i] = *reinterpret_cast<const u32x4_t*>(base + (s2 * AFR + wm * MBW + i) * 1024 + lane * 16);
 #pragma unroll
-        for (int i = 0; i < MBW; ++i)
+      for (int j = 0; j < NBW; ++j) {
+        if (!FP8)
+          bf[j] = *reinterpret_cast<const u32x4_t*>(base + A_BYTES + (s2 * WBL + wn * NBW + j) * 1024 +
+                                                    lane * 16);
+        else
+          fp8_half_to_bf16(bq[j], s2, bf[j]);
+      }
 #pragma unroll
-          for (int j = 0; j < NBW; ++j) acc[i][j] = mfma16x16x32(af[i], gb[par][s][j], acc[i][j]);
-      } else {
+      for (int i = 0; i < MBW; ++i)
 #pragma unroll
         for (int j = 0; j < NBW; ++j) {
-          u32x4_t bf;
-          fp8_half_to_bf16(gb[par][0][j], s, bf);
+          if (!FP8)
+            acc[i][j] = mfma16x16x32(af[i], bf[j], acc[i][j]);
+          else
+            part[i < (FP8 ? MBW : 1) ? i : 0][j] =
+                mfma16x16x32(af[i], bf[j], part[i < (FP8 ? MBW : 1) ? i : 0][j]);
+        }
+    }
+    if (FP8 && (kt & 1)) {  // a 128-K scale block is complete
+      const int kc = kt >> 1;
 #pragma unroll
-          for (int i = 0; i < (FP8 ? MBW : 1); ++i) part[i][j] = mfma16x16x32(af[i], bf, part[i][j]);
+      for (int j = 0; j < NBW; ++j) {
+        const float sc = S[(size_t)srow[j] * SK + kc];
+#pragma unroll
+        for (int i = 0; i < (FP8 ? MBW : 1); ++i) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[i][j][e] += sc * part[i][j][e];
+          part[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
         }
       }
     }
-  };
-  // FP8: after every second stage a 128-K scale block is complete
-  auto close_scale_block = [&](int kt) {
-    if (!FP8) return;
-    const int kc = kt >> 1;
-#pragma unroll
-    for (int j = 0; j < NBW; ++j) {
-      const float sc = S[(size_t)srow[j] * SK + kc];
-#pragma unroll
-      for (int i = 0; i < (FP8 ? MBW : 1); ++i) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[i][j][e] += sc * part[i][j][e];
-        part[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-      }
-    }
-  };
-
-  // prologue
-  load_a(0);
-  load_b(0, 0);
-  store_a(0);
-  if (KT > 1) load_a(1);
-  __syncthreads();
-
-  for (int kt = 0; kt < KT; kt += 2) {
-    // even stage: data in lds[0], weights in gb[0]
-    if (kt + 1 < KT) load_b(1, kt + 1);
-    compute(0, 0);
-    if (kt + 1 < KT) {
-      store_a(1);
-      if (kt + 2 < KT) load_a(kt + 2);
-    }
-    __syncthreads();
-    if (kt + 1 >= KT) break;
-    // odd stage: lds[1], gb[1]
-    if (kt + 2 < KT) load_b(0, kt + 2);
-    compute(1, 1);
-    close_scale_block(kt + 1);
-    if (kt + 2 < KT) {
-      store_a(0);
-      if (kt + 3 < KT) load_a(kt + 3);
-    }
-    __syncthreads();
+    // stage kt+1 landed (this wave's copies), then everyone's; stage kt is
+    // no longer read after this barrier
+    wait_vmcnt<0>();
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+    barrier_no_fence();
   }
 
   // epilogue: acc[i][j] lane holds rows 4*(lane/16)+e of column lane%16
@@ -291,15 +313,15 @@ __global__ __launch_bounds__(256, 1) void ffn_gemm_kernel(GemmParams p) {
       uint16_t* orow = out + (size_t)(row_base + r) * p.n_out;
       if (GATED) {
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          const int col = (nt * 4 + wn * 2 + q) * 16 + (lane & 15);
+        for (int q = 0; q < NBW / 2; ++q) {
+          const int col = (nt * (WBL / 2) + wn * (NBW / 2) + q) * 16 + (lane & 15);
           const float v = silu_f32(acc[i][2 * q][e]) * acc[i][2 * q + 1][e];
           orow[col] = (uint16_t)f32_to_bf16(v);
         }
       } else {
 #pragma unroll
         for (int j = 0; j < NBW; ++j) {
-          const int col = (nt * 8 + wn * 4 + j) * 16 + (lane & 15);
+          const int col = (nt * WBL + wn * NBW + j) * 16 + (lane & 15);
           orow[col] = (uint16_t)f32_to_bf16(acc[i][j][e]);
         }
       }
@@ -307,19 +329,19 @@ __global__ __launch_bounds__(256, 1) void ffn_gemm_kernel(GemmParams p) {
   }
 }
 
+template <int BM, bool FP8>
+void launch_gemm_kernel(bool gated, long long nwg, const GemmParams& p, hipStream_t st) {
+  if (gated)
+    ffn_gemm_kernel<BM, true, FP8><<<dim3((unsigned)nwg), 512, 0, st>>>(p);
+  else
+    ffn_gemm_kernel<BM, false, FP8><<<dim3((unsigned)nwg), 512, 0, st>>>(p);
+}
+
 }  // namespace
 
 int gemm_row_tile(int avg_rows, bool fp8) { return (!fp8 && avg_rows >= 192) ? 256 : 128; }
 
-bool gemm_shape_ok(int d, int d_ff) { return d % 128 == 0 && d_ff % 64 == 0; }
-
-template <int BM, bool FP8>
-static void launch_gemm_kernel(bool gated, long long nwg, const GemmParams& p, hipStream_t st) {
-  if (gated)
-    ffn_gemm_kernel<BM, true, FP8><<<dim3((unsigned)nwg), 256, 0, st>>>(p);
-  else
-    ffn_gemm_kernel<BM, false, FP8><<<dim3((unsigned)nwg), 256, 0, st>>>(p);
-}
+bool gemm_shape_ok(int d, int d_ff) { return d % 256 == 0 && d_ff % 128 == 0; }
 
 hipError_t launch_ffn_gemm(const FfnArgs& a, int pass, int g0, int g1, int bm, int max_rows,
                            int32_t* sched, hipStream_t st) {

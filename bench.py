@@ -71,6 +71,21 @@ def roofline_for(cfg, stage: dict, ms: float):
             "frac": round(ach / peak_f, 4)}
 
 
+def measured_traffic(workload: str):
+    """HBM bytes per launch of the gate/up kernel from the committed rocprofv3
+    counter summary, or None when there is none for this workload or the
+    kernel source has changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload.replace('-', '_')}_T16.json")
+    if workload != "mixtral-decode" or not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    src = open(os.path.join(ROOT, rec["source"]), "rb").read()
+    if hashlib.sha256(src).hexdigest() != rec["source_sha256"]:
+        return None
+    return rec["traffic_bytes_per_launch"]
+
+
 def cpu_baseline(cfg, x_cpu, n_tokens: int):
     """Time the CPU oracle (as it stands) on a bounded sample of the same
     workload: the first n_tokens tokens, weights decoded from their stored
@@ -114,6 +129,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=1, help="workload index (1 = Mixtral decode)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB, --steps times (calibrates "
+                         "the HBM byte counters)")
     a = ap.parse_args()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
@@ -121,6 +139,16 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if a.copy_probe:
+        n = a.copy_probe << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(a.steps):
+            torch.mul(src, 1.0, out=dst)   # reads n bytes, writes n bytes
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n, "launches": a.steps}))
+        return
 
     from mixture_experts_ffn_09_amd import moe, workloads as W
     from mixture_experts_ffn_09_amd.layer import build_device_layer
@@ -195,8 +223,8 @@ def main():
                         "achieved": r["achieved"], "unit": r["unit"]}
     dom = "gate_up"
     roof = roofline_for(cfg, st[dom], stage_ms[dom])
-    roof["traffic"] = None
-    roof["kernel"] = "ffn_stream_kernel (gate/up + SwiGLU)"
+    roof["traffic"] = measured_traffic(cfg.name)
+    roof["kernel"] = "expert gate/up + SwiGLU (moe_expert_gate_up)"
     layer_gbs = layer["bytes"] / (ms_step * 1e-3) / 1e9
     layer_tflops = layer["flops"] / (ms_step * 1e-3) / 1e12
 

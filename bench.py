@@ -176,7 +176,7 @@ def main():
         moe.moe_router_topk(s, x, L.weights, rb["topk_idx"], rb["topk_w"], ws)
         if ev is not None:
             ev[1].record()
-        moe.moe_permute(s, rb["topk_idx"], None, routing)
+        moe.moe_permute(s, rb["topk_idx"], None, routing, ws)
         if ev is not None:
             ev[2].record()
         moe.moe_expert_gate_up(s, x, None, rb["perm_token"], rb["offsets"], L.weights, h, h_sh, ws)

@@ -129,7 +129,8 @@ moe_status_t moe_pack_weights(const moe_shape_t* s, int which, int n_mats,
  * for this shape (0 when n_tokens == 0); each of them checks ws_bytes against
  * it.  Returns (size_t)-1 on a bad shape.  Layout (256-byte aligned pieces):
  * router partial logits [S][T][N] f32 (S >= 1 K-splits), topk idx/w,
- * counts, offsets, perm_token, inv_perm, an 8 KB tile schedule, H [T*k][d_ff]
+ * counts, offsets, perm_token, inv_perm, per-256-token-block expert counts
+ * [ceil(T/256)][N] int32, an 8 KB tile schedule, H [T*k][d_ff]
  * and H_shared [T][d_ff], Y [T*k][d] and Y_shared [T][d] (H, Y in the
  * activation type).  moe_expert_gate_up / moe_expert_down use only the
  * schedule piece but check ws_bytes against the full size. */
@@ -146,13 +147,14 @@ moe_status_t moe_router_topk(const moe_shape_t* s, const void* x,
                              hipStream_t stream);
 
 /* a3+a4: per-expert counts, offsets, and the stable expert-contiguous
- * permutation of (token, slot) assignments, ordered by (expert, token)
+ * permutation of (token, slot) assignments, ordered by (expert, token, slot)
  * ([CH19] 19.6.3 "Route and pack").  Ids outside [0, N) are not counted and
  * get inv_perm = -1.  If x_perm is not NULL, also gathers x_perm[r] =
- * x[perm_token[r]] ([T*k][d] act_dtype; x is then required). */
+ * x[perm_token[r]] ([T*k][d] act_dtype; x is then required).  ws holds
+ * per-block counts (moe_workspace_bytes(s) always suffices). */
 moe_status_t moe_permute(const moe_shape_t* s, const int32_t* topk_idx,
                          const void* x, moe_routing_t* out, void* x_perm,
-                         hipStream_t stream);
+                         void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* a5+a6: every routed expert's SwiGLU FFN on its rows, and the shared
  * expert on all T tokens.  Rows of expert e are r in

@@ -75,7 +75,7 @@ moe_status_t check_shape(const moe_shape_t* s) {
 }
 
 struct WsLayout {
-  size_t logits, idx, w, counts, offsets, perm, inv, sched, H, H_sh, Y, Y_sh, total;
+  size_t logits, idx, w, counts, offsets, perm, inv, hist, sched, H, H_sh, Y, Y_sh, total;
 };
 
 WsLayout ws_layout(const moe_shape_t* s) {
@@ -88,13 +88,15 @@ WsLayout ws_layout(const moe_shape_t* s) {
   };
   const size_t T = s->n_tokens, k = s->top_k, N = s->n_experts, d = s->d_model, f = s->d_ff;
   const size_t es = act_size(s), sh = s->n_shared;
-  L.logits = take((size_t)router_splits(s->n_tokens, s->n_experts, s->d_model) * T * N * 4);
+  L.logits = take((size_t)router_splits(s->n_tokens, s->n_experts, s->d_model,
+                                        s->act_dtype == MOE_BF16) * T * N * 4);
   L.idx = take(T * k * 4);
   L.w = take(T * k * 4);
   L.counts = take(N * 4);
   L.offsets = take((N + 1) * 4);
   L.perm = take(T * k * 4);
   L.inv = take(T * k * 4);
+  L.hist = take((size_t)permute_blocks(s->n_tokens) * N * 4);
   L.sched = take(2048 * 4);
   L.H = take(T * k * f * es);
   L.H_sh = take(sh * T * f * es);
@@ -138,7 +140,9 @@ moe_status_t run_router(const moe_shape_t* s, const void* x, const moe_weights_t
   HIP_TRY("router_logits", launch_router_logits(x, s->act_dtype == MOE_BF16, w->w_router, logits,
                                                 s->n_tokens, s->d_model, s->n_experts, st));
   HIP_TRY("router_topk",
-          launch_router_topk(logits, router_splits(s->n_tokens, s->n_experts, s->d_model),
+          launch_router_topk(logits,
+                             router_splits(s->n_tokens, s->n_experts, s->d_model,
+                                           s->act_dtype == MOE_BF16),
                              w->logit_offset,
                              s->route == MOE_ROUTE_SIGMOID_BIAS ? w->select_bias : nullptr,
                              s->route == MOE_ROUTE_SIGMOID_BIAS, s->n_tokens, s->n_experts,
@@ -261,16 +265,22 @@ moe_status_t moe_router_topk(const moe_shape_t* s, const void* x, const moe_weig
 }
 
 moe_status_t moe_permute(const moe_shape_t* s, const int32_t* topk_idx, const void* x,
-                         moe_routing_t* out, void* x_perm, hipStream_t stream) {
+                         moe_routing_t* out, void* x_perm, void* ws, size_t ws_bytes,
+                         hipStream_t stream) {
   moe_status_t st = check_shape(s);
   if (st != MOE_OK) return st;
   if (!out || !out->counts || !out->offsets || !out->perm_token || !out->inv_perm)
     return fail(MOE_ERR_INVALID_ARG, "routing counts / offsets / perm_token / inv_perm is NULL");
   if (!topk_idx) return fail(MOE_ERR_INVALID_ARG, "topk_idx is NULL");
   if (x_perm && !x) return fail(MOE_ERR_INVALID_ARG, "x_perm needs x");
+  if (s->n_tokens > 0 && (st = check_ws(s, ws, ws_bytes)) != MOE_OK) return st;
   // T == 0 still yields well-defined (zero) counts and offsets
-  HIP_TRY("permute", launch_permute(topk_idx, s->n_tokens, s->top_k, s->n_experts, out->counts,
-                                    out->offsets, out->perm_token, out->inv_perm, stream));
+  int32_t* hist = s->n_tokens > 0
+                      ? reinterpret_cast<int32_t*>(static_cast<char*>(ws) + ws_layout(s).hist)
+                      : nullptr;
+  HIP_TRY("permute", launch_permute(topk_idx, s->n_tokens, s->top_k, s->n_experts, hist,
+                                    out->counts, out->offsets, out->perm_token, out->inv_perm,
+                                    stream));
   if (x_perm && s->n_tokens > 0)
     HIP_TRY("gather", launch_gather_rows(x, out->perm_token, x_perm, s->n_tokens * s->top_k,
                                          s->d_model * act_size(s), stream));
@@ -368,7 +378,8 @@ moe_status_t moe_layer_forward(const moe_shape_t* s, const moe_weights_t* w, con
 
   if ((st = run_router(s, x, w, idx, gw, reinterpret_cast<float*>(b + L.logits), stream)) != MOE_OK)
     return st;
-  HIP_TRY("permute", launch_permute(idx, s->n_tokens, s->top_k, s->n_experts, counts, offs, perm,
+  HIP_TRY("permute", launch_permute(idx, s->n_tokens, s->top_k, s->n_experts,
+                                    reinterpret_cast<int32_t*>(b + L.hist), counts, offs, perm,
                                     inv, stream));
   if ((st = run_ffn(s, x, x, perm, offs, w, b + L.H, b + L.H_sh, b + L.Y, b + L.Y_sh,
                     b + L.sched, 3, stream)) != MOE_OK)

@@ -36,6 +36,8 @@ struct StreamParams {
   const uint16_t* a_sh;       // shared-expert activations, row t
   const int32_t* offsets;     // [N+1]
   int T, N, g0;
+  int n_routed;  // routed groups in this launch (g0 .. g0+n_routed-1)
+  int sh_rows;   // rows per shared-expert slice (grid rows past the routed ones)
   int K;       // reduction length
   int n_out;   // output width
   const uint8_t* w;           // packed routed weights
@@ -69,21 +71,23 @@ __global__ __launch_bounds__(256) void ffn_stream_kernel(StreamParams p) {
   static_assert(!FP8 || D % 2 == 0, "FP8 needs an even ring depth");
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int g = p.g0 + blockIdx.y;
   const int NB = p.n_out / 16;
   const int nb = blockIdx.x * SW_WAVES + wave;
   if (nb >= NB) return;
 
-  const bool shared = g >= p.N;
-  int row_base, rows;
+  // grid rows: routed groups, then slices of the shared expert's T rows
+  const bool shared = (int)blockIdx.y >= p.n_routed;
+  const int g = shared ? p.N : p.g0 + blockIdx.y;
+  int row_base, rows, m_first = 0;
   if (!shared) {
     row_base = p.offsets[g];
     rows = p.offsets[g + 1] - row_base;
   } else {
     row_base = 0;
-    rows = p.T;
+    m_first = (blockIdx.y - p.n_routed) * p.sh_rows;
+    rows = min(p.T, m_first + p.sh_rows);
   }
-  if (rows <= 0) return;
+  if (rows <= m_first) return;
   uint16_t* out = shared ? p.out_sh : p.out;
 
   const size_t wbytes = (size_t)NH * p.n_out * p.K * (FP8 ? 1 : 2);
@@ -98,7 +102,7 @@ __global__ __launch_bounds__(256) void ffn_stream_kernel(StreamParams p) {
   const int lrow = lane & 15;
   const int lk = (lane >> 4) * 8;
 
-  for (int m0 = 0; m0 < rows; m0 += 16 * MB) {
+  for (int m0 = m_first; m0 < rows; m0 += 16 * MB) {
     const uint16_t* arow[MB];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
@@ -205,6 +209,7 @@ __global__ __launch_bounds__(256) void ffn_stream_kernel(StreamParams p) {
 
 template <int MB, int D, bool FP8, bool GATED>
 hipError_t launch_stream_d(const StreamParams& sp, int groups, hipStream_t st) {
+  // groups = grid rows (routed groups + shared slices)
   const int NB = sp.n_out / 16;
   dim3 grid(ceil_div(NB, SW_WAVES), groups);
   ffn_stream_kernel<MB, D, FP8, GATED><<<grid, SW_WAVES * 64, 0, st>>>(sp);
@@ -228,8 +233,8 @@ template <int MB>
 static hipError_t stream_pass(bool fp8, bool gated, const StreamParams& sp, int groups,
                               hipStream_t st) {
   if (fp8)
-    return gated ? launch_stream<MB, 4, true, true>(sp, groups, st)
-                 : launch_stream<MB, 4, true, false>(sp, groups, st);
+    return gated ? launch_stream<MB, 8, true, true>(sp, groups, st)
+                 : launch_stream<MB, 8, true, false>(sp, groups, st);
   return gated ? launch_stream<MB, 8, false, true>(sp, groups, st)
                : launch_stream<MB, 8, false, false>(sp, groups, st);
 }
@@ -237,6 +242,13 @@ static hipError_t stream_pass(bool fp8, bool gated, const StreamParams& sp, int 
 hipError_t launch_ffn_stream(const FfnArgs& a, int pass, int g0, int g1, int rows_hint,
                              hipStream_t st) {
   if (g1 <= g0) return hipSuccess;
+  const int mb = rows_hint <= 16 ? 1 : (rows_hint <= 32 ? 2 : 4);
+  const bool with_shared = g1 > a.N;
+  const int n_routed = (g1 > a.N ? a.N : g1) - g0;
+  // the shared expert's rows are cut into slices of one pass each, run
+  // side by side (their repeated weight reads meet in L2 / MALL)
+  const int sh_rows = 16 * mb;
+  const int sh_slices = with_shared ? ceil_div(a.T, sh_rows) : 0;
   StreamParams up{};
   up.a = a.x_rows;
   up.perm = a.perm_token;
@@ -245,6 +257,8 @@ hipError_t launch_ffn_stream(const FfnArgs& a, int pass, int g0, int g1, int row
   up.T = a.T;
   up.N = a.N;
   up.g0 = g0;
+  up.n_routed = n_routed;
+  up.sh_rows = sh_rows;
   up.K = a.d;
   up.n_out = a.d_ff;
   up.w = static_cast<const uint8_t*>(a.w13);
@@ -267,15 +281,15 @@ hipError_t launch_ffn_stream(const FfnArgs& a, int pass, int g0, int g1, int row
   dn.out = a.Y;
   dn.out_sh = a.Y_sh;
 
-  const int groups = g1 - g0;
+  const int groups = n_routed + sh_slices;
   // rows held per pass: 16 * MB (a group with more rows takes more passes)
   hipError_t e = hipSuccess;
   for (int ps = 1; ps <= 2 && e == hipSuccess; ++ps) {
     if (!(pass & ps)) continue;
     const StreamParams& sp = ps == 1 ? up : dn;
-    if (rows_hint <= 16)
+    if (mb == 1)
       e = stream_pass<1>(a.fp8, ps == 1, sp, groups, st);
-    else if (rows_hint <= 32)
+    else if (mb == 2)
       e = stream_pass<2>(a.fp8, ps == 1, sp, groups, st);
     else
       e = stream_pass<4>(a.fp8, ps == 1, sp, groups, st);
@@ -287,7 +301,9 @@ hipError_t launch_ffn_lowp(const FfnArgs& a, int pass, hipStream_t st) {
   const bool gemm_ok = gemm_shape_ok(a.d, a.d_ff);
   const int avg = (int)(((long long)a.T * a.k + a.N - 1) / a.N);  // rows per routed expert
   const bool routed_gemm = gemm_ok && avg >= 64;
-  const bool shared_gemm = gemm_ok && a.n_shared && a.T >= 64;
+  // the shared expert joins a routed streaming launch up to a few hundred
+  // tokens; beyond that, or next to a routed GEMM, it is a GEMM too
+  const bool shared_gemm = gemm_ok && a.n_shared && (routed_gemm ? a.T >= 64 : a.T > 512);
   hipError_t e = hipSuccess;
   // Run pass by pass so the down projection always sees complete H rows.
   for (int ps = 1; ps <= 2; ++ps) {
@@ -299,18 +315,19 @@ hipError_t launch_ffn_lowp(const FfnArgs& a, int pass, hipStream_t st) {
       if (e != hipSuccess) return e;
       continue;
     }
-    if (routed_gemm)
+    if (routed_gemm) {
       e = launch_ffn_gemm(a, ps, 0, a.N, gemm_row_tile(avg, a.fp8), a.T * a.k, a.sched, st);
-    else
-      e = launch_ffn_stream(a, ps, 0, a.N, avg, st);
-    if (e != hipSuccess) return e;
-    if (a.n_shared) {
-      if (shared_gemm)
-        e = launch_ffn_gemm(a, ps, a.N, a.N + 1, gemm_row_tile(a.T, a.fp8), a.T, a.sched, st);
-      else
-        e = launch_ffn_stream(a, ps, a.N, a.N + 1, a.T, st);
       if (e != hipSuccess) return e;
+      if (a.n_shared)  // shared_gemm is false only below 64 tokens
+        e = launch_ffn_stream(a, ps, a.N, a.N + 1, a.T, st);
+    } else if (a.n_shared && !shared_gemm) {
+      e = launch_ffn_stream(a, ps, 0, a.N + 1, avg, st);  // routed + shared slices
+    } else {
+      e = launch_ffn_stream(a, ps, 0, a.N, avg, st);
+      if (e == hipSuccess && a.n_shared)
+        e = launch_ffn_gemm(a, ps, a.N, a.N + 1, gemm_row_tile(a.T, a.fp8), a.T, a.sched, st);
     }
+    if (e != hipSuccess) return e;
   }
   return e;
 }

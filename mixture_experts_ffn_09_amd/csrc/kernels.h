@@ -7,7 +7,7 @@
 
 // Router logits x[T][d] @ W[d][N] in float32 as router_splits() partial
 // sums over K: partial[S][T][N].  act_bf16: x is bfloat16 (else float32).
-int router_splits(int T, int N, int d);
+int router_splits(int T, int N, int d, bool act_bf16);
 hipError_t launch_router_logits(const void* x, bool act_bf16, const float* w_router,
                                 float* partial, int T, int d, int N, hipStream_t st);
 
@@ -17,10 +17,12 @@ hipError_t launch_router_topk(const float* partial, int S, const float* offset,
                               const float* select_bias, int sigmoid, int T, int N, int k,
                               int32_t* topk_idx, float* topk_w, hipStream_t st);
 
-// Counts, offsets and the stable (expert, token) permutation.
-hipError_t launch_permute(const int32_t* topk_idx, int T, int k, int N, int32_t* counts,
-                          int32_t* offsets, int32_t* perm_token, int32_t* inv_perm,
-                          hipStream_t st);
+// Counts, offsets and the stable (expert, token) permutation.  hist is
+// scratch of permute_blocks(T) * N int32 (unused when that is 1).
+int permute_blocks(int T);
+hipError_t launch_permute(const int32_t* topk_idx, int T, int k, int N, int32_t* hist,
+                          int32_t* counts, int32_t* offsets, int32_t* perm_token,
+                          int32_t* inv_perm, hipStream_t st);
 
 // x_perm[r] = x[perm_token[r]] for r < rows (row_bytes per row).
 hipError_t launch_gather_rows(const void* x, const int32_t* perm_token, void* x_perm,

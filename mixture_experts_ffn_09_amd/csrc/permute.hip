@@ -1,118 +1,142 @@
 // Route and pack ("Chapter 19", 19.6.3): per-expert counts, exclusive
 // offsets, and the stable expert-contiguous order of (token, slot)
-// assignments, by (expert ascending, token ascending).
+// assignments, by (expert ascending, token ascending, slot ascending).
 //
-// One 1024-thread workgroup.  Wave w owns a contiguous token range.  Pass 1
-// counts its assignments into a wave-private LDS histogram (order-free
-// adds).  The histograms are scanned over (expert, wave) into global row
-// bases.  Pass 2 revisits the range 64 tokens at a time; the rank of an
-// assignment among earlier same-expert assignments of the 64 is found with
-// ballots over the bits of the expert id, so positions never depend on the
-// order in which atomics land.
+// Tokens are cut into blocks of 256 (one workgroup, 4 waves of 64 tokens).
+// A first kernel writes each block's per-expert counts (order-free LDS adds).
+// The second kernel gives every block its row bases - expert offset plus the
+// counts of earlier blocks plus those of earlier waves in the block - and
+// ranks each assignment among earlier same-expert assignments of its wave
+// with ballots over the bits of the expert id.  Every position follows from
+// counts and ballots alone, never from the order in which atomics land.
+// With a single block the first kernel is skipped.
 
 #include "common.h"
 #include "kernels.h"
 
 namespace {
 
-constexpr int PW = 16;  // waves
+constexpr int PB_WAVES = 4;
+constexpr int PB_TOK = PB_WAVES * 64;  // tokens per block
 
 __device__ __forceinline__ uint64_t lanemask_lt() {
   const int lane = threadIdx.x & 63;
   return lane == 0 ? 0ull : (~0ull >> (64 - lane));
 }
 
-__global__ __launch_bounds__(1024) void permute_kernel(const int32_t* __restrict__ idx, int T,
-                                                       int k, int N, int nbits,
-                                                       int32_t* __restrict__ counts,
-                                                       int32_t* __restrict__ offsets,
-                                                       int32_t* __restrict__ perm_token,
-                                                       int32_t* __restrict__ inv_perm) {
-  extern __shared__ int32_t hist[];  // [PW][N] then scan[N]
-  int32_t* scan = hist + PW * N;
+// hist[b][e]: assignments of block b's tokens to expert e
+__global__ __launch_bounds__(256) void block_hist_kernel(const int32_t* __restrict__ idx, int T,
+                                                         int k, int N,
+                                                         int32_t* __restrict__ hist) {
+  extern __shared__ int32_t h[];
+  for (int e = threadIdx.x; e < N; e += 256) h[e] = 0;
+  __syncthreads();
+  const int t = blockIdx.x * PB_TOK + threadIdx.x;
+  if (t < T)
+    for (int i = 0; i < k; ++i) {
+      const int e = idx[(size_t)t * k + i];
+      if (e >= 0 && e < N) atomicAdd(&h[e], 1);
+    }
+  __syncthreads();
+  for (int e = threadIdx.x; e < N; e += 256) hist[(size_t)blockIdx.x * N + e] = h[e];
+}
+
+// hist == nullptr: a single block (T <= 256) counts for itself.
+__global__ __launch_bounds__(256) void permute_kernel(const int32_t* __restrict__ idx, int T,
+                                                      int k, int N, int nbits,
+                                                      const int32_t* __restrict__ hist, int nblk,
+                                                      int32_t* __restrict__ counts,
+                                                      int32_t* __restrict__ offsets,
+                                                      int32_t* __restrict__ perm_token,
+                                                      int32_t* __restrict__ inv_perm) {
+  extern __shared__ int32_t sm[];
+  int32_t* wh = sm;                       // [PB_WAVES][N] wave counts, then wave bases
+  int32_t* tot = sm + PB_WAVES * N;       // [N] totals, then exclusive offsets
+  int32_t* bef = tot + N;                 // [N] counts of earlier blocks
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63;
-  const int chunk = ceil_div(T, PW);
-  const int t_begin = min(T, w * chunk), t_end = min(T, t_begin + chunk);
+  const int b = blockIdx.x;
+  const int t = b * PB_TOK + w * 64 + lane;
+  const bool tv = t < T;
   const uint32_t sentinel = (1u << nbits) - 1u;  // >= N, never a valid id
 
-  for (int i = tid; i < PW * N; i += 1024) hist[i] = 0;
+  for (int i = tid; i < PB_WAVES * N; i += 256) wh[i] = 0;
   __syncthreads();
-
-  // pass 1: wave-private counts
-  for (int t = t_begin + lane; t < t_end; t += 64)
+  if (tv)
     for (int i = 0; i < k; ++i) {
-      int e = idx[(size_t)t * k + i];
-      if (e >= 0 && e < N) atomicAdd(&hist[w * N + e], 1);
+      const int e = idx[(size_t)t * k + i];
+      if (e >= 0 && e < N) atomicAdd(&wh[w * N + e], 1);
     }
   __syncthreads();
 
-  // per-expert totals (N <= 1024 = one expert per thread); hist becomes the
-  // wave's base within the expert
-  if (tid < N) {
+  // totals and the counts of earlier blocks
+  for (int e = tid; e < N; e += 256) {
+    int before = 0, total = 0;
+    if (hist) {
+      for (int bb = 0; bb < nblk; ++bb) {
+        const int v = hist[(size_t)bb * N + e];
+        total += v;
+        if (bb < b) before += v;
+      }
+    } else {
+      for (int ww = 0; ww < PB_WAVES; ++ww) total += wh[ww * N + e];
+    }
+    tot[e] = total;
+    bef[e] = before;
+  }
+  __syncthreads();
+  // exclusive scan of the totals (thread 0; N <= 512)
+  if (tid == 0) {
     int run = 0;
-    for (int ww = 0; ww < PW; ++ww) {
-      int v = hist[ww * N + tid];
-      hist[ww * N + tid] = run;
+    for (int e = 0; e < N; ++e) {
+      const int v = tot[e];
+      tot[e] = run;
       run += v;
     }
-    scan[tid] = run;
+    if (b == 0) offsets[N] = run;
   }
   __syncthreads();
-  // inclusive scan of the N totals (Hillis-Steele)
-  for (int off = 1; off < N; off <<= 1) {
-    int v = (tid < N && tid >= off) ? scan[tid - off] : 0;
-    __syncthreads();
-    if (tid < N) scan[tid] += v;
-    __syncthreads();
-  }
-  if (tid < N) {
-    const int excl = tid ? scan[tid - 1] : 0;
-    offsets[tid] = excl;
-    counts[tid] = scan[tid] - excl;
-    if (tid == N - 1) offsets[N] = scan[tid];
-    for (int ww = 0; ww < PW; ++ww) hist[ww * N + tid] += excl;
+  for (int e = tid; e < N; e += 256) {
+    if (b == 0) {
+      const int next = (e + 1 < N) ? tot[e + 1] : offsets[N];
+      offsets[e] = tot[e];
+      counts[e] = next - tot[e];
+    }
+    int run = tot[e] + bef[e];
+    for (int ww = 0; ww < PB_WAVES; ++ww) {
+      const int v = wh[ww * N + e];
+      wh[ww * N + e] = run;
+      run += v;
+    }
   }
   __syncthreads();
 
-  // pass 2: stable positions
+  // ranks within the wave's 64 tokens
   const uint64_t lt = lanemask_lt();
-  for (int tb = t_begin; tb < t_end; tb += 64) {
-    const int t = tb + lane;
-    const bool tv = t < t_end;
-    // my k expert ids (sentinel when absent)
-    for (int i = 0; i < k; ++i) {
-      int e = tv ? idx[(size_t)t * k + i] : -1;
-      bool ok = e >= 0 && e < N;
-      uint32_t my = ok ? (uint32_t)e : sentinel;
-      int rank = 0;
-      for (int i2 = 0; i2 < k; ++i2) {
-        int e2 = tv ? idx[(size_t)t * k + i2] : -1;
-        uint32_t other = (e2 >= 0 && e2 < N) ? (uint32_t)e2 : sentinel;
-        uint64_t m = ~0ull;
-        for (int b = 0; b < nbits; ++b) {
-          uint64_t bal = __ballot((other >> b) & 1u);
-          m &= ((my >> b) & 1u) ? bal : ~bal;
-        }
-        rank += __popcll(m & lt);
-        // the same token listing the expert in an earlier slot comes first
-        if (i2 < i && other == my && ok) ++rank;
+  for (int i = 0; i < k; ++i) {
+    const int e = tv ? idx[(size_t)t * k + i] : -1;
+    const bool ok = e >= 0 && e < N;
+    const uint32_t my = ok ? (uint32_t)e : sentinel;
+    int rank = 0;
+    for (int i2 = 0; i2 < k; ++i2) {
+      const int e2 = tv ? idx[(size_t)t * k + i2] : -1;
+      const uint32_t other = (e2 >= 0 && e2 < N) ? (uint32_t)e2 : sentinel;
+      uint64_t m = ~0ull;
+      for (int bit = 0; bit < nbits; ++bit) {
+        const uint64_t bal = __ballot((other >> bit) & 1u);
+        m &= ((my >> bit) & 1u) ? bal : ~bal;
       }
-      if (ok) {
-        int pos = hist[w * N + (int)my] + rank;
-        perm_token[pos] = t;
-        inv_perm[(size_t)t * k + i] = pos;
-      } else if (tv) {
-        inv_perm[(size_t)t * k + i] = -1;
-      }
+      rank += __popcll(m & lt);
+      // the same token listing the expert in an earlier slot comes first
+      if (i2 < i && other == my && ok) ++rank;
     }
-    // advance the wave's bases by this group's counts (after all reads)
-    __builtin_amdgcn_wave_barrier();
-    for (int i = 0; i < k; ++i) {
-      int e = tv ? idx[(size_t)t * k + i] : -1;
-      if (e >= 0 && e < N) atomicAdd(&hist[w * N + e], 1);
+    if (ok) {
+      const int pos = wh[w * N + (int)my] + rank;
+      perm_token[pos] = t;
+      inv_perm[(size_t)t * k + i] = pos;
+    } else if (tv) {
+      inv_perm[(size_t)t * k + i] = -1;
     }
-    __builtin_amdgcn_wave_barrier();
   }
 }
 
@@ -136,14 +160,22 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const uint8_t* __restr
 
 }  // namespace
 
-hipError_t launch_permute(const int32_t* topk_idx, int T, int k, int N, int32_t* counts,
-                          int32_t* offsets, int32_t* perm_token, int32_t* inv_perm,
-                          hipStream_t st) {
+int permute_blocks(int T) { return T <= 0 ? 1 : ceil_div(T, PB_TOK); }
+
+hipError_t launch_permute(const int32_t* topk_idx, int T, int k, int N, int32_t* hist,
+                          int32_t* counts, int32_t* offsets, int32_t* perm_token,
+                          int32_t* inv_perm, hipStream_t st) {
   int nbits = 1;
   while ((1 << nbits) <= N) ++nbits;  // 2^nbits > N: room for the sentinel
-  size_t lds = (size_t)(PW + 1) * N * sizeof(int32_t);
-  permute_kernel<<<1, 1024, lds, st>>>(topk_idx, T, k, N, nbits, counts, offsets, perm_token,
-                                       inv_perm);
+  const int nblk = permute_blocks(T);
+  if (nblk > 1) {
+    block_hist_kernel<<<nblk, 256, N * sizeof(int32_t), st>>>(topk_idx, T, k, N, hist);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const size_t lds = (size_t)(PB_WAVES + 2) * N * sizeof(int32_t);
+  permute_kernel<<<nblk, 256, lds, st>>>(topk_idx, T, k, N, nbits, nblk > 1 ? hist : nullptr,
+                                         nblk, counts, offsets, perm_token, inv_perm);
   return hipGetLastError();
 }
 

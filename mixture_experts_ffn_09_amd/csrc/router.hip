@@ -25,14 +25,18 @@ namespace {
 constexpr int RL_TM = 32, RL_TN = 64, RL_TK = 32;
 constexpr int RS_TM = 256, RS_KT = 256;
 
-template <bool BF16>
+template <bool BF16, int TPB>
 __global__ __launch_bounds__(256) void router_logits_small_n(const void* __restrict__ xv,
                                                              const float* __restrict__ w,
                                                              float* __restrict__ partial, int T,
                                                              int d, int N, int KC) {
+  // TPB tokens per workgroup, 256 / TPB lanes split each token's K range
+  constexpr int KL = 256 / TPB;
   __shared__ float ws[RS_KT][8];
+  __shared__ float red[KL > 1 ? KL : 1][TPB][8];
   const int tid = threadIdx.x;
-  const int t = blockIdx.x * RS_TM + tid;
+  const int tl = tid % TPB, kl = tid / TPB;
+  const int t = blockIdx.x * TPB + tl;
   const int s = blockIdx.z;
   const int k_begin = s * KC, k_end = min(d, k_begin + KC);
   float acc[8] = {};
@@ -46,7 +50,8 @@ __global__ __launch_bounds__(256) void router_logits_small_n(const void* __restr
     if (t < T) {
       if (BF16) {
         const uint16_t* xr = static_cast<const uint16_t*>(xv) + (size_t)t * d + kt;
-        for (int kk = 0; kk < kn; kk += 8) {  // bf16 K ranges are multiples of 8
+#pragma unroll 4
+        for (int kk = kl * 8; kk < kn; kk += 8 * KL) {  // bf16 K ranges are multiples of 8
           const u32x4_t q = *reinterpret_cast<const u32x4_t*>(xr + kk);
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
@@ -60,7 +65,7 @@ __global__ __launch_bounds__(256) void router_logits_small_n(const void* __restr
         }
       } else {
         const float* xr = static_cast<const float*>(xv) + (size_t)t * d + kt;
-        for (int kk = 0; kk < kn; ++kk) {
+        for (int kk = kl; kk < kn; kk += KL) {
           const float xk = xr[kk];
 #pragma unroll
           for (int e = 0; e < 8; ++e) acc[e] = fmaf(xk, ws[kk][e], acc[e]);
@@ -69,8 +74,121 @@ __global__ __launch_bounds__(256) void router_logits_small_n(const void* __restr
     }
     __syncthreads();
   }
-  if (t < T)
+  if (KL > 1) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) red[kl][tl][e] = acc[e];
+    __syncthreads();
+    if (kl == 0) {
+      for (int l = 1; l < KL; ++l)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] += red[l][tl][e];
+    }
+  }
+  if (kl == 0 && t < T)
     for (int e = 0; e < N; ++e) partial[((size_t)s * T + t) * N + e] = acc[e];
+}
+
+// ---------------------------------------------------------------------------
+// bf16 activations, N > 8: the float32 router weight is split exactly into
+// three bfloat16 planes (w = hi + mid + lo, 8 significand bits each), so each
+// product x * plane is exact in float32 (x is bf16) and three
+// v_mfma_f32_16x16x32_bf16 per step give the float32 dot product.  64 tokens
+// x 64 experts per workgroup (2 x 2 waves of 32 x 32); the weight slice is
+// split into the planes while it is staged in LDS in B-operand order;
+// activations load straight into A operands.  Optional split over K.
+// ---------------------------------------------------------------------------
+constexpr int RM_TM = 64, RM_TN = 64, RM_BK = 64;
+
+__device__ __forceinline__ void split3_bf16(float w, uint32_t& h, uint32_t& m, uint32_t& l) {
+  h = f32_to_bf16(w);
+  const float r1 = w - bf16_to_f32(h);   // exact
+  m = f32_to_bf16(r1);
+  const float r2 = r1 - bf16_to_f32(m);  // exact
+  l = f32_to_bf16(r2);
+}
+
+__global__ __launch_bounds__(256) void router_logits_mfma(const uint16_t* __restrict__ x,
+                                                          const float* __restrict__ w,
+                                                          float* __restrict__ partial, int T,
+                                                          int d, int N, int KC) {
+  // [plane][k step][n block][64 lanes][8 bf16]
+  __shared__ __attribute__((aligned(16))) uint16_t wl[3][RM_BK / 32][RM_TN / 16][64 * 8];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int t0 = blockIdx.x * RM_TM, e0 = blockIdx.y * RM_TN, s = blockIdx.z;
+  const int k_begin = s * KC, k_end = min(d, k_begin + KC);
+  // A rows of this lane for its two 16-token blocks (clamped; not stored)
+  const uint16_t* arow[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int t = min(t0 + (wm * 2 + i) * 16 + (lane & 15), T - 1);
+    arow[i] = x + (size_t)t * d + (lane >> 4) * 8;
+  }
+  floatx4_t acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+
+  for (int k0 = k_begin; k0 < k_end; k0 += RM_BK) {
+    // stage: each thread fills two B-operand lane slots (8 K values of one
+    // expert) in all three planes
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int slot = tid + 256 * r;          // 0 .. 511
+      const int frag = slot >> 6, l = slot & 63;
+      const int ks = frag / (RM_TN / 16), nb = frag % (RM_TN / 16);
+      const int e = e0 + nb * 16 + (l & 15);
+      const int kb = k0 + ks * 32 + (l >> 4) * 8;
+      uint32_t hh[4], mm[4], ll[4];
+#pragma unroll
+      for (int j = 0; j < 8; j += 2) {
+        const float w0 = (e < N && kb + j < k_end) ? w[(size_t)(kb + j) * N + e] : 0.f;
+        const float w1 = (e < N && kb + j + 1 < k_end) ? w[(size_t)(kb + j + 1) * N + e] : 0.f;
+        uint32_t h0, m0, l0, h1, m1, l1;
+        split3_bf16(w0, h0, m0, l0);
+        split3_bf16(w1, h1, m1, l1);
+        hh[j / 2] = h0 | (h1 << 16);
+        mm[j / 2] = m0 | (m1 << 16);
+        ll[j / 2] = l0 | (l1 << 16);
+      }
+      *reinterpret_cast<u32x4_t*>(&wl[0][ks][nb][l * 8]) = u32x4_t{hh[0], hh[1], hh[2], hh[3]};
+      *reinterpret_cast<u32x4_t*>(&wl[1][ks][nb][l * 8]) = u32x4_t{mm[0], mm[1], mm[2], mm[3]};
+      *reinterpret_cast<u32x4_t*>(&wl[2][ks][nb][l * 8]) = u32x4_t{ll[0], ll[1], ll[2], ll[3]};
+    }
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < RM_BK / 32; ++ks) {
+      const int kk = k0 + ks * 32;
+      if (kk >= k_end) break;  // K chunks are multiples of 32
+      u32x4_t a[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) a[i] = *reinterpret_cast<const u32x4_t*>(arow[i] + kk);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int nb = wn * 2 + j;
+#pragma unroll
+        for (int pl = 0; pl < 3; ++pl) {
+          const u32x4_t b = *reinterpret_cast<const u32x4_t*>(&wl[pl][ks][nb][lane * 8]);
+#pragma unroll
+          for (int i = 0; i < 2; ++i) acc[i][j] = mfma16x16x32(a[i], b, acc[i][j]);
+        }
+      }
+    }
+    __syncthreads();
+  }
+  // lane holds rows 4*(lane/16)+q of column lane%16
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int t = t0 + (wm * 2 + i) * 16 + (lane >> 4) * 4 + q;
+        const int e = e0 + (wn * 2 + j) * 16 + (lane & 15);
+        if (t < T && e < N) partial[((size_t)s * T + t) * N + e] = acc[i][j][q];
+      }
 }
 
 template <bool BF16>
@@ -224,39 +342,56 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
 
 }  // namespace
 
-int router_splits(int T, int N, int d) {
+// Router kernel choice: N <= 8 -> small_n; bf16 x -> MFMA; else tiled fp32.
+static int router_tiles(int T, int N, bool mfma) {
+  if (N <= 8) return ceil_div(T, RS_TM);
+  if (mfma) return ceil_div(T, RM_TM) * ceil_div(N, RM_TN);
+  return ceil_div(T, RL_TM) * ceil_div(N, RL_TN);
+}
+
+int router_splits(int T, int N, int d, bool act_bf16) {
   if (T <= 0) return 1;
-  const int tiles = N <= 8 ? ceil_div(T, RS_TM) : ceil_div(T, RL_TM) * ceil_div(N, RL_TN);
+  const int tiles = router_tiles(T, N, act_bf16 && N > 8);
   // enough workgroups to fill the chip, but at least 256 of K per split
   int S = 1024 / tiles;
   S = S < 1 ? 1 : S;
   const int smax = ceil_div(d, 256);
   S = S > smax ? smax : S;
-  const int KC = ceil_div(ceil_div(d, S), 32) * 32;
+  const int KC = ceil_div(ceil_div(d, S), 64) * 64;
   return ceil_div(d, KC);
 }
 
-static int router_chunk(int T, int N, int d) {
-  const int S = router_splits(T, N, d);
-  return ceil_div(ceil_div(d, S), 32) * 32;
+static int router_chunk(int T, int N, int d, bool act_bf16) {
+  const int S = router_splits(T, N, d, act_bf16);
+  return ceil_div(ceil_div(d, S), 64) * 64;
 }
 
 hipError_t launch_router_logits(const void* x, bool act_bf16, const float* w_router,
                                 float* partial, int T, int d, int N, hipStream_t st) {
-  const int S = router_splits(T, N, d);
-  const int KC = router_chunk(T, N, d);
+  const int S = router_splits(T, N, d, act_bf16);
+  const int KC = router_chunk(T, N, d, act_bf16);
   if (N <= 8) {
-    dim3 grid(ceil_div(T, RS_TM), 1, S);
-    if (act_bf16)
-      router_logits_small_n<true><<<grid, 256, 0, st>>>(x, w_router, partial, T, d, N, KC);
-    else
-      router_logits_small_n<false><<<grid, 256, 0, st>>>(x, w_router, partial, T, d, N, KC);
+    // few tokens: spread each token's K over lanes of the workgroup
+    if (T <= 16) {
+      dim3 grid(ceil_div(T, 16), 1, S);
+      if (act_bf16)
+        router_logits_small_n<true, 16><<<grid, 256, 0, st>>>(x, w_router, partial, T, d, N, KC);
+      else
+        router_logits_small_n<false, 16><<<grid, 256, 0, st>>>(x, w_router, partial, T, d, N, KC);
+    } else {
+      dim3 grid(ceil_div(T, RS_TM), 1, S);
+      if (act_bf16)
+        router_logits_small_n<true, RS_TM><<<grid, 256, 0, st>>>(x, w_router, partial, T, d, N, KC);
+      else
+        router_logits_small_n<false, RS_TM><<<grid, 256, 0, st>>>(x, w_router, partial, T, d, N, KC);
+    }
+  } else if (act_bf16) {
+    dim3 grid(ceil_div(T, RM_TM), ceil_div(N, RM_TN), S);
+    router_logits_mfma<<<grid, 256, 0, st>>>(static_cast<const uint16_t*>(x), w_router, partial,
+                                             T, d, N, KC);
   } else {
     dim3 grid(ceil_div(T, RL_TM), ceil_div(N, RL_TN), S);
-    if (act_bf16)
-      router_logits_tiled<true><<<grid, 256, 0, st>>>(x, w_router, partial, T, d, N, KC);
-    else
-      router_logits_tiled<false><<<grid, 256, 0, st>>>(x, w_router, partial, T, d, N, KC);
+    router_logits_tiled<false><<<grid, 256, 0, st>>>(x, w_router, partial, T, d, N, KC);
   }
   return hipGetLastError();
 }

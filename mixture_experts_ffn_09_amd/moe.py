@@ -70,7 +70,7 @@ def lib() -> C.CDLL:
         L.moe_workspace_bytes.argtypes = [S]
         L.moe_workspace_bytes.restype = C.c_size_t
         L.moe_router_topk.argtypes = [S, P, C.POINTER(Weights), P, P, P, C.c_size_t, P]
-        L.moe_permute.argtypes = [S, P, P, C.POINTER(Routing), P, P]
+        L.moe_permute.argtypes = [S, P, P, C.POINTER(Routing), P, P, C.c_size_t, P]
         L.moe_grouped_ffn.argtypes = [S, P, P, P, P, C.POINTER(Weights), P, P, P, C.c_size_t, P]
         L.moe_expert_gate_up.argtypes = [S, P, P, P, P, C.POINTER(Weights), P, P, P,
                                          C.c_size_t, P]
@@ -159,9 +159,10 @@ def moe_router_topk(shape: Shape, x: torch.Tensor, weights: Weights, topk_idx: t
 
 
 def moe_permute(shape: Shape, topk_idx: torch.Tensor, x: Optional[torch.Tensor],
-                routing: Routing, x_perm: Optional[torch.Tensor] = None):
+                routing: Routing, ws: torch.Tensor, x_perm: Optional[torch.Tensor] = None):
     _check(lib().moe_permute(C.byref(shape), _ptr(topk_idx), _ptr(x), C.byref(routing),
-                             _ptr(x_perm), _stream()))
+                             _ptr(x_perm), _ptr(ws), ws.numel() * ws.element_size(),
+                             _stream()))
 
 
 def moe_grouped_ffn(shape: Shape, x: Optional[torch.Tensor], x_perm: Optional[torch.Tensor],

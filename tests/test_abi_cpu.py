@@ -111,7 +111,7 @@ def test_null_shape_and_pointers():
                    None, FAKE, C.c_size_t(1 << 40), None) == moe.MOE_ERR_INVALID_ARG
     # permute without outputs
     r = moe.Routing()
-    assert _status("moe_permute", C.byref(s), FAKE, None, C.byref(r), None, None) == \
+    assert _status("moe_permute", C.byref(s), FAKE, None, C.byref(r), None, FAKE, ws, None) == \
         moe.MOE_ERR_INVALID_ARG
     # pack: src_b must be given exactly for the gate/up weight
     assert _status("moe_pack_weights", C.byref(s), 0, 1, FAKE, None, FAKE, None) == \
@@ -132,14 +132,19 @@ def test_workspace_too_small():
     assert b"needed" in _lib().moe_last_error()
 
 
-def _router_splits(T, N, d):
+def _router_splits(T, N, d, bf16=True):
     """Number of K-splits of the router logits (restated from the library's
     sizing rule: ~1024 workgroups, at least 256 of K per split)."""
     cdiv = lambda a, b: -(-a // b)
-    tiles = cdiv(T, 256) if N <= 8 else cdiv(T, 32) * cdiv(N, 64)
+    if N <= 8:
+        tiles = cdiv(T, 256)
+    elif bf16:
+        tiles = cdiv(T, 64) * cdiv(N, 64)
+    else:
+        tiles = cdiv(T, 32) * cdiv(N, 64)
     S = max(1, 1024 // tiles)
     S = min(S, cdiv(d, 256))
-    KC = cdiv(cdiv(d, S), 32) * 32
+    KC = cdiv(cdiv(d, S), 64) * 64
     return cdiv(d, KC)
 
 
@@ -151,7 +156,7 @@ def test_workspace_size_formula(T, N, k, d, f, sh):
     a = lambda v: (v + 255) // 256 * 256
     S = _router_splits(T, N, d)
     want = (a(S * T * N * 4) + 2 * a(T * k * 4) + a(N * 4) + a((N + 1) * 4) + 2 * a(T * k * 4)
-            + a(2048 * 4) + a(T * k * f * 2) + a(sh * T * f * 2) + a(T * k * d * 2)
+            + a(-(-T // 256) * N * 4) + a(2048 * 4) + a(T * k * f * 2) + a(sh * T * f * 2) + a(T * k * d * 2)
             + a(sh * T * d * 2))
     assert moe.moe_workspace_bytes(s) == want
 

@@ -128,7 +128,7 @@ def test_stages_through_abi_match_layer_forward():
     rb = L.routing_buffers()
     moe.moe_router_topk(s, xd, L.weights, rb["topk_idx"], rb["topk_w"], ws)
     x_perm = torch.empty(cfg.T * cfg.top_k, cfg.d_model, dtype=xd.dtype, device="cuda")
-    moe.moe_permute(s, rb["topk_idx"], xd, moe.make_routing(**rb), x_perm)
+    moe.moe_permute(s, rb["topk_idx"], xd, moe.make_routing(**rb), ws, x_perm)
     y = torch.empty(cfg.T * cfg.top_k, cfg.d_model, dtype=xd.dtype, device="cuda")
     ys = torch.empty(cfg.T, cfg.d_model, dtype=xd.dtype, device="cuda")
     moe.moe_grouped_ffn(s, xd, x_perm, None, rb["offsets"], L.weights, y, ys, ws)
@@ -198,3 +198,39 @@ def test_zero_tokens_is_a_noop():
     ws = torch.empty(256, dtype=torch.uint8, device="cuda")
     moe.moe_layer_forward(s, L.weights, x, out, ws)
     assert moe.moe_workspace_bytes(s) == 0
+
+
+@pytest.mark.parametrize("T,N,k", [(1000, 300, 5), (16, 8, 2), (256, 512, 8), (4096, 256, 8)])
+def test_permute_direct_against_sorted(T, N, k):
+    """moe_permute on given ids (several 256-token blocks, a ragged tail,
+    N above 256): counts, offsets and rows equal a Python sort of the valid
+    (expert, token, slot) keys; out-of-range ids are not counted and map to
+    -1; a token listing an expert twice gets consecutive rows."""
+    rng = np.random.default_rng(T + N + k)
+    idx = np.stack([rng.permutation(N)[:k] for _ in range(T)]).astype(np.int32)
+    if T > 20:
+        idx[3, 0] = -1
+        idx[7, k - 1] = N + 3
+        idx[11, 1] = idx[11, 0]  # duplicate within a token
+    s = moe.make_shape(T, 64, N, k, 64)
+    dev = "cuda"
+    r = {"counts": torch.empty(N, dtype=torch.int32, device=dev),
+         "offsets": torch.empty(N + 1, dtype=torch.int32, device=dev),
+         "perm_token": torch.full((T * k,), -7, dtype=torch.int32, device=dev),
+         "inv_perm": torch.empty(T, k, dtype=torch.int32, device=dev)}
+    ws = torch.empty(moe.moe_workspace_bytes(s), dtype=torch.uint8, device=dev)
+    moe.moe_permute(s, torch.from_numpy(idx).to(dev), None, moe.make_routing(**r), ws)
+    torch.cuda.synchronize()
+    g = {kk: v.cpu().numpy() for kk, v in r.items()}
+    keys = sorted((int(idx[t, i]), t, i) for t in range(T) for i in range(k) if 0 <= idx[t, i] < N)
+    nvalid = len(keys)
+    cnt = np.zeros(N, dtype=np.int64)
+    for e, _, _ in keys:
+        cnt[e] += 1
+    assert np.array_equal(g["counts"], cnt)
+    assert np.array_equal(g["offsets"], np.concatenate([[0], np.cumsum(cnt)]))
+    assert list(g["perm_token"][:nvalid]) == [t for _, t, _ in keys]
+    want_inv = np.full((T, k), -1)
+    for row, (e, t, i) in enumerate(keys):
+        want_inv[t, i] = row
+    assert np.array_equal(g["inv_perm"], want_inv)

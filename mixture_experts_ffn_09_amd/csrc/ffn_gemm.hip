@@ -17,8 +17,8 @@
 // 1 KB in LDS is one MFMA operand (lane l holds row l % 16, k = 8 * (l / 16)
 // + j): the activation copy picks its global addresses to produce that order
 // and the weights are pre-packed in it, so operand reads are contiguous
-// ds_read_b128.  Two 64-K stages: the copy of stage kt+1 is in flight while
-// stage kt is multiplied.
+// ds_read_b128.  A ring of up to four stages (32 K each; 64 for FP8) keeps
+// the copies of the next stages in flight while one is multiplied.
 //
 // Tile order: workgroup ids are spread over the 8 XCDs round-robin, so the
 // linear tile index is remapped to give each XCD a contiguous range, and the
@@ -33,7 +33,6 @@
 namespace {
 
 constexpr int GM_BN = 256;    // weight rows per workgroup tile
-constexpr int GM_BK = 64;     // K per LDS stage
 constexpr int GM_GN = 8;      // weight tiles per tile-order group
 constexpr int NXCD = 8;
 
@@ -119,21 +118,24 @@ __device__ __forceinline__ void barrier_no_fence() {
 
 template <int BM, bool GATED, bool FP8>
 __global__ __launch_bounds__(512, 1) void ffn_gemm_kernel(GemmParams p) {
-  constexpr int NS = 2;               // LDS stages in the ring
   constexpr int NWN = 4;              // wave grid 2 x 4 (8 waves, two per SIMD)
   constexpr int MBW = BM / 32;        // 16-row blocks per wave (wave tile BM/2 rows)
   constexpr int NBW = 4;              // 16-row weight blocks per wave (wave tile 64 wide)
   constexpr int AFR = BM / 16;        // activation fragments per 32-K step
   constexpr int WBL = NWN * NBW;      // weight blocks per tile (GM_BN / 16)
   constexpr int NH = GATED ? 2 : 1;
-  // per stage: activations [2 K steps][AFR] KB, weights [2][WBL] KB (FP8:
-  // [WBL] KB, one 16-byte lane chunk holds both K steps)
-  constexpr int A_BYTES = 2 * AFR * 1024;
-  constexpr int B_FRAGS = FP8 ? WBL : 2 * WBL;
+  // One stage = SK 32-K steps (FP8: 2, the width of one packed block).
+  constexpr int SK = FP8 ? 2 : 1;
+  constexpr int A_BYTES = SK * AFR * 1024;
+  constexpr int B_FRAGS = WBL * (FP8 ? 1 : SK);
   constexpr int STAGE = A_BYTES + B_FRAGS * 1024;
-  constexpr int A_PER_WAVE = 2 * AFR / 8;
+  constexpr int NS = (160 * 1024 / STAGE) < 4 ? (160 * 1024 / STAGE) : 4;  // ring depth
+  constexpr int A_PER_WAVE = SK * AFR / 8;
   constexpr int B_PER_WAVE = B_FRAGS / 8;
+  constexpr int LPS = A_PER_WAVE + B_PER_WAVE;  // copies per wave per stage
+  constexpr int KSTAGE = 32 * SK;
   static_assert(GM_BN == WBL * 16, "tile width");
+  static_assert(NS >= 2 && (NS - 2) * LPS < 64, "ring");
   __shared__ __attribute__((aligned(1024))) uint8_t lds[NS * STAGE];
 
   const int tid = threadIdx.x;
@@ -164,7 +166,7 @@ __global__ __launch_bounds__(512, 1) void ffn_gemm_kernel(GemmParams p) {
   const bool shared = g >= p.N;
   uint16_t* out = shared ? p.out_sh : p.out;
 
-  const int KT = p.K / GM_BK;                 // LDS stages over K
+  const int KT = p.K / KSTAGE;                // stages over K
   const int KS = FP8 ? p.K / 64 : p.K / 32;   // packed weight K steps
   const size_t wbytes = (size_t)NH * p.n_out * p.K * (FP8 ? 1 : 2);
   const uint8_t* W = shared ? p.w_sh : p.w + (size_t)g * wbytes;
@@ -184,8 +186,8 @@ __global__ __launch_bounds__(512, 1) void ffn_gemm_kernel(GemmParams p) {
 #pragma unroll
   for (int i = 0; i < B_PER_WAVE; ++i) {
     const int q = wave * B_PER_WAVE + i;
-    const int jb = FP8 ? q : (q >> 1);
-    const int sb = FP8 ? 0 : (q & 1);
+    const int jb = FP8 ? q : (q % WBL);
+    const int sb = FP8 ? 0 : (q / WBL);
     bsrc[i] = W + block_offset(jb) + lane * 16;
     bks[i] = sb;
     bdst[i] = A_BYTES + (FP8 ? jb : (sb * WBL + jb)) * 1024;
@@ -195,7 +197,7 @@ __global__ __launch_bounds__(512, 1) void ffn_gemm_kernel(GemmParams p) {
 #pragma unroll
   for (int i = 0; i < A_PER_WAVE; ++i) {
     const int q = wave * A_PER_WAVE + i;
-    const int mb = q >> 1, sa = q & 1;
+    const int mb = q % AFR, sa = q / AFR;
     const int r = min(m0 + mb * 16 + (lane & 15), rows - 1);  // rows past the end are not stored
     const uint16_t* ptr;
     if (shared)
@@ -211,12 +213,12 @@ __global__ __launch_bounds__(512, 1) void ffn_gemm_kernel(GemmParams p) {
     uint8_t* base = lds + (kt % NS) * STAGE;
 #pragma unroll
     for (int i = 0; i < A_PER_WAVE; ++i)
-      __builtin_amdgcn_global_load_lds((const void*)(asrc[i] + kt * GM_BK),
+      __builtin_amdgcn_global_load_lds((const void*)(asrc[i] + kt * KSTAGE),
                                        (void*)(base + adst[i]), 16, 0, 0);
 #pragma unroll
     for (int i = 0; i < B_PER_WAVE; ++i)
       __builtin_amdgcn_global_load_lds(
-          (const void*)(bsrc[i] + (size_t)(FP8 ? kt : kt * 2 + bks[i]) * wstep),
+          (const void*)(bsrc[i] + (size_t)(FP8 ? kt : kt * SK + bks[i]) * wstep),
           (void*)(base + bdst[i]), 16, 0, 0);
   };
 
@@ -230,9 +232,9 @@ __global__ __launch_bounds__(512, 1) void ffn_gemm_kernel(GemmParams p) {
     else
       srow[j] = ((nt * WBL + jb) * 16) / MOE_FP8_BLOCK;
   }
-  const int SK = p.K / MOE_FP8_BLOCK;
+  const int SKB = p.K / MOE_FP8_BLOCK;
   const float* S = nullptr;
-  if (FP8) S = shared ? p.s_sh : p.s + (size_t)g * NH * (p.n_out / MOE_FP8_BLOCK) * SK;
+  if (FP8) S = shared ? p.s_sh : p.s + (size_t)g * NH * (p.n_out / MOE_FP8_BLOCK) * SKB;
 
   floatx4_t acc[MBW][NBW];
   floatx4_t part[FP8 ? MBW : 1][NBW];
@@ -245,12 +247,21 @@ __global__ __launch_bounds__(512, 1) void ffn_gemm_kernel(GemmParams p) {
 #pragma unroll
     for (int j = 0; j < NBW; ++j) part[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
-  issue_stage(0);
-  wait_vmcnt<0>();
-  barrier_no_fence();
+  // prologue: NS-1 stages in flight
+#pragma unroll
+  for (int st = 0; st < NS - 1; ++st)
+    if (st < KT) issue_stage(st);
+
   for (int kt = 0; kt < KT; ++kt) {
-    // the other buffer was last read in stage kt-1, before the barrier below
-    if (kt + 1 < KT) issue_stage(kt + 1);
+    // stage kt has landed (this wave's copies): later stages may still fly
+    const int later = min(NS - 2, KT - 1 - kt);
+    if (NS - 2 >= 2 && later >= 2) wait_vmcnt<(NS - 2 >= 2 ? 2 : 0) * LPS>();
+    else if (later == 1) wait_vmcnt<LPS>();
+    else wait_vmcnt<0>();
+    // everyone's copies of stage kt are visible, and stage kt-1 is no
+    // longer read: its buffer takes stage kt+NS-1
+    barrier_no_fence();
+    if (kt + NS - 1 < KT) issue_stage(kt + NS - 1);
     const uint8_t* base = lds + (kt % NS) * STAGE;
     u32x4_t bq[NBW];
     if (FP8) {
@@ -259,7 +270,7 @@ __global__ __launch_bounds__(512, 1) void ffn_gemm_kernel(GemmParams p) {
         bq[j] = *reinterpret_cast<const u32x4_t*>(base + A_BYTES + (wn * NBW + j) * 1024 + lane * 16);
     }
 #pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
+    for (int s2 = 0; s2 < SK; ++s2) {
       u32x4_t af[MBW], bf[NBW];
 #pragma unroll
       for (int i = 0; i < MBW; ++i)
@@ -272,6 +283,7 @@ __global__ __launch_bounds__(512, 1) void ffn_gemm_kernel(GemmParams p) {
         else
           fp8_half_to_bf16(bq[j], s2, bf[j]);
       }
+      __builtin_amdgcn_sched_barrier(0);  // all operand reads issued before the MFMAs
 #pragma unroll
       for (int i = 0; i < MBW; ++i)
 #pragma unroll
@@ -287,7 +299,7 @@ __global__ __launch_bounds__(512, 1) void ffn_gemm_kernel(GemmParams p) {
       const int kc = kt >> 1;
 #pragma unroll
       for (int j = 0; j < NBW; ++j) {
-        const float sc = S[(size_t)srow[j] * SK + kc];
+        const float sc = S[(size_t)srow[j] * SKB + kc];
 #pragma unroll
         for (int i = 0; i < (FP8 ? MBW : 1); ++i) {
 #pragma unroll
@@ -296,11 +308,9 @@ __global__ __launch_bounds__(512, 1) void ffn_gemm_kernel(GemmParams p) {
         }
       }
     }
-    // stage kt+1 landed (this wave's copies), then everyone's; stage kt is
-    // no longer read after this barrier
-    wait_vmcnt<0>();
+    // this wave's operand reads of stage kt are complete before the next
+    // barrier lets its buffer be refilled
     __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
-    barrier_no_fence();
   }
 
   // epilogue: acc[i][j] lane holds rows 4*(lane/16)+e of column lane%16

@@ -97,6 +97,10 @@ __global__ __launch_bounds__(1024) void tile_schedule_kernel(GemmParams p, int b
   if (i == 0) tiles[0] = 0;
 }
 
+// Fourth dword of a raw buffer resource on gfx950 (32-bit data format, no
+// swizzle), as used for bounds-checked byte-addressed loads.
+constexpr int BUF_DWORD3 = 0x00020000;
+
 // s_waitcnt vmcnt(N) leaving the other counters untouched (gfx9 encoding:
 // vmcnt low bits 3:0 and high bits 15:14, expcnt 6:4, lgkmcnt 11:8).
 template <int N>
@@ -339,6 +343,206 @@ __global__ __launch_bounds__(512, 1) void ffn_gemm_kernel(GemmParams p) {
   }
 }
 
+// Large-tile form for bf16 weights and many rows per group: 4 waves (one
+// per SIMD), 256 rows x 256 weight rows per workgroup, each wave 128 x 128
+// (256 accumulator registers, held in AGPRs).  Per 32-K stage a wave reads
+// 16 KB of operands from LDS for 64 MFMAs, a third less LDS traffic per flop
+// than the 8-wave form.  With a single wave per SIMD nothing hides a stall,
+// so each stage spreads its eight operand copies and sixteen fragment reads
+// evenly between its MFMAs instead of issuing them in bursts.
+template <bool GATED>
+__global__ __launch_bounds__(256, 1) void ffn_gemm_big_kernel(GemmParams p) {
+  constexpr int BM = 256;
+  constexpr int MBW = 8, NBW = 8;     // 16-row blocks per wave
+  constexpr int AFR = BM / 16;        // activation fragments per stage (one 32-K step)
+  constexpr int WBL = GM_BN / 16;     // weight blocks per stage
+  constexpr int NH = GATED ? 2 : 1;
+  constexpr int A_BYTES = AFR * 1024;
+  constexpr int STAGE = A_BYTES + WBL * 1024;
+  constexpr int NS = 4;                 // ring depth: NS-1 stages in flight
+  constexpr int A_PER_WAVE = AFR / 4, B_PER_WAVE = WBL / 4;
+  constexpr int LPS = A_PER_WAVE + B_PER_WAVE;
+  static_assert(NS * STAGE <= 160 * 1024, "LDS");
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[NS * STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+
+  const int ngroups = p.g1 - p.g0;
+  const int MT = p.tiles[ngroups];
+  const int per = gridDim.x / NXCD;
+  const int L = (blockIdx.x % NXCD) * per + blockIdx.x / NXCD;
+  if (L >= MT * p.NT) return;
+  const int blk = L / (MT * GM_GN);
+  const int gw = min(GM_GN, p.NT - blk * GM_GN);
+  const int rr = L - blk * MT * GM_GN;
+  const int mt = rr / gw;
+  const int nt = blk * GM_GN + rr % gw;
+  int lo = 0, hi = ngroups - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (p.tiles[mid] <= mt) lo = mid; else hi = mid - 1;
+  }
+  const int g = p.g0 + lo;
+  const int m0 = (mt - p.tiles[lo]) * BM;
+  int row_base, rows;
+  group_rows(p, g, row_base, rows);
+  const bool shared = g >= p.N;
+  uint16_t* out = shared ? p.out_sh : p.out;
+
+  const int KT = p.K / 32;
+  const size_t wbytes = (size_t)NH * p.n_out * p.K * 2;
+  const uint8_t* W = shared ? p.w_sh : p.w + (size_t)g * wbytes;
+  const size_t wstep = (size_t)NH * 1024;
+
+  // Operands are copied with buffer loads straight into LDS: the per-lane
+  // byte offsets stay in VGPRs for the whole loop and the K advance is a
+  // scalar offset, so a stage's copies need no address arithmetic.  Reads
+  // past a resource's size return zero.
+  const __amdgpu_buffer_rsrc_t wres =
+      __builtin_amdgcn_make_buffer_rsrc((void*)W, 0, (int)(uint32_t)wbytes, BUF_DWORD3);
+  uint32_t boff[B_PER_WAVE];
+  int bdst[B_PER_WAVE];
+#pragma unroll
+  for (int i = 0; i < B_PER_WAVE; ++i) {
+    const int jb = wave * B_PER_WAVE + i;
+    uint32_t off;
+    if (GATED) {
+      const int pb = nt * (WBL / 2) + (jb >> 1);
+      off = (((uint32_t)pb * KT) * 2 + (jb & 1)) * 1024;
+    } else {
+      off = ((uint32_t)(nt * WBL + jb) * KT) * 1024;
+    }
+    boff[i] = off + lane * 16;
+    bdst[i] = A_BYTES + jb * 1024;
+  }
+  const uint16_t* abase = shared ? p.a_sh : p.a;
+  const uint32_t abytes = (uint32_t)((size_t)(shared ? rows : (p.perm ? p.T : row_base + rows)) * p.K * 2);
+  const __amdgpu_buffer_rsrc_t ares =
+      __builtin_amdgcn_make_buffer_rsrc((void*)abase, 0, (int)abytes, BUF_DWORD3);
+  uint32_t aoff[A_PER_WAVE];
+  int adst[A_PER_WAVE];
+#pragma unroll
+  for (int i = 0; i < A_PER_WAVE; ++i) {
+    const int mb = wave * A_PER_WAVE + i;
+    const int r = min(m0 + mb * 16 + (lane & 15), rows - 1);  // rows past the end are not stored
+    int src;
+    if (shared)
+      src = r;
+    else if (p.perm)
+      src = p.perm[row_base + r];
+    else
+      src = row_base + r;
+    aoff[i] = (uint32_t)src * (uint32_t)p.K * 2 + (lane >> 4) * 16;
+    adst[i] = mb * 1024;
+  }
+  typedef __attribute__((address_space(3))) void* lds_ptr_t;
+  // the q-th of a wave's LPS copies of stage kl into ring buffer buf
+  auto copy_one = [&](int q, int kl, int buf) {
+    uint8_t* base = lds + buf * STAGE;
+    if (q < A_PER_WAVE)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ares, (lds_ptr_t)(base + adst[q]), 16, aoff[q],
+                                               kl * 64, 0, 0);
+    else
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(wres, (lds_ptr_t)(base + bdst[q - A_PER_WAVE]), 16,
+                                               boff[q - A_PER_WAVE], kl * (int)wstep, 0, 0);
+  };
+
+  floatx4_t acc[MBW][NBW];
+#pragma unroll
+  for (int i = 0; i < MBW; ++i)
+#pragma unroll
+    for (int j = 0; j < NBW; ++j) acc[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+  u32x4_t ca[MBW], cb[NBW], na[MBW], nb[NBW];
+  // fragment f of stage kt: f < MBW are activation blocks, the rest weight blocks
+  auto read_one = [&](u32x4_t (&fa)[MBW], u32x4_t (&fb)[NBW], int f, int kt) {
+    const uint8_t* base = lds + (kt % NS) * STAGE;
+    if (f < MBW)
+      fa[f] = *reinterpret_cast<const u32x4_t*>(base + ((wm * MBW + f) * 64 + lane) * 16);
+    else
+      fb[f - MBW] = *reinterpret_cast<const u32x4_t*>(
+          base + A_BYTES + ((wn * NBW + f - MBW) * 64 + lane) * 16);
+  };
+  // Stage kt: wait until stage kt+1 has landed for every wave, then run
+  // stage kt's 64 MFMAs with two streams interleaved: the copy of stage
+  // kt+NS-1 into the buffer of stage kt-1 (whose fragments the previous stage's
+  // MFMAs consumed) and the 16 fragment reads of stage kt+1.  Every stage
+  // issues its copy, clamped to the last K step near the end, so that one
+  // vmcnt threshold holds throughout and no branch splits the schedule; the
+  // clamped copies only land in buffers no later stage reads, and the reads
+  // past the last stage land in registers that are never used.
+  auto stage = [&](const u32x4_t (&fa)[MBW], const u32x4_t (&fb)[NBW], u32x4_t (&ga)[MBW],
+                   u32x4_t (&gb)[NBW], int kt) {
+    wait_vmcnt<(NS - 3) * LPS>();
+    barrier_no_fence();
+    __builtin_amdgcn_sched_barrier(0);
+    // program order already alternates copies and reads, as the compiler may
+    // not move an LDS read past a copy into LDS
+#pragma unroll
+    for (int q = 0; q < LPS; ++q) {
+      copy_one(q, min(kt + NS - 1, KT - 1), (kt + NS - 1) % NS);
+      read_one(ga, gb, 2 * q, kt + 1);
+      read_one(ga, gb, 2 * q + 1, kt + 1);
+    }
+#pragma unroll
+    for (int i = 0; i < MBW; ++i)
+#pragma unroll
+      for (int j = 0; j < NBW; ++j) acc[i][j] = mfma16x16x32(fa[i], fb[j], acc[i][j]);
+#pragma unroll
+    for (int q = 0; q < LPS; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);  // one copy
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // two MFMAs
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);  // three MFMAs
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);  // three MFMAs
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  static_assert(LPS * 8 == MBW * NBW && LPS * 2 == MBW + NBW, "interleave pattern");
+
+  // K/32 is even (and at least 2) for every accepted shape
+#pragma unroll
+  for (int st = 0; st < NS - 1; ++st)
+#pragma unroll
+    for (int q = 0; q < LPS; ++q) copy_one(q, min(st, KT - 1), st);
+  wait_vmcnt<(NS - 2) * LPS>();
+  barrier_no_fence();
+#pragma unroll
+  for (int f = 0; f < MBW + NBW; ++f) read_one(ca, cb, f, 0);
+
+  for (int kt = 0; kt < KT; kt += 2) {
+    stage(ca, cb, na, nb, kt);
+    stage(na, nb, ca, cb, kt + 1);
+  }
+  wait_vmcnt<0>();  // the clamped copies of the last stages
+
+#pragma unroll
+  for (int i = 0; i < MBW; ++i) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = m0 + (wm * MBW + i) * 16 + (lane >> 4) * 4 + e;
+      if (r >= rows) continue;
+      uint16_t* orow = out + (size_t)(row_base + r) * p.n_out;
+      if (GATED) {
+#pragma unroll
+        for (int q = 0; q < NBW / 2; ++q) {
+          const int col = (nt * (WBL / 2) + wn * (NBW / 2) + q) * 16 + (lane & 15);
+          orow[col] = (uint16_t)f32_to_bf16(silu_f32(acc[i][2 * q][e]) * acc[i][2 * q + 1][e]);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < NBW; ++j) {
+          const int col = (nt * WBL + wn * NBW + j) * 16 + (lane & 15);
+          orow[col] = (uint16_t)f32_to_bf16(acc[i][j][e]);
+        }
+      }
+    }
+  }
+}
+
 template <int BM, bool FP8>
 void launch_gemm_kernel(bool gated, long long nwg, const GemmParams& p, hipStream_t st) {
   if (gated)
@@ -356,6 +560,13 @@ bool gemm_shape_ok(int d, int d_ff) { return d % 256 == 0 && d_ff % 128 == 0; }
 hipError_t launch_ffn_gemm(const FfnArgs& a, int pass, int g0, int g1, int bm, int max_rows,
                            int32_t* sched, hipStream_t st) {
   if (g1 <= g0) return hipSuccess;
+  if (bm == 256) {
+    // the 256-row kernel addresses operands through 32-bit buffer offsets
+    const long long lim = 0x7fffffffLL;
+    if ((long long)a.T * a.d * 2 > lim || (long long)a.T * a.k * a.d_ff * 2 > lim ||
+        4LL * a.d * a.d_ff > lim)
+      bm = 128;
+  }
   for (int ps = 1; ps <= 2; ++ps) {
     if (!(pass & ps)) continue;
     const bool gated = ps == 1;
@@ -387,9 +598,12 @@ hipError_t launch_ffn_gemm(const FfnArgs& a, int pass, int g0, int g1, int bm, i
     nwg = (nwg + NXCD - 1) / NXCD * NXCD;
     if (a.fp8)
       launch_gemm_kernel<128, true>(gated, nwg, p, st);
-    else if (bm == 256)
-      launch_gemm_kernel<256, false>(gated, nwg, p, st);
-    else
+    else if (bm == 256) {
+      if (gated)
+        ffn_gemm_big_kernel<true><<<dim3((unsigned)nwg), 256, 0, st>>>(p);
+      else
+        ffn_gemm_big_kernel<false><<<dim3((unsigned)nwg), 256, 0, st>>>(p);
+    } else
       launch_gemm_kernel<128, false>(gated, nwg, p, st);
     e = hipGetLastError();
     if (e != hipSuccess) return e;

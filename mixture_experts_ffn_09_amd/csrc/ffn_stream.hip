@@ -10,7 +10,7 @@
 // touch their weights.
 //
 // Work split: grid.y = group (routed expert, then the shared expert), grid.x
-// over 16-row blocks of the weight matrix.  Each wave owns P such blocks
+// over 16-row blocks of the weight matrix.  Each wave owns NP such blocks
 // (pairs of gate/up blocks in pass 1) and streams them along K exactly once
 // per 16*MB rows of activations, so the weight stream is read once for up to
 // 16*MB rows.  Weights are pre-packed so that one K step of one block is a
@@ -59,21 +59,23 @@ __device__ __forceinline__ void fp8_block_to_bf16(const u32x4_t& q, u32x4_t& lo,
   hi[3] = e4m3x2_to_bf16x2<true>(q[3]);
 }
 
-// GATED: pass 1 (gate+up, SwiGLU) else pass 2 (down).  One wave owns one
-// 16-row output block and walks K with a ring of D K-steps of loads in
-// flight (each step: NH weight blocks of 1 KB plus MB activation fragments).
-// Activation rows past the group's end are clamped to its last row: row m of
-// an MFMA result depends only on row m of A, and those rows are not stored.
-template <int MB, int D, bool FP8, bool GATED>
+// GATED: pass 1 (gate+up, SwiGLU) else pass 2 (down).  One wave owns NP
+// consecutive 16-row output blocks and walks K with a ring of D K-steps of
+// loads in flight (each step: NP * NH weight blocks of 1 KB plus MB
+// activation fragments, which serve all NP blocks).  Activation rows past
+// the group's end are clamped to its last row: row m of an MFMA result
+// depends only on row m of A, and those rows are not stored.
+template <int MB, int NP, int D, bool FP8, bool GATED>
 __global__ __launch_bounds__(256) void ffn_stream_kernel(StreamParams p) {
   constexpr int NH = GATED ? 2 : 1;
   constexpr int AF = FP8 ? 2 : 1;  // activation fragments per K step
   static_assert(!FP8 || D % 2 == 0, "FP8 needs an even ring depth");
+  static_assert(8 % NP == 0, "the NP blocks of a wave share one 128-row scale block");
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int NB = p.n_out / 16;
-  const int nb = blockIdx.x * SW_WAVES + wave;
-  if (nb >= NB) return;
+  const int NB = p.n_out / 16;  // a multiple of NP
+  const int nb0 = (blockIdx.x * SW_WAVES + wave) * NP;
+  if (nb0 >= NB) return;
 
   // grid rows: routed groups, then slices of the shared expert's T rows
   const bool shared = (int)blockIdx.y >= p.n_routed;
@@ -93,11 +95,12 @@ __global__ __launch_bounds__(256) void ffn_stream_kernel(StreamParams p) {
   const size_t wbytes = (size_t)NH * p.n_out * p.K * (FP8 ? 1 : 2);
   const uint8_t* W = shared ? p.w_sh : p.w + (size_t)g * wbytes;
   const int KS = FP8 ? p.K / 64 : p.K / 32;
-  const uint8_t* Wnb = W + (size_t)nb * KS * NH * 1024 + lane * 16;
+  const size_t bstride = (size_t)KS * NH * 1024;  // one 16-row block, all K
+  const uint8_t* Wnb = W + (size_t)nb0 * bstride + lane * 16;
   const int SK = p.K / MOE_FP8_BLOCK;
   const int SR = p.n_out / MOE_FP8_BLOCK;
   const float* S = nullptr;
-  if (FP8) S = (shared ? p.s_sh : p.s + (size_t)g * NH * SR * SK) + (size_t)((nb * 16) / MOE_FP8_BLOCK) * SK;
+  if (FP8) S = (shared ? p.s_sh : p.s + (size_t)g * NH * SR * SK) + (size_t)((nb0 * 16) / MOE_FP8_BLOCK) * SK;
 
   const int lrow = lane & 15;
   const int lk = (lane >> 4) * 8;
@@ -117,22 +120,27 @@ __global__ __launch_bounds__(256) void ffn_stream_kernel(StreamParams p) {
       arow[mb] = ptr + lk;
     }
 
-    floatx4_t acc[NH][MB];
-    floatx4_t part[NH][MB];
+    floatx4_t acc[NP][NH][MB];
+    floatx4_t part[NP][NH][MB];
 #pragma unroll
-    for (int h = 0; h < NH; ++h)
+    for (int j = 0; j < NP; ++j)
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        acc[h][mb] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-        part[h][mb] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-      }
+      for (int h = 0; h < NH; ++h)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          acc[j][h][mb] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+          part[j][h][mb] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+        }
 
-    u32x4_t bq[D][NH];
+    u32x4_t bq[D][NP][NH];
     u32x4_t aq[D][MB][AF];
     auto load_step = [&](int u, int ks) {
 #pragma unroll
-      for (int h = 0; h < NH; ++h)
-        bq[u][h] = *reinterpret_cast<const u32x4_t*>(Wnb + ((size_t)ks * NH + h) * 1024);
+      for (int j = 0; j < NP; ++j)
+#pragma unroll
+        for (int h = 0; h < NH; ++h)
+          bq[u][j][h] =
+              *reinterpret_cast<const u32x4_t*>(Wnb + j * bstride + ((size_t)ks * NH + h) * 1024);
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -148,38 +156,42 @@ __global__ __launch_bounds__(256) void ffn_stream_kernel(StreamParams p) {
 #pragma unroll
       for (int u = 0; u < D; ++u) {
         const int ks = ks0 + u;  // KS is a multiple of D: no bounds branch
-        {
-          if (!FP8) {
+        if (!FP8) {
+#pragma unroll
+          for (int j = 0; j < NP; ++j)
 #pragma unroll
             for (int h = 0; h < NH; ++h)
 #pragma unroll
               for (int mb = 0; mb < MB; ++mb)
-                acc[h][mb] = mfma16x16x32(aq[u][mb][0], bq[u][h], acc[h][mb]);
-          } else {
+                acc[j][h][mb] = mfma16x16x32(aq[u][mb][0], bq[u][j][h], acc[j][h][mb]);
+        } else {
+#pragma unroll
+          for (int j = 0; j < NP; ++j)
 #pragma unroll
             for (int h = 0; h < NH; ++h) {
               u32x4_t blo, bhi;
-              fp8_block_to_bf16(bq[u][h], blo, bhi);
+              fp8_block_to_bf16(bq[u][j][h], blo, bhi);
 #pragma unroll
               for (int mb = 0; mb < MB; ++mb) {
-                part[h][mb] = mfma16x16x32(aq[u][mb][0], blo, part[h][mb]);
-                part[h][mb] = mfma16x16x32(aq[u][mb][AF - 1], bhi, part[h][mb]);
+                part[j][h][mb] = mfma16x16x32(aq[u][mb][0], blo, part[j][h][mb]);
+                part[j][h][mb] = mfma16x16x32(aq[u][mb][AF - 1], bhi, part[j][h][mb]);
               }
             }
-            // every second 64-wide step closes a 128-wide scale block (D is
-            // even and ks0 a multiple of D, so ks and u have the same parity)
-            if (u & 1) {
-              const int kc = ks >> 1;
+          // every second 64-wide step closes a 128-wide scale block (D is
+          // even and ks0 a multiple of D, so ks and u have the same parity)
+          if (u & 1) {
+            const int kc = ks >> 1;
 #pragma unroll
-              for (int h = 0; h < NH; ++h) {
-                const float sc = S[(size_t)h * SR * SK + kc];
+            for (int h = 0; h < NH; ++h) {
+              const float sc = S[(size_t)h * SR * SK + kc];
+#pragma unroll
+              for (int j = 0; j < NP; ++j)
 #pragma unroll
                 for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
-                  for (int e = 0; e < 4; ++e) acc[h][mb][e] += sc * part[h][mb][e];
-                  part[h][mb] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+                  for (int e = 0; e < 4; ++e) acc[j][h][mb][e] += sc * part[j][h][mb][e];
+                  part[j][h][mb] = floatx4_t{0.f, 0.f, 0.f, 0.f};
                 }
-              }
             }
           }
         }
@@ -190,41 +202,61 @@ __global__ __launch_bounds__(256) void ffn_stream_kernel(StreamParams p) {
     }
 
     // epilogue: lane holds rows 4*(lane/16)+e of column lane%16
-    const int n = nb * 16 + lrow;
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
+    for (int j = 0; j < NP; ++j) {
+      const int n = (nb0 + j) * 16 + lrow;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = m0 + mb * 16 + (lane >> 4) * 4 + e;
-        if (r >= rows) continue;
-        float v;
-        if (GATED)
-          v = silu_f32(acc[0][mb][e]) * acc[NH - 1][mb][e];
-        else
-          v = acc[0][mb][e];
-        out[(size_t)(row_base + r) * p.n_out + n] = (uint16_t)f32_to_bf16(v);
-      }
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = m0 + mb * 16 + (lane >> 4) * 4 + e;
+          if (r >= rows) continue;
+          float v;
+          if (GATED)
+            v = silu_f32(acc[j][0][mb][e]) * acc[j][NH - 1][mb][e];
+          else
+            v = acc[j][0][mb][e];
+          out[(size_t)(row_base + r) * p.n_out + n] = (uint16_t)f32_to_bf16(v);
+        }
+    }
   }
 }
 
-template <int MB, int D, bool FP8, bool GATED>
+template <int MB, int NP, int D, bool FP8, bool GATED>
 hipError_t launch_stream_d(const StreamParams& sp, int groups, hipStream_t st) {
   // groups = grid rows (routed groups + shared slices)
-  const int NB = sp.n_out / 16;
-  dim3 grid(ceil_div(NB, SW_WAVES), groups);
-  ffn_stream_kernel<MB, D, FP8, GATED><<<grid, SW_WAVES * 64, 0, st>>>(sp);
+  const int NW = sp.n_out / 16 / NP;  // waves per group
+  dim3 grid(ceil_div(NW, SW_WAVES), groups);
+  ffn_stream_kernel<MB, NP, D, FP8, GATED><<<grid, SW_WAVES * 64, 0, st>>>(sp);
   return hipGetLastError();
 }
 
-// The ring depth must divide the number of K steps.
-template <int MB, int DMAX, bool FP8, bool GATED>
+// The ring depth must divide the number of K steps; it shrinks as NP grows
+// so that a wave keeps about 8 KB of weights in flight.
+template <int MB, int NP, bool FP8, bool GATED>
 hipError_t launch_stream(const StreamParams& sp, int groups, hipStream_t st) {
+  constexpr int DMAX = 8 / NP;
   const int KS = FP8 ? sp.K / 64 : sp.K / 32;
-  if (DMAX >= 8 && KS % 8 == 0) return launch_stream_d<MB, (DMAX >= 8 ? 8 : DMAX), FP8, GATED>(sp, groups, st);
-  if (DMAX >= 4 && KS % 4 == 0) return launch_stream_d<MB, (DMAX >= 4 ? 4 : DMAX), FP8, GATED>(sp, groups, st);
-  if (KS % 2 == 0) return launch_stream_d<MB, 2, FP8, GATED>(sp, groups, st);
+  if (DMAX >= 8 && KS % 8 == 0) return launch_stream_d<MB, NP, (DMAX >= 8 ? 8 : 2), FP8, GATED>(sp, groups, st);
+  if (DMAX >= 4 && KS % 4 == 0) return launch_stream_d<MB, NP, (DMAX >= 4 ? 4 : 2), FP8, GATED>(sp, groups, st);
+  if (KS % 2 == 0) return launch_stream_d<MB, NP, 2, FP8, GATED>(sp, groups, st);
   // FP8 K is a multiple of 128, so KS is even there
-  return launch_stream_d<MB, (FP8 ? 2 : 1), FP8, GATED>(sp, groups, st);
+  return launch_stream_d<MB, NP, (FP8 ? 2 : 1), FP8, GATED>(sp, groups, st);
+}
+
+// Weight blocks per wave.  The activation fragments of a K step are loaded
+// once per wave and used for all its blocks.  With fp8 weights a 16-row
+// activation step (bf16) is as large as two weight blocks, which on the down
+// pass (one weight block per step) makes the activation reads the larger
+// stream; there a wave takes two blocks (measured: 47% -> 64% of HBM peak
+// on the 7168 x 2048 fp8 down projection; four blocks, with the ring depth
+// halved again, reach only 60%).  Everywhere else one block per wave with
+// the deepest ring measured fastest.
+int stream_np(bool fp8, bool gated, int n_out) {
+  const int NB = n_out / 16;
+  int np = (fp8 && !gated) ? 2 : 1;
+  while (np > 1 && NB % np) np >>= 1;
+  return np;
 }
 
 }  // namespace
@@ -232,11 +264,17 @@ hipError_t launch_stream(const StreamParams& sp, int groups, hipStream_t st) {
 template <int MB>
 static hipError_t stream_pass(bool fp8, bool gated, const StreamParams& sp, int groups,
                               hipStream_t st) {
-  if (fp8)
-    return gated ? launch_stream<MB, 8, true, true>(sp, groups, st)
-                 : launch_stream<MB, 8, true, false>(sp, groups, st);
-  return gated ? launch_stream<MB, 8, false, true>(sp, groups, st)
-               : launch_stream<MB, 8, false, false>(sp, groups, st);
+  const int np = stream_np(fp8, gated, sp.n_out);
+#define SP_CASE(NP)                                                                 \
+  if (np == NP)                                                                     \
+    return fp8 ? (gated ? launch_stream<MB, NP, true, true>(sp, groups, st)        \
+                        : launch_stream<MB, NP, true, false>(sp, groups, st))      \
+               : (gated ? launch_stream<MB, NP, false, true>(sp, groups, st)       \
+                        : launch_stream<MB, NP, false, false>(sp, groups, st));
+  SP_CASE(2)
+  SP_CASE(1)
+#undef SP_CASE
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_ffn_stream(const FfnArgs& a, int pass, int g0, int g1, int rows_hint,

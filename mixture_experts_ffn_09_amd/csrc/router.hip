@@ -260,47 +260,36 @@ __device__ __forceinline__ bool better(float s1, int i1, float s2, int i2) {
   return s1 > s2 || (s1 == s2 && i1 < i2);
 }
 
+// One wave scores and selects for one token.  Lane l holds the logits of
+// experts l + 64 j (j < NJ) in lg; on return lanes i < k hold the i-th
+// selected expert (best first, the lower index winning ties) and its gate.
 template <int NJ>
-__global__ __launch_bounds__(256) void router_topk_kernel(const float* __restrict__ partial,
-                                                          int S, const float* __restrict__ offset,
-                                                          const float* __restrict__ bias,
-                                                          int sigmoid, int T, int N, int k,
-                                                          int32_t* __restrict__ topk_idx,
-                                                          float* __restrict__ topk_w) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
-  float lg[NJ], sc[NJ];
+__device__ __forceinline__ void select_topk(const float (&lg)[NJ], int N, int k, int sigmoid,
+                                            const float* __restrict__ bias, int lane,
+                                            int& my_idx, float& my_w) {
+  float sc[NJ];
   bool live[NJ];
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
-    int e = lane + 64 * j;
+    const int e = lane + 64 * j;
     live[j] = e < N;
-    float l = 0.f;
-    if (live[j]) {
-#pragma unroll 4
-      for (int sp = 0; sp < S; ++sp) l += partial[((size_t)sp * T + t) * N + e];
-      if (offset) l += offset[e];
-    }
-    lg[j] = l;
-    float s = l;
+    float s = lg[j];
     if (sigmoid) {
-      s = sigmoid_f32(l);
+      s = sigmoid_f32(lg[j]);
       if (bias && live[j]) s += bias[e];
     }
     sc[j] = s;
   }
-  // lane i keeps the i-th selected expert (k <= 64)
   float my_logit = 0.f;
-  int my_idx = 0;
   float sel_logit0 = 0.f;
+  my_idx = 0;
   for (int r = 0; r < k; ++r) {
     float bs = -INFINITY;
     int bi = 0x7fffffff;
     float bl = 0.f;
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
-      int e = lane + 64 * j;
+      const int e = lane + 64 * j;
       if (live[j] && better(sc[j], e, bs, bi)) {
         bs = sc[j];
         bi = e;
@@ -309,9 +298,9 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
     }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) {
-      float os = __shfl_xor(bs, off);
-      int oi = __shfl_xor(bi, off);
-      float ol = __shfl_xor(bl, off);
+      const float os = __shfl_xor(bs, off);
+      const int oi = __shfl_xor(bi, off);
+      const float ol = __shfl_xor(bl, off);
       if (better(os, oi, bs, bi)) {
         bs = os;
         bi = oi;
@@ -328,15 +317,44 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
       my_idx = bi;
     }
   }
-  // gates over the k selected (k <= 64 handled by lanes; k > 64 loops)
+  // gates over the k selected: softmax of their logits, or their unbiased
+  // sigmoid scores divided by the sum
   float v = 0.f;
   if (lane < k) v = sigmoid ? sigmoid_f32(my_logit) : __expf(my_logit - sel_logit0);
   float sum = v;
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
+  my_w = v / sum;
+}
+
+template <int NJ>
+__global__ __launch_bounds__(256) void router_topk_kernel(const float* __restrict__ partial,
+                                                          int S, const float* __restrict__ offset,
+                                                          const float* __restrict__ bias,
+                                                          int sigmoid, int T, int N, int k,
+                                                          int32_t* __restrict__ topk_idx,
+                                                          float* __restrict__ topk_w) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  float lg[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int e = lane + 64 * j;
+    float l = 0.f;
+    if (e < N) {
+#pragma unroll 4
+      for (int sp = 0; sp < S; ++sp) l += partial[((size_t)sp * T + t) * N + e];
+      if (offset) l += offset[e];
+    }
+    lg[j] = l;
+  }
+  int my_idx;
+  float my_w;
+  select_topk<NJ>(lg, N, k, sigmoid, bias, lane, my_idx, my_w);
   if (lane < k) {
     topk_idx[(size_t)t * k + lane] = my_idx;
-    topk_w[(size_t)t * k + lane] = v / sum;
+    topk_w[(size_t)t * k + lane] = my_w;
   }
 }
 

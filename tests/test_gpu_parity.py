@@ -40,6 +40,13 @@ SMALL = {
                                               n_experts=16),
     # FP8 weights through the GEMM path (routed + shared)
     "gemm_fp8": H.small_config(C[4], 110, T=256, d_model=256, d_ff=256, n_experts=8, top_k=4),
+    # decode-sized batches: ragged T, odd N, sigmoid + selection bias + logit
+    # offsets with a shared expert, fp32 x
+    "decode_T5_N6": H.small_config(C[1], 111, T=5, d_model=288, n_experts=6, top_k=3,
+                                   d_ff=96),
+    "decode_sigmoid_T16": H.small_config(C[4], 112, T=16, d_model=128, n_experts=8, top_k=3,
+                                         d_ff=128, w_dtype="bf16"),
+    "decode_f32_N7": H.small_config(C[0], 113, T=11, d_model=96, n_experts=7, top_k=2),
 }
 
 
@@ -117,11 +124,12 @@ def test_layer_full_size_sampled(ci):
     torch.cuda.empty_cache()
 
 
-def test_stages_through_abi_match_layer_forward():
+@pytest.mark.parametrize("name", ["c4_structure_T37", "decode_sigmoid_T16"])
+def test_stages_through_abi_match_layer_forward(name):
     """router -> permute (with x_perm) -> grouped_ffn -> combine, each
     through its own entry point, reproduces moe_layer_forward bit for bit,
     and the permuted gather is exactly x[perm_token]."""
-    cfg = SMALL["c4_structure_T37"]
+    cfg = SMALL[name]
     L, x, xd, out, g = _run_gpu(cfg)
     s = L.shape_for(cfg.T)
     ws = L.workspace()
@@ -146,6 +154,8 @@ def test_stages_through_abi_match_layer_forward():
     moe.moe_expert_gate_up(s, xd, None, rb["perm_token"], rb["offsets"], L.weights, h4, hs4, ws)
     moe.moe_expert_down(s, h4, hs4, rb["offsets"], L.weights, y4, ys4, ws)
     torch.cuda.synchronize()
+    for key, v in g.items():  # routing from the staged calls = from the single call
+        assert np.array_equal(v, rb[key].cpu().numpy()), key
     assert torch.equal(y.view(torch.int16), y4.view(torch.int16))
     assert torch.equal(ys.view(torch.int16), ys4.view(torch.int16))
     assert torch.equal(x_perm, xd[rb["perm_token"].long()])

@@ -8,17 +8,19 @@
 // local": each expert is a full FFN; "Mixture of Experts Explained", "The
 // slot it replaces": three matrices.)
 //
-// Tiling for gfx950: a 512-thread workgroup (8 waves, two per SIMD, so one
-// wave's LDS or barrier wait is covered by the other's MFMAs) computes BM
-// rows x 256 weight rows (pass 1: 128 gate/up pairs) with 2 x 4 waves, each
-// wave (BM/2) x 64 with v_mfma_f32_16x16x32_bf16.  Both operands reach LDS through direct
-// global-to-LDS loads (global_load_lds_dwordx4: each lane's 16 bytes land at
-// lane * 16 of a 1 KB block), so no registers are spent on staging.  Every
-// 1 KB in LDS is one MFMA operand (lane l holds row l % 16, k = 8 * (l / 16)
-// + j): the activation copy picks its global addresses to produce that order
-// and the weights are pre-packed in it, so operand reads are contiguous
-// ds_read_b128.  A ring of up to four stages (32 K each; 64 for FP8) keeps
-// the copies of the next stages in flight while one is multiplied.
+// Two tilings for gfx950, both on v_mfma_f32_16x16x32_bf16:
+//  * 256-row tiles (bf16, many rows per group): 4 waves, one per SIMD, each
+//    128 x 128 with its accumulators in AGPRs (ffn_gemm_big_kernel below).
+//  * 128-row tiles (and FP8 weights): a 512-thread workgroup (8 waves, two
+//    per SIMD, so one wave's LDS or barrier wait is covered by the other's
+//    MFMAs), 2 x 4 waves of 64 x 64.
+// Both operands reach LDS through direct global-to-LDS loads (each lane's 16
+// bytes land at lane * 16 of a 1 KB block), so no registers are spent on
+// staging.  Every 1 KB in LDS is one MFMA operand (lane l holds row l % 16,
+// k = 8 * (l / 16) + j): the activation copy picks its global addresses to
+// produce that order and the weights are pre-packed in it, so operand reads
+// are contiguous ds_read_b128.  A ring of stages (32 K each; 64 for FP8)
+// keeps the copies of the next stages in flight while one is multiplied.
 //
 // Tile order: workgroup ids are spread over the 8 XCDs round-robin, so the
 // linear tile index is remapped to give each XCD a contiguous range, and the
@@ -109,6 +111,20 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// Wait until at most `later` stages of LPS copies each are still in flight
+// (later <= MAXL, a run-time value turned into an immediate).
+template <int LPS, int MAXL>
+__device__ __forceinline__ void wait_stages(int later) {
+  static_assert(MAXL >= 0 && MAXL <= 6, "ring depth");
+  if (MAXL >= 6 && later >= 6) wait_vmcnt<(MAXL >= 6 ? 6 : 0) * LPS>();
+  else if (MAXL >= 5 && later == 5) wait_vmcnt<(MAXL >= 5 ? 5 : 0) * LPS>();
+  else if (MAXL >= 4 && later == 4) wait_vmcnt<(MAXL >= 4 ? 4 : 0) * LPS>();
+  else if (MAXL >= 3 && later == 3) wait_vmcnt<(MAXL >= 3 ? 3 : 0) * LPS>();
+  else if (MAXL >= 2 && later == 2) wait_vmcnt<(MAXL >= 2 ? 2 : 0) * LPS>();
+  else if (MAXL >= 1 && later == 1) wait_vmcnt<LPS>();
+  else wait_vmcnt<0>();
+}
+
 // Workgroup barrier without the release/acquire fences of __syncthreads():
 // those would wait for every outstanding global-to-LDS copy (vmcnt(0)) and
 // drain the ring.  The copies are ordered by explicit wait_vmcnt() instead;
@@ -133,7 +149,10 @@ __global__ __launch_bounds__(512, 1) void ffn_gemm_kernel(GemmParams p) {
   constexpr int A_BYTES = SK * AFR * 1024;
   constexpr int B_FRAGS = WBL * (FP8 ? 1 : SK);
   constexpr int STAGE = A_BYTES + B_FRAGS * 1024;
-  constexpr int NS = (160 * 1024 / STAGE) < 4 ? (160 * 1024 / STAGE) : 4;  // ring depth
+  // ring depth: bf16 keeps three 24 KB stages so that two workgroups share a
+  // CU (their barriers interleave; measured faster than one workgroup with
+  // four to six stages); fp8 keeps up to four 32 KB stages
+  constexpr int NS = FP8 ? ((160 * 1024 / STAGE) < 4 ? (160 * 1024 / STAGE) : 4) : 3;
   constexpr int A_PER_WAVE = SK * AFR / 8;
   constexpr int B_PER_WAVE = B_FRAGS / 8;
   constexpr int LPS = A_PER_WAVE + B_PER_WAVE;  // copies per wave per stage
@@ -258,10 +277,7 @@ __global__ __launch_bounds__(512, 1) void ffn_gemm_kernel(GemmParams p) {
 
   for (int kt = 0; kt < KT; ++kt) {
     // stage kt has landed (this wave's copies): later stages may still fly
-    const int later = min(NS - 2, KT - 1 - kt);
-    if (NS - 2 >= 2 && later >= 2) wait_vmcnt<(NS - 2 >= 2 ? 2 : 0) * LPS>();
-    else if (later == 1) wait_vmcnt<LPS>();
-    else wait_vmcnt<0>();
+    wait_stages<LPS, NS - 2>(min(NS - 2, KT - 1 - kt));
     // everyone's copies of stage kt are visible, and stage kt-1 is no
     // longer read: its buffer takes stage kt+NS-1
     barrier_no_fence();

@@ -41,6 +41,36 @@ __global__ __launch_bounds__(256) void block_hist_kernel(const int32_t* __restri
   for (int e = threadIdx.x; e < N; e += 256) hist[(size_t)blockIdx.x * N + e] = h[e];
 }
 
+// Exclusive scan of v[0..n) in place (n <= 2 * 256), by all 256 threads of
+// the workgroup: each thread sums two neighbours, the waves scan with
+// shuffles, the wave totals are scanned in LDS.  Returns the grand total.
+__device__ int block_exclusive_scan(int32_t* v, int n, int32_t* wtot) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int i0 = 2 * tid;
+  const int a = i0 < n ? v[i0] : 0, b = i0 + 1 < n ? v[i0 + 1] : 0;
+  int incl = a + b;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int up = __shfl_up(incl, o);
+    if (lane >= o) incl += up;
+  }
+  if (lane == 63) wtot[w] = incl;
+  __syncthreads();
+  int before = 0, total = 0;
+#pragma unroll
+  for (int ww = 0; ww < PB_WAVES; ++ww) {
+    const int t = wtot[ww];
+    if (ww < w) before += t;
+    total += t;
+  }
+  const int excl = before + incl - (a + b);
+  __syncthreads();  // every thread has read its inputs and wtot
+  if (i0 < n) v[i0] = excl;
+  if (i0 + 1 < n) v[i0 + 1] = excl + a;
+  __syncthreads();
+  return total;
+}
+
 // hist == nullptr: a single block (T <= 256) counts for itself.
 __global__ __launch_bounds__(256) void permute_kernel(const int32_t* __restrict__ idx, int T,
                                                       int k, int N, int nbits,
@@ -53,6 +83,8 @@ __global__ __launch_bounds__(256) void permute_kernel(const int32_t* __restrict_
   int32_t* wh = sm;                       // [PB_WAVES][N] wave counts, then wave bases
   int32_t* tot = sm + PB_WAVES * N;       // [N] totals, then exclusive offsets
   int32_t* bef = tot + N;                 // [N] counts of earlier blocks
+  int32_t* wtot = bef + N;                // [PB_WAVES] scan scratch
+  int32_t* sid = wtot + PB_WAVES;         // [PB_TOK][k] the block's expert ids
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63;
   const int b = blockIdx.x;
@@ -61,10 +93,17 @@ __global__ __launch_bounds__(256) void permute_kernel(const int32_t* __restrict_
   const uint32_t sentinel = (1u << nbits) - 1u;  // >= N, never a valid id
 
   for (int i = tid; i < PB_WAVES * N; i += 256) wh[i] = 0;
+  // the block's ids, read once (coalesced) and kept in LDS
+  {
+    const int first = b * PB_TOK * k;
+    const int cnt = min(PB_TOK, T - b * PB_TOK) * k;
+    for (int i = tid; i < cnt; i += 256) sid[i] = idx[(size_t)first + i];
+  }
   __syncthreads();
+  int32_t* my = sid + (w * 64 + lane) * k;
   if (tv)
     for (int i = 0; i < k; ++i) {
-      const int e = idx[(size_t)t * k + i];
+      const int e = my[i];
       if (e >= 0 && e < N) atomicAdd(&wh[w * N + e], 1);
     }
   __syncthreads();
@@ -85,20 +124,11 @@ __global__ __launch_bounds__(256) void permute_kernel(const int32_t* __restrict_
     bef[e] = before;
   }
   __syncthreads();
-  // exclusive scan of the totals (thread 0; N <= 512)
-  if (tid == 0) {
-    int run = 0;
-    for (int e = 0; e < N; ++e) {
-      const int v = tot[e];
-      tot[e] = run;
-      run += v;
-    }
-    if (b == 0) offsets[N] = run;
-  }
-  __syncthreads();
+  const int grand = block_exclusive_scan(tot, N, wtot);
+  if (b == 0 && tid == 0) offsets[N] = grand;
   for (int e = tid; e < N; e += 256) {
     if (b == 0) {
-      const int next = (e + 1 < N) ? tot[e + 1] : offsets[N];
+      const int next = (e + 1 < N) ? tot[e + 1] : grand;
       offsets[e] = tot[e];
       counts[e] = next - tot[e];
     }
@@ -114,24 +144,24 @@ __global__ __launch_bounds__(256) void permute_kernel(const int32_t* __restrict_
   // ranks within the wave's 64 tokens
   const uint64_t lt = lanemask_lt();
   for (int i = 0; i < k; ++i) {
-    const int e = tv ? idx[(size_t)t * k + i] : -1;
+    const int e = tv ? my[i] : -1;
     const bool ok = e >= 0 && e < N;
-    const uint32_t my = ok ? (uint32_t)e : sentinel;
+    const uint32_t mine = ok ? (uint32_t)e : sentinel;
     int rank = 0;
     for (int i2 = 0; i2 < k; ++i2) {
-      const int e2 = tv ? idx[(size_t)t * k + i2] : -1;
+      const int e2 = tv ? my[i2] : -1;
       const uint32_t other = (e2 >= 0 && e2 < N) ? (uint32_t)e2 : sentinel;
       uint64_t m = ~0ull;
       for (int bit = 0; bit < nbits; ++bit) {
         const uint64_t bal = __ballot((other >> bit) & 1u);
-        m &= ((my >> bit) & 1u) ? bal : ~bal;
+        m &= ((mine >> bit) & 1u) ? bal : ~bal;
       }
       rank += __popcll(m & lt);
       // the same token listing the expert in an earlier slot comes first
-      if (i2 < i && other == my && ok) ++rank;
+      if (i2 < i && other == mine && ok) ++rank;
     }
     if (ok) {
-      const int pos = wh[w * N + (int)my] + rank;
+      const int pos = wh[w * N + (int)mine] + rank;
       perm_token[pos] = t;
       inv_perm[(size_t)t * k + i] = pos;
     } else if (tv) {
@@ -173,7 +203,7 @@ hipError_t launch_permute(const int32_t* topk_idx, int T, int k, int N, int32_t*
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const size_t lds = (size_t)(PB_WAVES + 2) * N * sizeof(int32_t);
+  const size_t lds = ((size_t)(PB_WAVES + 2) * N + PB_WAVES + (size_t)PB_TOK * k) * sizeof(int32_t);
   permute_kernel<<<nblk, 256, lds, st>>>(topk_idx, T, k, N, nbits, nblk > 1 ? hist : nullptr,
                                          nblk, counts, offsets, perm_token, inv_perm);
   return hipGetLastError();

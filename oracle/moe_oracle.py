@@ -53,6 +53,7 @@ __all__ = [
     "expert_counts", "expert_offsets", "Permutation", "permute_assignments",
     "gather_rows", "silu", "swiglu_expert", "combine",
     "moe_forward", "moe_forward_with_routing", "expected_experts_touched",
+    "router_probabilities", "load_statistics", "bias_controller_step",
     "PARITY_PINS",
 ]
 
@@ -75,6 +76,13 @@ PARITY_PINS = {
         "SwiGLU (torch fp64 library) at k=N and k<N; pure-Python brute "
         "force; [AIS-12] combine arithmetic; token independence",
     "expected_experts_touched": "[MoE-EXP] batching table, [AIS-12] 3/64/98%",
+    "router_probabilities": "rows sum to 1; softmax mode vs torch.softmax "
+        "(library); sigmoid mode reduces to softmax of log-sigmoid; top-1 of "
+        "the probabilities equals the selection in softmax mode",
+    "load_statistics": "closed forms: L_aux = alpha when P (or f) is uniform, "
+        "alpha*N at full collapse; sum f = sum P = 1; pure-Python brute force",
+    "bias_controller_step": "[AIS-12] +-0.001 rule on hand-built counts "
+        "(over, under, exactly at the mean); float32 exactness",
 }
 
 
@@ -405,3 +413,64 @@ def expected_experts_touched(n_experts: int, k: int, batch: int) -> float:
     wake: N * (1 - (1 - k/N)^B) ([AIS-12] "What happens when many users share
     the GPU?"; [MoE-EXP] "Why batching erodes the advantage")."""
     return n_experts * (1.0 - (1.0 - k / n_experts) ** batch)
+
+
+# ---------------------------------------------------------------------------
+# Load statistics and the selection-bias controller
+# ---------------------------------------------------------------------------
+
+def router_probabilities(logits: np.ndarray, route: str) -> np.ndarray:
+    """Each token's routing probability over all N experts, [T][N].
+
+    Softmax mode: the softmax of the N logits, the distribution the Switch
+    balancing term averages ([CH19] 19.3.3: P_i is the batch's average routing
+    probability of expert i).  Sigmoid mode (reading: the pages define no
+    probability for it): the affinities sigmoid(s) divided by their sum over
+    all N experts.  The selection bias never enters ([CH19] 19.3.4)."""
+    s = np.asarray(logits, dtype=np.float64)
+    if route == "softmax":
+        z = np.exp(s - s.max(axis=1, keepdims=True))
+    elif route == "sigmoid":
+        z = sigmoid(s)
+    else:
+        raise ValueError(route)
+    return z / z.sum(axis=1, keepdims=True)
+
+
+def load_statistics(counts: np.ndarray, probs: np.ndarray, k: int,
+                    alpha: float = 0.01):
+    """Assignment shares f, mean probabilities P and the Switch balancing term
+    L_aux = alpha * N * sum_i f_i P_i ([CH19] 19.3.3; weight 0.01 as Switch
+    set it, [MoE-LLM] "Classic fix: auxiliary loss").
+
+    f_i is expert i's share of the batch's T*k assignments (for top-1, the
+    fraction of tokens routed to i, as the pages define it).  Returns
+    (f [N], P [N], L_aux)."""
+    counts = np.asarray(counts, dtype=np.float64)
+    p = np.asarray(probs, dtype=np.float64)
+    T, N = p.shape
+    f = counts / (T * k)
+    P = p.mean(axis=0)
+    return f, P, alpha * N * float(np.dot(f, P))
+
+
+def bias_controller_step(bias: np.ndarray, counts: np.ndarray, k: int,
+                         step: float = 1e-3) -> np.ndarray:
+    """One step of the selection-bias controller ([MoE-LLM] "DeepSeek-style
+    bias controller"; [AIS-12] "How are experts kept evenly busy?": after a
+    batch, an overloaded expert's bias drops by 0.001 and an underloaded
+    one's rises by 0.001; [CH19] 19.3.4).
+
+    Load is compared with the mean T*k/N in exact integer arithmetic
+    (c_i * N against T*k); an expert exactly at the mean keeps its bias
+    (reading: the pages name only the two other cases).  The bias is a float32
+    parameter and the step is added in float32.  The result is the bias the
+    next batch selects with: the controller reads only past batches."""
+    c = np.asarray(counts, dtype=np.int64)
+    N = c.shape[0]
+    total = int(c.sum())
+    if total % k:
+        raise ValueError("counts must sum to T*k")
+    sign = np.sign(total - c * N).astype(np.float32)  # +1 under-, -1 overloaded
+    b = np.asarray(bias, dtype=np.float32)
+    return (b + np.float32(step) * sign).astype(np.float32)

@@ -92,3 +92,18 @@ def moe_layer(x, w_router, experts, k, route="softmax", bias=None, shared=None,
             acc = [a + v for a, v in zip(acc, ys)]
         out.append(acc)
     return out
+
+
+def load_stats(logits, counts, k, alpha):
+    """f_i = count_i / (T k), P_i = mean over tokens of softmax(logits_t)_i,
+    aux = alpha * N * sum_i f_i P_i, by explicit loops."""
+    T, N = len(logits), len(logits[0])
+    P = [0.0] * N
+    for t in range(T):
+        m = max(logits[t])
+        z = [math.exp(v - m) for v in logits[t]]
+        tot = math.fsum(z)
+        for i in range(N):
+            P[i] += z[i] / tot / T
+    f = [counts[i] / (T * k) for i in range(N)]
+    return f, P, alpha * N * math.fsum(f[i] * P[i] for i in range(N))

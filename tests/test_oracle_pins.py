@@ -359,6 +359,92 @@ def pin_touched_statistics(seed=10):
         assert abs(vals.mean() - mu) <= 4 * vals.std() / math.sqrt(trials) + 1e-9
 
 
+
+# ---------------------------------------------------------------------------
+# load statistics and the selection-bias controller
+# ---------------------------------------------------------------------------
+
+def pin_router_probabilities():
+    """Softmax mode is the library softmax; sigmoid mode equals the softmax
+    of log-sigmoid (a different route to sigmoid / sum); rows sum to 1; the
+    most probable expert is the softmax-mode top-1."""
+    rng = np.random.default_rng(21)
+    s = rng.normal(0, 2, (37, 11))
+    p = O.router_probabilities(s, "softmax")
+    ref = torch.softmax(torch.tensor(s, dtype=torch.float64), dim=1).numpy()
+    assert np.allclose(p, ref, rtol=1e-13, atol=1e-15)
+    q = O.router_probabilities(s, "sigmoid")
+    refq = torch.softmax(torch.nn.functional.logsigmoid(torch.tensor(s, dtype=torch.float64)), dim=1).numpy()
+    assert np.allclose(q, refq, rtol=1e-12, atol=1e-15)
+    assert np.allclose(q.sum(axis=1), 1.0) and np.allclose(p.sum(axis=1), 1.0)
+    top1 = O.top_k_select(O.selection_scores(s, "softmax"), 1)[:, 0]
+    assert np.array_equal(np.argmax(p, axis=1), top1)
+
+
+def pin_load_statistics_closed_forms():
+    """[CH19] 19.3.3: L_aux = alpha * N * sum f_i P_i.  With P uniform the
+    sum is 1/N whatever f is, so L_aux = alpha; likewise with f uniform; when
+    every token goes to one expert with probability -> 1, L_aux -> alpha * N."""
+    rng = np.random.default_rng(22)
+    T, N, k, alpha = 40, 8, 2, 0.01
+    counts = rng.multinomial(T * k, rng.dirichlet(np.ones(N)))
+    flat = O.router_probabilities(np.zeros((T, N)), "softmax")
+    f, P, aux = O.load_statistics(counts, flat, k, alpha)
+    assert abs(aux - alpha) < 1e-15 and abs(f.sum() - 1) < 1e-15 and abs(P.sum() - 1) < 1e-12
+    probs = O.router_probabilities(rng.normal(0, 1, (T, N)), "softmax")
+    _, _, aux2 = O.load_statistics(np.full(N, T * k // N), probs, k, alpha)
+    assert abs(aux2 - alpha) < 1e-14
+    s = np.full((T, N), -60.0)
+    s[:, 0] = 60.0
+    one = np.zeros(N, dtype=np.int64)
+    one[0] = T
+    _, P3, aux3 = O.load_statistics(one, O.router_probabilities(s, "softmax"), 1, alpha)
+    assert abs(aux3 - alpha * N) < 1e-12 and abs(P3[0] - 1) < 1e-12
+
+
+def pin_load_statistics_brute():
+    rng = np.random.default_rng(23)
+    T, N, k, alpha = 6, 5, 2, 0.01
+    s = rng.normal(0, 1, (T, N))
+    counts = [2, 0, 5, 3, 2]
+    f, P, aux = O.load_statistics(counts, O.router_probabilities(s, "softmax"), k, alpha)
+    bf, bP, baux = B.load_stats(s.tolist(), counts, k, alpha)
+    assert np.allclose(f, bf, rtol=0, atol=1e-15) and np.allclose(P, bP, rtol=1e-13)
+    assert abs(aux - baux) < 1e-14
+
+
+def pin_bias_controller_rule():
+    """[AIS-12] "How are experts kept evenly busy?": overloaded experts' biases
+    drop by 0.001, underloaded ones rise by 0.001; exactly at the mean the
+    bias stays.  Mean 2 (T*k = 8 over N = 4) and mean 2.5 (10 over 4)."""
+    d = np.float32(0.001)
+    b = O.bias_controller_step(np.zeros(4, np.float32), [5, 1, 2, 0], 2)
+    assert b.dtype == np.float32 and np.array_equal(b, np.array([-d, d, 0, d], np.float32))
+    b0 = np.array([0.5, -0.25, 0.1, 0.0], np.float32)
+    b = O.bias_controller_step(b0, [3, 2, 3, 2], 1)
+    want = np.array([b0[0] - d, b0[1] + d, b0[2] - d, b0[3] + d], dtype=np.float32)
+    assert np.array_equal(b, want)
+
+
+def pin_bias_controller_balances():
+    """[MoE-LLM] "DeepSeek-style bias controller": applied batch after batch,
+    the biases settle where traffic spreads evenly.  A skewed sigmoid router
+    (per-expert logit offsets) routes fresh random batches; the controller
+    (step 0.01 to converge quickly) lowers the max/mean load."""
+    rng = np.random.default_rng(24)
+    N, d, k, T = 16, 8, 2, 256
+    w = rng.normal(0, 1 / math.sqrt(d), (d, N))
+    off = -1.0 * np.log(np.arange(1, N + 1))
+    bias = np.zeros(N, np.float32)
+    imb = []
+    for it in range(60):
+        x = rng.normal(0, 1, (T, d))
+        r = O.route_tokens(x, w, k, "sigmoid", off, bias.astype(np.float64))
+        c = O.expert_counts(r.idx, N)
+        imb.append(c.max() / c.mean())
+        bias = O.bias_controller_step(bias, c, k, step=0.01)
+    assert np.mean(imb[-10:]) < 0.6 * np.mean(imb[:3]), imb
+
 ALL_PINS = [
     pin_router_worked_example_skillsuites, pin_router_worked_example_ai_infra,
     pin_softmax_placement_equivalence, pin_brute_force_routing,
@@ -366,7 +452,8 @@ ALL_PINS = [
     pin_permutation, pin_layer_brute_force, pin_identical_experts_equal_dense,
     pin_distinct_experts_k_equals_n, pin_token_independence_and_relabel,
     pin_bf16_decoder, pin_e4m3_decoder, pin_fp8_block_dequant,
-    pin_experts_touched,
+    pin_experts_touched, pin_router_probabilities, pin_load_statistics_closed_forms,
+    pin_load_statistics_brute, pin_bias_controller_rule, pin_bias_controller_balances,
 ]
 
 
@@ -450,6 +537,30 @@ def _m_logits_no_offset(x, w, off=None):
     return _orig_logits(x, w, None)
 
 
+def _m_aux_without_n(counts, probs, k, alpha=0.01):
+    f, P, aux = _orig_load_stats(counts, probs, k, alpha)
+    return f, P, aux / len(f)
+
+
+def _m_probs_before_normalise(logits, route):
+    s = np.asarray(logits, dtype=np.float64)
+    return np.exp(s - s.max(axis=1, keepdims=True)) if route == "softmax" else O.sigmoid(s)
+
+
+def _m_bias_sign_flipped(bias, counts, k, step=1e-3):
+    return _orig_bias_step(bias, counts, k, -step)
+
+
+def _m_bias_moves_at_mean(bias, counts, k, step=1e-3):
+    c = np.asarray(counts)
+    sign = np.where(c * len(c) > c.sum(), -1.0, 1.0).astype(np.float32)
+    return (np.asarray(bias, np.float32) + np.float32(step) * sign).astype(np.float32)
+
+
+_orig_load_stats = O.load_statistics
+_orig_bias_step = O.bias_controller_step
+
+
 _orig_perm = O.permute_assignments
 _orig_bf16 = O.bf16_bits_to_f64
 _orig_e4m3 = O.e4m3_bits_to_f64
@@ -470,6 +581,10 @@ MUTATIONS = {
     "e4m3_decoder_wrong_bias": ("e4m3_bits_to_f64", lambda: _m_e4m3_bias8),
     "experts_touched_linear": ("expected_experts_touched", lambda: _m_touched_linear),
     "router_drops_offset": ("router_logits", lambda: _m_logits_no_offset),
+    "aux_loss_without_n": ("load_statistics", lambda: _m_aux_without_n),
+    "probabilities_not_normalised": ("router_probabilities", lambda: _m_probs_before_normalise),
+    "bias_controller_sign_flipped": ("bias_controller_step", lambda: _m_bias_sign_flipped),
+    "bias_controller_moves_at_mean": ("bias_controller_step", lambda: _m_bias_moves_at_mean),
 }
 
 

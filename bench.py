@@ -226,6 +226,25 @@ def main():
     stage_ms = {name: sum(ev[j].elapsed_time(ev[j + 1]) for ev in events) / a.steps
                 for j, name in enumerate(STAGES)}
 
+    # Next-row kernels, timed on the same stream: load statistics of this
+    # batch plus one selection-bias step (on a scratch copy of the bias)
+    N_ = cfg.n_experts
+    st_out = [torch.empty(N_, device="cuda"), torch.empty(N_, device="cuda"),
+              torch.empty(1, device="cuda")]
+    bias_scratch = (L.tensors["select_bias"].clone() if cfg.route == "sigmoid" else None)
+    for _ in range(2):
+        moe.moe_load_stats(s, x, L.weights, rb["counts"], ws, 0.01, 1e-3, *st_out, bias_scratch)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(a.steps):
+        moe.moe_load_stats(s, x, L.weights, rb["counts"], ws, 0.01, 1e-3, *st_out, bias_scratch)
+    e1.record()
+    torch.cuda.synchronize()
+    ls_ms = e0.elapsed_time(e1) / a.steps
+    ls_bytes = T * d * (2 if adt == torch.bfloat16 else 4) + d * N_ * 4 + 4 * N_ * 4
+    ls_gbs = ls_bytes / (ls_ms * 1e-3) / 1e9
+
     counts = rb["counts"].cpu()
     touched = int((counts > 0).sum())
     st, layer = accounting(cfg, touched)
@@ -258,6 +277,10 @@ def main():
                   "TFLOPs": round(layer_tflops, 2),
                   "staged_ms_per_step": round(staged_ms, 4)},
         "stages": stages,
+        "next_rows": {"load_stats": {
+            "ms": round(ls_ms, 4), "bytes": ls_bytes, "bound": "hbm",
+            "achieved": round(ls_gbs, 1), "unit": "GB/s", "frac": round(ls_gbs / PEAK_HBM_GBS, 4),
+            "what": "moe_load_stats: router probabilities, shares, balancing term, bias step"}},
     }
     if not a.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)

@@ -130,7 +130,8 @@ moe_status_t moe_pack_weights(const moe_shape_t* s, int which, int n_mats,
  * it.  Returns (size_t)-1 on a bad shape.  Layout (256-byte aligned pieces):
  * router partial logits [S][T][N] f32 (S >= 1 K-splits), topk idx/w,
  * counts, offsets, perm_token, inv_perm, per-256-token-block expert counts
- * [ceil(T/256)][N] int32, an 8 KB tile schedule, H [T*k][d_ff]
+ * [ceil(T/256)][N] int32, per-16-token-block probability sums
+ * [ceil(T/16)][N] f32, an 8 KB tile schedule, H [T*k][d_ff]
  * and H_shared [T][d_ff], Y [T*k][d] and Y_shared [T][d] (H, Y in the
  * activation type).  moe_expert_gate_up / moe_expert_down use only the
  * schedule piece but check ws_bytes against the full size. */
@@ -193,6 +194,30 @@ moe_status_t moe_expert_down(const moe_shape_t* s, const void* h,
 moe_status_t moe_combine(const moe_shape_t* s, const void* y_perm,
                          const void* y_shared, const int32_t* inv_perm,
                          const float* topk_w, void* out, hipStream_t stream);
+
+/* Load statistics of one routed batch and one step of the selection-bias
+ * controller ([CH19] 19.3.3 "Why probability variance alone cannot describe
+ * load balancing", 19.3.4; [MoE-LLM] "Classic fix: auxiliary loss",
+ * "DeepSeek-style bias controller"; [AIS-12] "How are experts kept evenly
+ * busy?").  x: the batch [T][d] act_dtype whose routing produced counts [N]
+ * (int32, as written by moe_permute).  The router logits are recomputed
+ * from x (w->w_router, w->logit_offset); a token's routing probability p is
+ * the softmax of its N logits, or in sigmoid mode sigmoid(s) divided by its
+ * sum over all N (the selection bias never enters).  Outputs, each NULL to
+ * skip (device float32):
+ *   frac[N] = counts[i] / (T*k)                    share f_i
+ *   prob[N] = (1/T) * sum_t p[t][i]                 mean probability P_i
+ *   aux[1]  = alpha * N * sum_i frac[i] * prob[i]   (Switch used alpha 0.01)
+ *   bias[N] += step * sign(T*k - N*counts[i])       in place, float32: +step
+ *             below the mean load T*k/N, -step above it, unchanged at it
+ *             (the pages' step is 0.001); sigmoid router only, else
+ *             MOE_ERR_INVALID_ARG.  The result is the bias for the NEXT
+ *             batch; it may be the buffer w->select_bias points to.
+ * Sums run in a fixed order (bit-reproducible).  ws: moe_workspace_bytes(s). */
+moe_status_t moe_load_stats(const moe_shape_t* s, const void* x, const moe_weights_t* w,
+                            const int32_t* counts, float alpha, float step, float* frac,
+                            float* prob, float* aux, float* bias, void* ws, size_t ws_bytes,
+                            hipStream_t stream);
 
 /* The whole layer forward: router, permute, grouped FFN, combine.  x and
  * out: [T][d] act_dtype (must not overlap).  routing_out may be NULL, and

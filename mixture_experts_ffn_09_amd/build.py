@@ -20,7 +20,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libmoe_ffn.so")
 SOURCES = ["abi.cpp", "router.hip", "permute.hip", "ffn_stream.hip", "ffn_gemm.hip",
-           "ffn_f32.hip", "combine.hip", "pack.hip"]
+           "ffn_f32.hip", "combine.hip", "pack.hip", "stats.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

@@ -75,7 +75,7 @@ moe_status_t check_shape(const moe_shape_t* s) {
 }
 
 struct WsLayout {
-  size_t logits, idx, w, counts, offsets, perm, inv, hist, sched, H, H_sh, Y, Y_sh, total;
+  size_t logits, idx, w, counts, offsets, perm, inv, hist, stats, sched, H, H_sh, Y, Y_sh, total;
 };
 
 WsLayout ws_layout(const moe_shape_t* s) {
@@ -97,6 +97,7 @@ WsLayout ws_layout(const moe_shape_t* s) {
   L.perm = take(T * k * 4);
   L.inv = take(T * k * 4);
   L.hist = take((size_t)permute_blocks(s->n_tokens) * N * 4);
+  L.stats = take((size_t)stats_blocks(s->n_tokens) * N * 4);
   L.sched = take(2048 * 4);
   L.H = take(T * k * f * es);
   L.H_sh = take(sh * T * f * es);
@@ -354,6 +355,35 @@ moe_status_t moe_combine(const moe_shape_t* s, const void* y_perm, const void* y
   HIP_TRY("combine", launch_combine(y_perm, s->n_shared ? y_shared : nullptr, inv_perm, topk_w,
                                     out, s->n_tokens, s->top_k, s->d_model,
                                     s->act_dtype == MOE_BF16, stream));
+  return MOE_OK;
+}
+
+moe_status_t moe_load_stats(const moe_shape_t* s, const void* x, const moe_weights_t* w,
+                            const int32_t* counts, float alpha, float step, float* frac,
+                            float* prob, float* aux, float* bias, void* ws, size_t ws_bytes,
+                            hipStream_t stream) {
+  moe_status_t st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (s->n_tokens == 0) return MOE_OK;
+  if ((st = check_weights(s, w, true, false)) != MOE_OK) return st;
+  if (!x || !counts) return fail(MOE_ERR_INVALID_ARG, "x / counts is NULL");
+  if (!(alpha == alpha) || !(step == step)) return fail(MOE_ERR_INVALID_ARG, "alpha / step is NaN");
+  if (bias && s->route != MOE_ROUTE_SIGMOID_BIAS)
+    return fail(MOE_ERR_INVALID_ARG, "the selection bias belongs to the sigmoid router");
+  if ((st = check_ws(s, ws, ws_bytes)) != MOE_OK) return st;
+  const WsLayout L = ws_layout(s);
+  char* b = static_cast<char*>(ws);
+  float* logits = reinterpret_cast<float*>(b + L.logits);
+  HIP_TRY("router_logits", launch_router_logits(x, s->act_dtype == MOE_BF16, w->w_router, logits,
+                                                s->n_tokens, s->d_model, s->n_experts, stream));
+  HIP_TRY("load_stats",
+          launch_load_stats(logits,
+                            router_splits(s->n_tokens, s->n_experts, s->d_model,
+                                          s->act_dtype == MOE_BF16),
+                            w->logit_offset, s->route == MOE_ROUTE_SIGMOID_BIAS, s->n_tokens,
+                            s->n_experts, s->top_k, counts, alpha, step,
+                            reinterpret_cast<float*>(b + L.stats), frac, prob, aux, bias,
+                            stream));
   return MOE_OK;
 }
 

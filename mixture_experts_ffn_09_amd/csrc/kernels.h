@@ -13,6 +13,13 @@ hipError_t launch_router_logits(const void* x, bool act_bf16, const float* w_rou
 
 // Sums the S partials (+ offset[N]), selects the top k and writes the gates
 // (one wave per token).
+// per-16-token-block probability sums [stats_blocks(T)][N], then P, f, the
+// balancing term and the bias step
+int stats_blocks(int T);
+hipError_t launch_load_stats(const float* partial, int S, const float* offset, int sigmoid, int T,
+                             int N, int k, const int32_t* counts, float alpha, float step,
+                             float* bp, float* frac, float* prob, float* aux, float* bias,
+                             hipStream_t st);
 hipError_t launch_router_topk(const float* partial, int S, const float* offset,
                               const float* select_bias, int sigmoid, int T, int N, int k,
                               int32_t* topk_idx, float* topk_w, hipStream_t st);

@@ -26,8 +26,8 @@ ROUTE_CODES = {"softmax": MOE_ROUTE_SOFTMAX_TOPK, "sigmoid": MOE_ROUTE_SIGMOID_B
 
 EXPORTS = ["moe_packed_weight_bytes", "moe_pack_weights", "moe_workspace_bytes",
            "moe_router_topk", "moe_permute", "moe_grouped_ffn", "moe_expert_gate_up",
-           "moe_expert_down", "moe_combine", "moe_layer_forward", "moe_status_string",
-           "moe_last_error"]
+           "moe_expert_down", "moe_combine", "moe_layer_forward", "moe_load_stats",
+           "moe_status_string", "moe_last_error"]
 
 
 class MoEError(RuntimeError):
@@ -78,8 +78,11 @@ def lib() -> C.CDLL:
         L.moe_combine.argtypes = [S, P, P, P, P, P, P]
         L.moe_layer_forward.argtypes = [S, C.POINTER(Weights), P, P, C.POINTER(Routing), P,
                                         C.c_size_t, P]
+        L.moe_load_stats.argtypes = [S, P, C.POINTER(Weights), P, C.c_float, C.c_float, P, P, P, P,
+                                     P, C.c_size_t, P]
         for f in ("moe_pack_weights", "moe_router_topk", "moe_permute", "moe_grouped_ffn",
-                  "moe_expert_gate_up", "moe_expert_down", "moe_combine", "moe_layer_forward"):
+                  "moe_expert_gate_up", "moe_expert_down", "moe_combine", "moe_layer_forward",
+                  "moe_load_stats"):
             getattr(L, f).restype = C.c_int
         L.moe_status_string.argtypes = [C.c_int]
         L.moe_status_string.restype = C.c_char_p
@@ -201,3 +204,13 @@ def moe_layer_forward(shape: Shape, weights: Weights, x: torch.Tensor, out: torc
     _check(lib().moe_layer_forward(C.byref(shape), C.byref(weights), _ptr(x), _ptr(out),
                                    C.byref(routing) if routing is not None else None, _ptr(ws),
                                    ws.numel() * ws.element_size(), _stream()))
+
+
+def moe_load_stats(shape: Shape, x: torch.Tensor, weights: Weights, counts: torch.Tensor,
+                   ws: torch.Tensor, alpha: float = 0.01, step: float = 1e-3,
+                   frac: Optional[torch.Tensor] = None, prob: Optional[torch.Tensor] = None,
+                   aux: Optional[torch.Tensor] = None, bias: Optional[torch.Tensor] = None):
+    _check(lib().moe_load_stats(C.byref(shape), _ptr(x), C.byref(weights), _ptr(counts),
+                                C.c_float(alpha), C.c_float(step), _ptr(frac), _ptr(prob),
+                                _ptr(aux), _ptr(bias), _ptr(ws), ws.numel() * ws.element_size(),
+                                _stream()))

@@ -156,7 +156,8 @@ def test_workspace_size_formula(T, N, k, d, f, sh):
     a = lambda v: (v + 255) // 256 * 256
     S = _router_splits(T, N, d)
     want = (a(S * T * N * 4) + 2 * a(T * k * 4) + a(N * 4) + a((N + 1) * 4) + 2 * a(T * k * 4)
-            + a(-(-T // 256) * N * 4) + a(2048 * 4) + a(T * k * f * 2) + a(sh * T * f * 2) + a(T * k * d * 2)
+            + a(-(-T // 256) * N * 4) + a(-(-T // 16) * N * 4) + a(2048 * 4) + a(T * k * f * 2)
+            + a(sh * T * f * 2) + a(T * k * d * 2)
             + a(sh * T * d * 2))
     assert moe.moe_workspace_bytes(s) == want
 
@@ -184,3 +185,30 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(moe, "LIB_PATH", str(tmp_path / "nope.so"))
     with pytest.raises(RuntimeError, match="not built"):
         moe.lib()
+
+
+def test_load_stats_argument_checks():
+    s = shape()
+    w = moe.Weights(w_router=FAKE.value)
+    ws = C.c_size_t(moe.moe_workspace_bytes(s))
+    f = C.c_float
+    call = lambda *a: _status("moe_load_stats", *a)
+    # x or counts missing
+    assert call(C.byref(s), None, C.byref(w), FAKE, f(0.01), f(1e-3), None, None, None, None,
+                FAKE, ws, None) == moe.MOE_ERR_INVALID_ARG
+    assert call(C.byref(s), FAKE, C.byref(w), None, f(0.01), f(1e-3), None, None, None, None,
+                FAKE, ws, None) == moe.MOE_ERR_INVALID_ARG
+    # the bias belongs to the sigmoid router
+    assert call(C.byref(s), FAKE, C.byref(w), FAKE, f(0.01), f(1e-3), None, None, None, FAKE,
+                FAKE, ws, None) == moe.MOE_ERR_INVALID_ARG
+    # NaN step, small workspace, no router weight
+    assert call(C.byref(s), FAKE, C.byref(w), FAKE, f(0.01), f(float("nan")), None, None, None,
+                None, FAKE, ws, None) == moe.MOE_ERR_INVALID_ARG
+    assert call(C.byref(s), FAKE, C.byref(w), FAKE, f(0.01), f(1e-3), None, None, None, None,
+                FAKE, C.c_size_t(ws.value - 1), None) == moe.MOE_ERR_WORKSPACE_TOO_SMALL
+    assert call(C.byref(s), FAKE, C.byref(moe.Weights()), FAKE, f(0.01), f(1e-3), None, None, None,
+                None, FAKE, ws, None) == moe.MOE_ERR_INVALID_ARG
+    # zero tokens: a no-op that touches nothing
+    s0 = shape(T=0)
+    assert call(C.byref(s0), None, None, None, f(0.01), f(1e-3), None, None, None, None, None,
+                C.c_size_t(0), None) == moe.MOE_OK

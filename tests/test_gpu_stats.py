@@ -1,0 +1,137 @@
+"""Load statistics and the selection-bias controller on the GPU against the
+oracle: shares f, mean routing probabilities P, the balancing term and one
+bias step (moe_load_stats)."""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.moe_oracle as O
+from mixture_experts_ffn_09_amd import moe, workloads as W
+from tests import _harness as H
+
+pytestmark = pytest.mark.gpu
+
+C = W.CONFIGS
+CASES = {
+    "c1_tiny_f32": C[0],
+    "c2_mixtral_decode": C[1],
+    "c4_structure_T37": H.small_config(C[3], 102, T=37, d_model=256, d_ff=128),
+    "c5_structure_T300_offsets": H.small_config(C[4], 120, T=300, d_model=256, d_ff=256),
+    "c4_full_T4096": C[3],
+}
+ALPHA, STEP = 0.01, 1e-3
+
+
+def _log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+class RouterOnly:
+    """The router's device tensors and a workspace; no expert weights."""
+
+    def __init__(self, cfg):
+        self.cfg = cfg
+        r = W.make_router(cfg)
+        self.t = {k: v.to("cuda") for k, v in r.items() if v is not None}
+        self.shape = moe.make_shape(cfg.T, cfg.d_model, cfg.n_experts, cfg.top_k, cfg.d_ff,
+                                    cfg.n_shared, cfg.route, cfg.act_dtype, cfg.w_dtype)
+        self.weights = moe.make_weights(**self.t)
+        self.ws = torch.empty(moe.moe_workspace_bytes(self.shape), dtype=torch.uint8,
+                              device="cuda")
+
+    def route(self, x):
+        cfg = self.cfg
+        T, k, N = cfg.T, cfg.top_k, cfg.n_experts
+        rb = {"topk_idx": torch.empty(T, k, dtype=torch.int32, device="cuda"),
+              "topk_w": torch.empty(T, k, dtype=torch.float32, device="cuda"),
+              "counts": torch.empty(N, dtype=torch.int32, device="cuda"),
+              "offsets": torch.empty(N + 1, dtype=torch.int32, device="cuda"),
+              "perm_token": torch.empty(T * k, dtype=torch.int32, device="cuda"),
+              "inv_perm": torch.empty(T * k, dtype=torch.int32, device="cuda")}
+        moe.moe_router_topk(self.shape, x, self.weights, rb["topk_idx"], rb["topk_w"], self.ws)
+        moe.moe_permute(self.shape, rb["topk_idx"], None, moe.make_routing(**rb), self.ws)
+        return rb
+
+    def stats(self, x, counts, bias=None):
+        N = self.cfg.n_experts
+        out = {"frac": torch.full((N,), float("nan"), device="cuda"),
+               "prob": torch.full((N,), float("nan"), device="cuda"),
+               "aux": torch.full((1,), float("nan"), device="cuda")}
+        moe.moe_load_stats(self.shape, x, self.weights, counts, self.ws, ALPHA, STEP,
+                           out["frac"], out["prob"], out["aux"], bias)
+        return out
+
+
+def _oracle_probs(cfg, x_cpu):
+    w_r, off, _ = H.oracle_router(cfg)
+    logits = O.router_logits(H.x_f64(cfg, x_cpu), w_r, off)
+    return O.router_probabilities(logits, cfg.route)
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_load_stats_match_oracle(name):
+    cfg = CASES[name]
+    _log(f"[case] load stats {name} T={cfg.T} d={cfg.d_model} N={cfg.n_experts} k={cfg.top_k}")
+    R = RouterOnly(cfg)
+    x_cpu = W.make_x(cfg)
+    x = x_cpu.to("cuda")
+    rb = R.route(x)
+    bias = R.t["select_bias"].clone() if cfg.route == "sigmoid" else None
+    b0 = bias.cpu().numpy() if bias is not None else None
+    got = R.stats(x, rb["counts"], bias)
+    torch.cuda.synchronize()
+    counts = rb["counts"].cpu().numpy()
+    f, P, aux = O.load_statistics(counts, _oracle_probs(cfg, x_cpu), cfg.top_k, ALPHA)
+    gf, gP, gaux = (got[k].cpu().numpy().astype(np.float64) for k in ("frac", "prob", "aux"))
+    assert np.all(np.abs(gf - f) <= 1.2e-7 * f), "frac"
+    assert np.all(np.abs(gP - P) <= 2e-5 * P + 1e-9), f"prob max rel {np.max(np.abs(gP - P) / P):.2e}"
+    assert abs(gaux[0] - aux) <= 2e-5 * aux, (gaux[0], aux)
+    if bias is not None:
+        want = O.bias_controller_step(b0, counts, cfg.top_k, STEP)
+        assert np.array_equal(bias.cpu().numpy(), want), "bias step"
+    _log(f"  ok: aux {gaux[0]:.6g} vs {aux:.6g}")
+
+
+def test_bias_step_feeds_the_next_batch():
+    """Batch A routes with b0; moe_load_stats updates the bias buffer in place
+    to b1; batch B, routed through the same weights struct, selects with b1
+    (the controller reads only past batches)."""
+    cfg = CASES["c5_structure_T300_offsets"]
+    R = RouterOnly(cfg)
+    xa = W.make_x(cfg)
+    cfg_b = H.small_config(cfg, 121)
+    xb = W.make_x(cfg_b)
+    rb = R.route(xa.to("cuda"))
+    b0 = R.t["select_bias"].cpu().numpy()
+    R.stats(xa.to("cuda"), rb["counts"], R.t["select_bias"])
+    torch.cuda.synchronize()
+    b1 = O.bias_controller_step(b0, rb["counts"].cpu().numpy(), cfg.top_k, STEP)
+    assert np.array_equal(R.t["select_bias"].cpu().numpy(), b1)
+    rb2 = R.route(xb.to("cuda"))
+    torch.cuda.synchronize()
+    w_r, off, _ = H.oracle_router(cfg)
+    Rb = O.route_tokens(H.x_f64(cfg_b, xb), w_r, cfg.top_k, cfg.route, off, b1.astype(np.float64))
+    H.resolve_routing(Rb, rb2["topk_idx"].cpu().numpy(), cfg.top_k)
+
+
+def test_bias_step_at_exact_mean_and_determinism():
+    """Counts given directly: experts at, above and below the mean T*k/N;
+    two calls give bit-identical statistics."""
+    cfg = H.small_config(C[3], 122, T=8, d_model=64, n_experts=4, top_k=2, d_ff=64)
+    R = RouterOnly(cfg)
+    x = W.make_x(cfg).to("cuda")
+    counts = torch.tensor([4, 5, 3, 4], dtype=torch.int32, device="cuda")  # mean 4
+    bias = R.t["select_bias"].clone()
+    b0 = bias.cpu().numpy()
+    s1 = R.stats(x, counts, bias)
+    s2 = R.stats(x, counts, None)
+    torch.cuda.synchronize()
+    d = np.float32(STEP)
+    assert np.array_equal(bias.cpu().numpy(),
+                          np.array([b0[0], b0[1] - d, b0[2] + d, b0[3]], dtype=np.float32))
+    for k in s1:
+        assert torch.equal(s1[k], s2[k]), k

@@ -54,6 +54,7 @@ __all__ = [
     "gather_rows", "silu", "swiglu_expert", "combine",
     "moe_forward", "moe_forward_with_routing", "expected_experts_touched",
     "router_probabilities", "load_statistics", "bias_controller_step",
+    "capacity_limit", "capacity_dispatch", "moe_forward_capacity",
     "PARITY_PINS",
 ]
 
@@ -83,6 +84,11 @@ PARITY_PINS = {
         "alpha*N at full collapse; sum f = sum P = 1; pure-Python brute force",
     "bias_controller_step": "[AIS-12] +-0.001 rule on hand-built counts "
         "(over, under, exactly at the mean); float32 exactness",
+    "capacity_limit": "[CH19] 19.6.1 formula on exact cases, including "
+        "factors whose float product overshoots an integer",
+    "capacity_dispatch / moe_forward_capacity": "pure-Python first-come "
+        "brute force; C >= max load equals dropless; C = 0 leaves only the "
+        "shared expert; dropped branches contribute 0, gates not renormalised",
 }
 
 
@@ -474,3 +480,62 @@ def bias_controller_step(bias: np.ndarray, counts: np.ndarray, k: int,
     sign = np.sign(total - c * N).astype(np.float32)  # +1 under-, -1 overloaded
     b = np.asarray(bias, dtype=np.float32)
     return (b + np.float32(step) * sign).astype(np.float32)
+
+
+# ---------------------------------------------------------------------------
+# Capacity-limited dispatch
+# ---------------------------------------------------------------------------
+
+def capacity_limit(factor, T: int, k: int, n_experts: int) -> int:
+    """Per-expert capacity C = ceil(c * T * k / N) ([CH19] 19.6.1), computed
+    exactly in rational arithmetic with the factor taken as the decimal number
+    it is written as (a float's shortest decimal form), so that c = 1.1 with
+    T*k/N = 100 gives 110, not the 111 a float product would give."""
+    from fractions import Fraction
+    c = Fraction(repr(float(factor))) if isinstance(factor, float) else Fraction(factor)
+    q = c * T * k / n_experts
+    return int(math.ceil(q))
+
+
+def capacity_dispatch(idx: np.ndarray, n_experts: int, capacity: int):
+    """Dispatch with a per-expert cap ([CH19] 19.6.1 "Capacity-limited";
+    [AIS-12] "How are experts kept evenly busy?"; [MoE-EXP] capacity
+    paragraph): each expert keeps its first `capacity` assignments in token
+    order (then slot order) and drops the rest.
+
+    Returns (Permutation of the kept assignments in the same (expert, token,
+    slot) order, keep mask [T][k]).  Dropped assignments have inv_perm -1."""
+    idx = np.asarray(idx, dtype=np.int64)
+    T, k = idx.shape
+    full = permute_assignments(idx, n_experts)
+    keep = np.zeros((T, k), dtype=bool)
+    counts = np.minimum(full.counts, capacity)
+    offsets = expert_offsets(counts)
+    perm = np.zeros(int(offsets[-1]), dtype=np.int64)
+    slot = np.zeros(int(offsets[-1]), dtype=np.int64)
+    inv = np.full((T, k), -1, dtype=np.int64)
+    for t in range(T):
+        for i in range(k):
+            e = int(idx[t, i])
+            rank = int(full.inv_perm[t, i]) - int(full.offsets[e])
+            if rank < capacity:
+                keep[t, i] = True
+                r = int(offsets[e]) + rank
+                perm[r], slot[r] = t, i
+                inv[t, i] = r
+    return Permutation(counts=counts, offsets=offsets, perm_token=perm, perm_slot=slot,
+                       inv_perm=inv), keep
+
+
+def moe_forward_capacity(x, w_router, experts, k: int, capacity: int, route: str = "softmax",
+                         offset=None, select_bias=None, shared=None):
+    """The layer with capacity-limited dispatch: a dropped assignment's
+    branch contributes nothing and the remaining gates are not renormalised
+    (reading: the pages say only that the dropped branch skips its expert,
+    [MoE-EXP] capacity paragraph; [CH19] 19.6.1)."""
+    x = np.asarray(x, dtype=np.float64)
+    r = route_tokens(x, w_router, k, route, offset, select_bias)
+    _, keep = capacity_dispatch(r.idx, w_router.shape[1], capacity)
+    gates = np.where(keep, r.gates, 0.0)
+    out, _, _, _ = moe_forward_with_routing(x, r.idx, gates, experts, w_router.shape[1], shared)
+    return out, r, keep

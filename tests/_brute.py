@@ -107,3 +107,16 @@ def load_stats(logits, counts, k, alpha):
             P[i] += z[i] / tot / T
     f = [counts[i] / (T * k) for i in range(N)]
     return f, P, alpha * N * math.fsum(f[i] * P[i] for i in range(N))
+
+
+def capacity_keep(idx, n_experts, cap):
+    """First come, first served in token order then slot order: keep[t][i]."""
+    used = [0] * n_experts
+    keep = []
+    for row in idx:
+        kr = []
+        for e in row:
+            kr.append(used[e] < cap)
+            used[e] += 1
+        keep.append(kr)
+    return keep

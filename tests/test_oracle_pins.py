@@ -445,6 +445,65 @@ def pin_bias_controller_balances():
         bias = O.bias_controller_step(bias, c, k, step=0.01)
     assert np.mean(imb[-10:]) < 0.6 * np.mean(imb[:3]), imb
 
+
+# ---------------------------------------------------------------------------
+# capacity-limited dispatch
+# ---------------------------------------------------------------------------
+
+def pin_capacity_limit():
+    """[CH19] 19.6.1: C = ceil(c * T * K / N).  T*K/N = 100 and c = 1.1 give
+    110 (the float product 1.1 * 100 is 110.00000000000001, and the binary
+    value of 1.1 also exceeds 11/10); T*K/N = 10: c = 1.1 gives 11, c = 1.25
+    gives 13 (12.5 up), c = 1.0 gives 10; T*K/N = 2.5 with c = 1.0 gives 3."""
+    assert O.capacity_limit(1.1, 20, 2, 4) == 11
+    assert O.capacity_limit(1.1, 100, 1, 1) == 110
+    assert O.capacity_limit(1.1, 400, 2, 8) == 110
+    assert O.capacity_limit(1.25, 20, 2, 4) == 13
+    assert O.capacity_limit(1.0, 20, 2, 4) == 10
+    assert O.capacity_limit(1.0, 5, 2, 4) == 3
+    assert O.capacity_limit(2.0, 64, 1, 8) == 16
+
+
+def pin_capacity_dispatch_brute():
+    rng = np.random.default_rng(31)
+    T, N, k = 40, 6, 2
+    scores = rng.normal(0, 1, (T, N)) + np.array([1.5, 1.0, 0, 0, 0, 0])  # two hot experts
+    idx = O.top_k_select(scores, k)
+    for cap in (0, 3, 9, 40):
+        P, keep = O.capacity_dispatch(idx, N, cap)
+        bk = B.capacity_keep(idx.tolist(), N, cap)
+        assert keep.tolist() == bk
+        assert np.array_equal(P.counts, np.minimum(np.bincount(idx.ravel(), minlength=N), cap))
+        kept = [(int(idx[t, i]), t, i) for t in range(T) for i in range(k) if bk[t][i]]
+        assert [(int(idx[t, i]), t, i) for t, i in zip(P.perm_token, P.perm_slot)] == sorted(kept)
+        for t in range(T):
+            for i in range(k):
+                r = P.inv_perm[t, i]
+                assert (r >= 0) == bk[t][i] and (r < 0 or (P.perm_token[r], P.perm_slot[r]) == (t, i))
+
+
+def pin_capacity_layer():
+    """C >= max load is the dropless layer; C = 0 leaves only the shared
+    expert; with a cap, a dropped branch contributes nothing and the kept
+    gate keeps its value (no renormalisation)."""
+    rng = np.random.default_rng(32)
+    T, d, N, k, f = 24, 8, 4, 2, 6
+    x = rng.normal(0, 1, (T, d))
+    w = rng.normal(0, 1, (d, N)) + np.array([0.8, 0, 0, 0])
+    ex = [tuple(rng.normal(0, 0.3, s) for s in ((f, d), (f, d), (d, f))) for _ in range(N + 1)]
+    full, r, _ = O.moe_forward(x, w, ex[:N], k, "softmax", shared=ex[N])
+    same, _, keep = O.moe_forward_capacity(x, w, ex[:N], k, T * k, "softmax", shared=ex[N])
+    assert keep.all() and np.allclose(same, full, rtol=0, atol=1e-15)
+    zero, _, _ = O.moe_forward_capacity(x, w, ex[:N], k, 0, "softmax", shared=ex[N])
+    assert np.allclose(zero, O.swiglu_expert(x, *ex[N]), rtol=0, atol=1e-15)
+    cap = 5
+    out, r, keep = O.moe_forward_capacity(x, w, ex[:N], k, cap, "softmax")
+    assert not keep.all()
+    for t in range(T):
+        want = sum(r.gates[t, i] * O.swiglu_expert(x[t:t + 1], *ex[r.idx[t, i]])[0]
+                   for i in range(k) if keep[t, i]) if keep[t].any() else np.zeros(d)
+        assert np.allclose(out[t], want, rtol=1e-12, atol=1e-14)
+
 ALL_PINS = [
     pin_router_worked_example_skillsuites, pin_router_worked_example_ai_infra,
     pin_softmax_placement_equivalence, pin_brute_force_routing,
@@ -454,6 +513,7 @@ ALL_PINS = [
     pin_bf16_decoder, pin_e4m3_decoder, pin_fp8_block_dequant,
     pin_experts_touched, pin_router_probabilities, pin_load_statistics_closed_forms,
     pin_load_statistics_brute, pin_bias_controller_rule, pin_bias_controller_balances,
+    pin_capacity_limit, pin_capacity_dispatch_brute, pin_capacity_layer,
 ]
 
 
@@ -561,6 +621,31 @@ _orig_load_stats = O.load_statistics
 _orig_bias_step = O.bias_controller_step
 
 
+def _m_capacity_float_ceil(factor, T, k, n):
+    return int(math.ceil(factor * T * k / n))
+
+
+def _m_capacity_keeps_last(idx, n_experts, capacity):
+    rev = np.asarray(idx)[::-1]
+    P, keep = _orig_cap_dispatch(rev, n_experts, capacity)
+    return P, keep[::-1]
+
+
+def _m_capacity_renormalise(x, w_router, experts, k, capacity, route="softmax", offset=None,
+                            select_bias=None, shared=None):
+    x = np.asarray(x, dtype=np.float64)
+    r = O.route_tokens(x, w_router, k, route, offset, select_bias)
+    _, keep = O.capacity_dispatch(r.idx, w_router.shape[1], capacity)
+    g = np.where(keep, r.gates, 0.0)
+    s = g.sum(axis=1, keepdims=True)
+    g = np.where(s > 0, g / np.where(s > 0, s, 1), 0)
+    out, _, _, _ = O.moe_forward_with_routing(x, r.idx, g, experts, w_router.shape[1], shared)
+    return out, r, keep
+
+
+_orig_cap_dispatch = O.capacity_dispatch
+
+
 _orig_perm = O.permute_assignments
 _orig_bf16 = O.bf16_bits_to_f64
 _orig_e4m3 = O.e4m3_bits_to_f64
@@ -585,6 +670,9 @@ MUTATIONS = {
     "probabilities_not_normalised": ("router_probabilities", lambda: _m_probs_before_normalise),
     "bias_controller_sign_flipped": ("bias_controller_step", lambda: _m_bias_sign_flipped),
     "bias_controller_moves_at_mean": ("bias_controller_step", lambda: _m_bias_moves_at_mean),
+    "capacity_float_ceiling": ("capacity_limit", lambda: _m_capacity_float_ceil),
+    "capacity_keeps_last_arrivals": ("capacity_dispatch", lambda: _m_capacity_keeps_last),
+    "capacity_renormalises_gates": ("moe_forward_capacity", lambda: _m_capacity_renormalise),
 }
 
 

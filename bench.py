@@ -245,6 +245,31 @@ def main():
     ls_bytes = T * d * (2 if adt == torch.bfloat16 else 4) + d * N_ * 4 + 4 * N_ * 4
     ls_gbs = ls_bytes / (ls_ms * 1e-3) / 1e9
 
+    # Capacity-limited dispatch at capacity factor 1.0: the capped routing on
+    # its own, and the whole layer with it
+    cap = -(-T * k // N_)  # ceil(1.0 * T * k / N)
+    rc = {kk: torch.empty_like(v) for kk, v in rb.items() if kk in
+          ("counts", "offsets", "perm_token", "inv_perm")}
+    rcs = moe.make_routing(**rc)
+    out_c = torch.empty_like(x)
+    for _ in range(2):
+        moe.moe_permute_capacity(s, rb["topk_idx"], cap, rcs, ws)
+        moe.moe_layer_forward_capacity(s, L.weights, x, out_c, cap, ws)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(a.steps):
+        moe.moe_permute_capacity(s, rb["topk_idx"], cap, rcs, ws)
+    e1.record()
+    torch.cuda.synchronize()
+    cap_ms = e0.elapsed_time(e1) / a.steps
+    kept = int(rc["offsets"][N_].item())
+    e0.record()
+    for _ in range(a.steps):
+        moe.moe_layer_forward_capacity(s, L.weights, x, out_c, cap, ws)
+    e1.record()
+    torch.cuda.synchronize()
+    cap_layer_ms = e0.elapsed_time(e1) / a.steps
+
     counts = rb["counts"].cpu()
     touched = int((counts > 0).sum())
     st, layer = accounting(cfg, touched)
@@ -280,7 +305,12 @@ def main():
         "next_rows": {"load_stats": {
             "ms": round(ls_ms, 4), "bytes": ls_bytes, "bound": "hbm",
             "achieved": round(ls_gbs, 1), "unit": "GB/s", "frac": round(ls_gbs / PEAK_HBM_GBS, 4),
-            "what": "moe_load_stats: router probabilities, shares, balancing term, bias step"}},
+            "what": "moe_load_stats: router probabilities, shares, balancing term, bias step"},
+            "capacity_dispatch": {
+                "capacity_factor": 1.0, "capacity": cap, "kept": kept, "assignments": T * k,
+                "permute_capacity_ms": round(cap_ms, 4), "layer_ms": round(cap_layer_ms, 4),
+                "layer_tokens_per_s": round(T / (cap_layer_ms * 1e-3), 2),
+                "what": "moe_permute_capacity and moe_layer_forward_capacity, C = ceil(T*k/N)"}},
     }
     if not a.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)

@@ -131,7 +131,8 @@ moe_status_t moe_pack_weights(const moe_shape_t* s, int which, int n_mats,
  * router partial logits [S][T][N] f32 (S >= 1 K-splits), topk idx/w,
  * counts, offsets, perm_token, inv_perm, per-256-token-block expert counts
  * [ceil(T/256)][N] int32, per-16-token-block probability sums
- * [ceil(T/16)][N] f32, an 8 KB tile schedule, H [T*k][d_ff]
+ * [ceil(T/16)][N] f32, a second counts / offsets / perm_token / inv_perm
+ * set (capacity-limited routing), an 8 KB tile schedule, H [T*k][d_ff]
  * and H_shared [T][d_ff], Y [T*k][d] and Y_shared [T][d] (H, Y in the
  * activation type).  moe_expert_gate_up / moe_expert_down use only the
  * schedule piece but check ws_bytes against the full size. */
@@ -156,6 +157,20 @@ moe_status_t moe_router_topk(const moe_shape_t* s, const void* x,
 moe_status_t moe_permute(const moe_shape_t* s, const int32_t* topk_idx,
                          const void* x, moe_routing_t* out, void* x_perm,
                          void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* a3+a4 with a per-expert capacity ([CH19] 19.6.1 "Expert capacity: where
+ * do overflow tokens go?"; [AIS-12] "How are experts kept evenly busy?";
+ * [MoE-EXP] capacity paragraph): as moe_permute, then each expert keeps only
+ * its first `capacity` assignments in token order (then slot order); the
+ * rest are dropped and get inv_perm = -1, so moe_combine gives them no
+ * contribution (the remaining gates are not renormalised).  counts and
+ * offsets describe the kept rows.  The capacity is an integer, normally
+ * C = ceil(c * T * k / N) for a capacity factor c; capacity < 0 is
+ * MOE_ERR_INVALID_ARG.  x_perm is not offered (moe_grouped_ffn gathers
+ * through perm_token).  ws holds the dropless routing. */
+moe_status_t moe_permute_capacity(const moe_shape_t* s, const int32_t* topk_idx,
+                                  int32_t capacity, moe_routing_t* out, void* ws,
+                                  size_t ws_bytes, hipStream_t stream);
 
 /* a5+a6: every routed expert's SwiGLU FFN on its rows, and the shared
  * expert on all T tokens.  Rows of expert e are r in
@@ -226,6 +241,15 @@ moe_status_t moe_layer_forward(const moe_shape_t* s, const moe_weights_t* w,
                                const void* x, void* out,
                                moe_routing_t* routing_out, void* ws,
                                size_t ws_bytes, hipStream_t stream);
+
+/* moe_layer_forward with capacity-limited dispatch (see
+ * moe_permute_capacity): experts run only on their kept rows and dropped
+ * branches contribute nothing.  routing_out, when given, receives the
+ * capped routing.  capacity >= T*k is the dropless layer. */
+moe_status_t moe_layer_forward_capacity(const moe_shape_t* s, const moe_weights_t* w,
+                                        const void* x, void* out, int32_t capacity,
+                                        moe_routing_t* routing_out, void* ws,
+                                        size_t ws_bytes, hipStream_t stream);
 
 /* Static description of a status code. */
 const char* moe_status_string(moe_status_t st);

@@ -75,7 +75,8 @@ moe_status_t check_shape(const moe_shape_t* s) {
 }
 
 struct WsLayout {
-  size_t logits, idx, w, counts, offsets, perm, inv, hist, stats, sched, H, H_sh, Y, Y_sh, total;
+  size_t logits, idx, w, counts, offsets, perm, inv, hist, stats, ccounts, coffsets, cperm, cinv,
+      sched, H, H_sh, Y, Y_sh, total;
 };
 
 WsLayout ws_layout(const moe_shape_t* s) {
@@ -98,6 +99,10 @@ WsLayout ws_layout(const moe_shape_t* s) {
   L.inv = take(T * k * 4);
   L.hist = take((size_t)permute_blocks(s->n_tokens) * N * 4);
   L.stats = take((size_t)stats_blocks(s->n_tokens) * N * 4);
+  L.ccounts = take(N * 4);
+  L.coffsets = take((N + 1) * 4);
+  L.cperm = take(T * k * 4);
+  L.cinv = take(T * k * 4);
   L.sched = take(2048 * 4);
   L.H = take(T * k * f * es);
   L.H_sh = take(sh * T * f * es);
@@ -288,6 +293,36 @@ moe_status_t moe_permute(const moe_shape_t* s, const int32_t* topk_idx, const vo
   return MOE_OK;
 }
 
+moe_status_t moe_permute_capacity(const moe_shape_t* s, const int32_t* topk_idx, int32_t capacity,
+                                  moe_routing_t* out, void* ws, size_t ws_bytes,
+                                  hipStream_t stream) {
+  moe_status_t st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (!out || !out->counts || !out->offsets || !out->perm_token || !out->inv_perm)
+    return fail(MOE_ERR_INVALID_ARG, "routing counts / offsets / perm_token / inv_perm is NULL");
+  if (!topk_idx) return fail(MOE_ERR_INVALID_ARG, "topk_idx is NULL");
+  if (capacity < 0) return fail(MOE_ERR_INVALID_ARG, "capacity is negative");
+  if (s->n_tokens == 0) {
+    HIP_TRY("permute", launch_permute(topk_idx, 0, s->top_k, s->n_experts, nullptr, out->counts,
+                                      out->offsets, out->perm_token, out->inv_perm, stream));
+    return MOE_OK;
+  }
+  if ((st = check_ws(s, ws, ws_bytes)) != MOE_OK) return st;
+  const WsLayout L = ws_layout(s);
+  char* b = static_cast<char*>(ws);
+  int32_t* cf = reinterpret_cast<int32_t*>(b + L.counts);
+  int32_t* of = reinterpret_cast<int32_t*>(b + L.offsets);
+  int32_t* pf = reinterpret_cast<int32_t*>(b + L.perm);
+  int32_t* vf = reinterpret_cast<int32_t*>(b + L.inv);
+  HIP_TRY("permute", launch_permute(topk_idx, s->n_tokens, s->top_k, s->n_experts,
+                                    reinterpret_cast<int32_t*>(b + L.hist), cf, of, pf, vf,
+                                    stream));
+  HIP_TRY("capacity", launch_capacity(topk_idx, s->n_tokens, s->top_k, s->n_experts, capacity, cf,
+                                      of, vf, out->counts, out->offsets, out->perm_token,
+                                      out->inv_perm, stream));
+  return MOE_OK;
+}
+
 moe_status_t moe_grouped_ffn(const moe_shape_t* s, const void* x, const void* x_perm,
                              const int32_t* perm_token, const int32_t* offsets,
                              const moe_weights_t* w, void* y_perm, void* y_shared, void* ws,
@@ -387,9 +422,9 @@ moe_status_t moe_load_stats(const moe_shape_t* s, const void* x, const moe_weigh
   return MOE_OK;
 }
 
-moe_status_t moe_layer_forward(const moe_shape_t* s, const moe_weights_t* w, const void* x,
-                               void* out, moe_routing_t* r, void* ws, size_t ws_bytes,
-                               hipStream_t stream) {
+static moe_status_t layer_forward(const moe_shape_t* s, const moe_weights_t* w, const void* x,
+                                  void* out, moe_routing_t* r, int32_t capacity, void* ws,
+                                  size_t ws_bytes, hipStream_t stream) {
   moe_status_t st = check_shape(s);
   if (st != MOE_OK) return st;
   if (s->n_tokens == 0) return MOE_OK;
@@ -399,18 +434,31 @@ moe_status_t moe_layer_forward(const moe_shape_t* s, const moe_weights_t* w, con
   if ((st = check_ws(s, ws, ws_bytes)) != MOE_OK) return st;
   const WsLayout L = ws_layout(s);
   char* b = static_cast<char*>(ws);
-  int32_t* idx = (r && r->topk_idx) ? r->topk_idx : reinterpret_cast<int32_t*>(b + L.idx);
+  auto wsi = [&](size_t off) { return reinterpret_cast<int32_t*>(b + off); };
+  int32_t* idx = (r && r->topk_idx) ? r->topk_idx : wsi(L.idx);
   float* gw = (r && r->topk_w) ? r->topk_w : reinterpret_cast<float*>(b + L.w);
-  int32_t* counts = (r && r->counts) ? r->counts : reinterpret_cast<int32_t*>(b + L.counts);
-  int32_t* offs = (r && r->offsets) ? r->offsets : reinterpret_cast<int32_t*>(b + L.offsets);
-  int32_t* perm = (r && r->perm_token) ? r->perm_token : reinterpret_cast<int32_t*>(b + L.perm);
-  int32_t* inv = (r && r->inv_perm) ? r->inv_perm : reinterpret_cast<int32_t*>(b + L.inv);
+  // the routing the experts and the combine use: the caller's buffers when
+  // given, else the workspace; with a capacity, the dropless routing goes to
+  // the workspace first and the capped one to these
+  const bool capped = capacity >= 0;
+  int32_t* counts = (r && r->counts) ? r->counts : wsi(capped ? L.ccounts : L.counts);
+  int32_t* offs = (r && r->offsets) ? r->offsets : wsi(capped ? L.coffsets : L.offsets);
+  int32_t* perm = (r && r->perm_token) ? r->perm_token : wsi(capped ? L.cperm : L.perm);
+  int32_t* inv = (r && r->inv_perm) ? r->inv_perm : wsi(capped ? L.cinv : L.inv);
 
   if ((st = run_router(s, x, w, idx, gw, reinterpret_cast<float*>(b + L.logits), stream)) != MOE_OK)
     return st;
-  HIP_TRY("permute", launch_permute(idx, s->n_tokens, s->top_k, s->n_experts,
-                                    reinterpret_cast<int32_t*>(b + L.hist), counts, offs, perm,
-                                    inv, stream));
+  if (!capped) {
+    HIP_TRY("permute", launch_permute(idx, s->n_tokens, s->top_k, s->n_experts, wsi(L.hist),
+                                      counts, offs, perm, inv, stream));
+  } else {
+    HIP_TRY("permute", launch_permute(idx, s->n_tokens, s->top_k, s->n_experts, wsi(L.hist),
+                                      wsi(L.counts), wsi(L.offsets), wsi(L.perm), wsi(L.inv),
+                                      stream));
+    HIP_TRY("capacity", launch_capacity(idx, s->n_tokens, s->top_k, s->n_experts, capacity,
+                                        wsi(L.counts), wsi(L.offsets), wsi(L.inv), counts, offs,
+                                        perm, inv, stream));
+  }
   if ((st = run_ffn(s, x, x, perm, offs, w, b + L.H, b + L.H_sh, b + L.Y, b + L.Y_sh,
                     b + L.sched, 3, stream)) != MOE_OK)
     return st;
@@ -418,6 +466,20 @@ moe_status_t moe_layer_forward(const moe_shape_t* s, const moe_weights_t* w, con
                                     s->n_tokens, s->top_k, s->d_model, s->act_dtype == MOE_BF16,
                                     stream));
   return MOE_OK;
+}
+
+moe_status_t moe_layer_forward(const moe_shape_t* s, const moe_weights_t* w, const void* x,
+                               void* out, moe_routing_t* r, void* ws, size_t ws_bytes,
+                               hipStream_t stream) {
+  return layer_forward(s, w, x, out, r, -1, ws, ws_bytes, stream);
+}
+
+moe_status_t moe_layer_forward_capacity(const moe_shape_t* s, const moe_weights_t* w,
+                                        const void* x, void* out, int32_t capacity,
+                                        moe_routing_t* r, void* ws, size_t ws_bytes,
+                                        hipStream_t stream) {
+  if (capacity < 0) return fail(MOE_ERR_INVALID_ARG, "capacity is negative");
+  return layer_forward(s, w, x, out, r, capacity, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -32,6 +32,11 @@ hipError_t launch_permute(const int32_t* topk_idx, int T, int k, int N, int32_t*
                           int32_t* inv_perm, hipStream_t st);
 
 // x_perm[r] = x[perm_token[r]] for r < rows (row_bytes per row).
+// capacity-limited routing from the dropless one (counts_f/offsets_f/inv_f)
+hipError_t launch_capacity(const int32_t* topk_idx, int T, int k, int N, int cap,
+                           const int32_t* counts_f, const int32_t* offsets_f, const int32_t* inv_f,
+                           int32_t* counts, int32_t* offsets, int32_t* perm_token,
+                           int32_t* inv_perm, hipStream_t st);
 hipError_t launch_gather_rows(const void* x, const int32_t* perm_token, void* x_perm,
                               int rows, int row_bytes, hipStream_t st);
 

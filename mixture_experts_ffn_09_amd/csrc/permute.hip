@@ -170,6 +170,47 @@ __global__ __launch_bounds__(256) void permute_kernel(const int32_t* __restrict_
   }
 }
 
+// Capacity-limited dispatch ("Chapter 19", 19.6.1): from the dropless
+// routing (counts_f, offsets_f, inv_f as written by permute_kernel), each
+// expert keeps the first `cap` rows of its segment - its first cap
+// assignments in token order, then slot order - and the kept rows are packed
+// in the same order.  Dropped assignments get inv_perm = -1.  Every block
+// recomputes the capped offsets (N <= 512); block 0 writes counts/offsets.
+__global__ __launch_bounds__(256) void capacity_kernel(
+    const int32_t* __restrict__ idx, int A, int k, int N, int cap,
+    const int32_t* __restrict__ counts_f, const int32_t* __restrict__ offsets_f,
+    const int32_t* __restrict__ inv_f, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ perm_token,
+    int32_t* __restrict__ inv_perm) {
+  extern __shared__ int32_t sm[];
+  int32_t* oc = sm;           // [N] capped counts, then their exclusive offsets
+  int32_t* wtot = sm + N;     // [PB_WAVES]
+  const int tid = threadIdx.x;
+  for (int e = tid; e < N; e += 256) oc[e] = min(counts_f[e], cap);
+  __syncthreads();
+  if (blockIdx.x == 0)
+    for (int e = tid; e < N; e += 256) counts[e] = oc[e];
+  __syncthreads();
+  const int total = block_exclusive_scan(oc, N, wtot);
+  if (blockIdx.x == 0) {
+    for (int e = tid; e < N; e += 256) offsets[e] = oc[e];
+    if (tid == 0) offsets[N] = total;
+  }
+  for (int a = blockIdx.x * 256 + tid; a < A; a += gridDim.x * 256) {
+    const int e = idx[a];
+    const int pos = inv_f[a];
+    int r = -1;
+    if (pos >= 0 && e >= 0 && e < N) {
+      const int rank = pos - offsets_f[e];
+      if (rank < cap) {
+        r = oc[e] + rank;
+        perm_token[r] = a / k;
+      }
+    }
+    inv_perm[a] = r;
+  }
+}
+
 __global__ __launch_bounds__(256) void gather_rows_kernel(const uint8_t* __restrict__ x,
                                                           const int32_t* __restrict__ perm,
                                                           uint8_t* __restrict__ xp, int rows,
@@ -206,6 +247,19 @@ hipError_t launch_permute(const int32_t* topk_idx, int T, int k, int N, int32_t*
   const size_t lds = ((size_t)(PB_WAVES + 2) * N + PB_WAVES + (size_t)PB_TOK * k) * sizeof(int32_t);
   permute_kernel<<<nblk, 256, lds, st>>>(topk_idx, T, k, N, nbits, nblk > 1 ? hist : nullptr,
                                          nblk, counts, offsets, perm_token, inv_perm);
+  return hipGetLastError();
+}
+
+hipError_t launch_capacity(const int32_t* topk_idx, int T, int k, int N, int cap,
+                           const int32_t* counts_f, const int32_t* offsets_f, const int32_t* inv_f,
+                           int32_t* counts, int32_t* offsets, int32_t* perm_token,
+                           int32_t* inv_perm, hipStream_t st) {
+  const int A = T * k;
+  int grid = ceil_div(A, 256);
+  grid = grid < 1 ? 1 : (grid > 1024 ? 1024 : grid);
+  const size_t lds = ((size_t)N + PB_WAVES) * sizeof(int32_t);
+  capacity_kernel<<<grid, 256, lds, st>>>(topk_idx, A, k, N, cap, counts_f, offsets_f, inv_f,
+                                          counts, offsets, perm_token, inv_perm);
   return hipGetLastError();
 }
 

@@ -27,7 +27,8 @@ ROUTE_CODES = {"softmax": MOE_ROUTE_SOFTMAX_TOPK, "sigmoid": MOE_ROUTE_SIGMOID_B
 EXPORTS = ["moe_packed_weight_bytes", "moe_pack_weights", "moe_workspace_bytes",
            "moe_router_topk", "moe_permute", "moe_grouped_ffn", "moe_expert_gate_up",
            "moe_expert_down", "moe_combine", "moe_layer_forward", "moe_load_stats",
-           "moe_status_string", "moe_last_error"]
+           "moe_permute_capacity", "moe_layer_forward_capacity", "moe_status_string",
+           "moe_last_error"]
 
 
 class MoEError(RuntimeError):
@@ -80,9 +81,12 @@ def lib() -> C.CDLL:
                                         C.c_size_t, P]
         L.moe_load_stats.argtypes = [S, P, C.POINTER(Weights), P, C.c_float, C.c_float, P, P, P, P,
                                      P, C.c_size_t, P]
+        L.moe_permute_capacity.argtypes = [S, P, C.c_int32, C.POINTER(Routing), P, C.c_size_t, P]
+        L.moe_layer_forward_capacity.argtypes = [S, C.POINTER(Weights), P, P, C.c_int32,
+                                                 C.POINTER(Routing), P, C.c_size_t, P]
         for f in ("moe_pack_weights", "moe_router_topk", "moe_permute", "moe_grouped_ffn",
                   "moe_expert_gate_up", "moe_expert_down", "moe_combine", "moe_layer_forward",
-                  "moe_load_stats"):
+                  "moe_load_stats", "moe_permute_capacity", "moe_layer_forward_capacity"):
             getattr(L, f).restype = C.c_int
         L.moe_status_string.argtypes = [C.c_int]
         L.moe_status_string.restype = C.c_char_p
@@ -214,3 +218,19 @@ def moe_load_stats(shape: Shape, x: torch.Tensor, weights: Weights, counts: torc
                                 C.c_float(alpha), C.c_float(step), _ptr(frac), _ptr(prob),
                                 _ptr(aux), _ptr(bias), _ptr(ws), ws.numel() * ws.element_size(),
                                 _stream()))
+
+
+def moe_permute_capacity(shape: Shape, topk_idx: torch.Tensor, capacity: int, out: Routing,
+                         ws: torch.Tensor):
+    _check(lib().moe_permute_capacity(C.byref(shape), _ptr(topk_idx), C.c_int32(capacity),
+                                      C.byref(out), _ptr(ws), ws.numel() * ws.element_size(),
+                                      _stream()))
+
+
+def moe_layer_forward_capacity(shape: Shape, weights: Weights, x: torch.Tensor,
+                               out: torch.Tensor, capacity: int, ws: torch.Tensor,
+                               routing: Optional[Routing] = None):
+    _check(lib().moe_layer_forward_capacity(C.byref(shape), C.byref(weights), _ptr(x), _ptr(out),
+                                            C.c_int32(capacity),
+                                            C.byref(routing) if routing is not None else None,
+                                            _ptr(ws), ws.numel() * ws.element_size(), _stream()))

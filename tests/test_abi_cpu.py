@@ -156,7 +156,8 @@ def test_workspace_size_formula(T, N, k, d, f, sh):
     a = lambda v: (v + 255) // 256 * 256
     S = _router_splits(T, N, d)
     want = (a(S * T * N * 4) + 2 * a(T * k * 4) + a(N * 4) + a((N + 1) * 4) + 2 * a(T * k * 4)
-            + a(-(-T // 256) * N * 4) + a(-(-T // 16) * N * 4) + a(2048 * 4) + a(T * k * f * 2)
+            + a(-(-T // 256) * N * 4) + a(-(-T // 16) * N * 4)
+            + a(N * 4) + a((N + 1) * 4) + 2 * a(T * k * 4) + a(2048 * 4) + a(T * k * f * 2)
             + a(sh * T * f * 2) + a(T * k * d * 2)
             + a(sh * T * d * 2))
     assert moe.moe_workspace_bytes(s) == want
@@ -212,3 +213,21 @@ def test_load_stats_argument_checks():
     s0 = shape(T=0)
     assert call(C.byref(s0), None, None, None, f(0.01), f(1e-3), None, None, None, None, None,
                 C.c_size_t(0), None) == moe.MOE_OK
+
+
+def test_capacity_argument_checks():
+    s = shape()
+    ws = C.c_size_t(moe.moe_workspace_bytes(s))
+    r = moe.Routing(counts=FAKE.value, offsets=FAKE.value, perm_token=FAKE.value,
+                    inv_perm=FAKE.value)
+    assert _status("moe_permute_capacity", C.byref(s), FAKE, -1, C.byref(r), FAKE, ws,
+                   None) == moe.MOE_ERR_INVALID_ARG
+    assert _status("moe_permute_capacity", C.byref(s), None, 4, C.byref(r), FAKE, ws,
+                   None) == moe.MOE_ERR_INVALID_ARG
+    assert _status("moe_permute_capacity", C.byref(s), FAKE, 4, C.byref(moe.Routing()), FAKE, ws,
+                   None) == moe.MOE_ERR_INVALID_ARG
+    assert _status("moe_permute_capacity", C.byref(s), FAKE, 4, C.byref(r), FAKE,
+                   C.c_size_t(ws.value - 1), None) == moe.MOE_ERR_WORKSPACE_TOO_SMALL
+    w = moe.Weights(w_router=FAKE.value, w13=FAKE.value, w2=FAKE.value)
+    assert _status("moe_layer_forward_capacity", C.byref(s), C.byref(w), FAKE,
+                   C.c_void_p(0x2000), -3, None, FAKE, ws, None) == moe.MOE_ERR_INVALID_ARG

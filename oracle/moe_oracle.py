@@ -55,7 +55,7 @@ __all__ = [
     "moe_forward", "moe_forward_with_routing", "expected_experts_touched",
     "router_probabilities", "load_statistics", "bias_controller_step",
     "capacity_limit", "capacity_dispatch", "moe_forward_capacity",
-    "PARITY_PINS",
+    "group_limited_top_k", "PARITY_PINS",
 ]
 
 # Which test pins each function (documentation for readers of the oracle).
@@ -86,6 +86,10 @@ PARITY_PINS = {
         "(over, under, exactly at the mean); float32 exactness",
     "capacity_limit": "[CH19] 19.6.1 formula on exact cases, including "
         "factors whose float product overshoots an integer",
+    "group_limited_top_k": "all groups allowed == top_k_select; one group "
+        "== the best expert's group; pure-Python enumeration of group subsets; "
+        "selections span <= max_groups groups.  The group-ranking rule itself "
+        "(best expert score) is a reading the pages do not fix",
     "capacity_dispatch / moe_forward_capacity": "pure-Python first-come "
         "brute force; C >= max load equals dropless; C = 0 leaves only the "
         "shared expert; dropped branches contribute 0, gates not renormalised",
@@ -225,6 +229,34 @@ def top_k_select(scores: np.ndarray, k: int) -> np.ndarray:
     return order[:, :k].astype(np.int64)
 
 
+def group_limited_top_k(scores: np.ndarray, k: int, n_groups: int,
+                        max_groups: int) -> np.ndarray:
+    """Top-k restricted to at most max_groups groups of experts ([MoE-LLM]
+    "Three tricks that tame the all-to-alls": DeepSeek-V3 ranges experts into
+    groups, one per node, and caps how many nodes a token may visit; [AIS-12]
+    "How much traffic is that? A worked example": at most 4 servers).
+
+    Groups are contiguous runs of N / n_groups experts.  Reading (the pages
+    give no ranking rule for groups): a group's score is the best selection
+    score among its experts; the max_groups best groups are kept (exact ties
+    to the lower group index), then the usual top-k runs over the experts of
+    the kept groups.  Decisions on float32-rounded scores, as top_k_select."""
+    s32 = np.asarray(scores, dtype=np.float64).astype(np.float32)
+    T, N = s32.shape
+    if N % n_groups or not 1 <= max_groups <= n_groups:
+        raise ValueError("need n_groups | N and 1 <= max_groups <= n_groups")
+    gs = N // n_groups
+    if k > max_groups * gs:
+        raise ValueError("k exceeds the experts of the allowed groups")
+    gscore = s32.reshape(T, n_groups, gs).max(axis=2)
+    keep_g = np.argsort(-gscore, axis=1, kind="stable")[:, :max_groups]
+    allowed = np.zeros((T, n_groups), dtype=bool)
+    np.put_along_axis(allowed, keep_g, True, axis=1)
+    masked = np.where(np.repeat(allowed, gs, axis=1), s32, np.float32(-np.inf))
+    order = np.argsort(-masked, axis=1, kind="stable")
+    return order[:, :k].astype(np.int64)
+
+
 def gate_weights(logits: np.ndarray, idx: np.ndarray, route: str) -> np.ndarray:
     """Mixing weights of the selected experts; each row sums to 1.
 
@@ -254,14 +286,18 @@ class Routing:
 
 
 def route_tokens(x, w_router, k: int, route: str = "softmax",
-                 logit_offset=None, select_bias=None) -> Routing:
+                 logit_offset=None, select_bias=None, groups=None) -> Routing:
     """Score, select, renormalise ([MoE-LLM] "Opening the router": the
-    skeleton is the same for softmax and sigmoid routers)."""
+    skeleton is the same for softmax and sigmoid routers).  groups =
+    (n_groups, max_groups) limits the groups a token may use."""
     if select_bias is not None and route != "sigmoid":
         raise ValueError("a selection bias belongs to the sigmoid router")
     logits = router_logits(x, w_router, logit_offset)
     scores = selection_scores(logits, route, select_bias)
-    idx = top_k_select(scores, k)
+    if groups is None:
+        idx = top_k_select(scores, k)
+    else:
+        idx = group_limited_top_k(scores, k, *groups)
     gates = gate_weights(logits, idx, route)
     return Routing(logits, scores, idx, gates)
 

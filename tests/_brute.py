@@ -120,3 +120,24 @@ def capacity_keep(idx, n_experts, cap):
             used[e] += 1
         keep.append(kr)
     return keep
+
+
+def group_limited(scores, k, n_groups, max_groups):
+    """Enumerate every set of max_groups groups; a set's value is its sorted
+    list of group maxima (float32) compared lexicographically, ties to the
+    set of lower group indices; then the k best experts inside the winning
+    set, ties to lower indices."""
+    N = len(scores[0])
+    gs = N // n_groups
+    out = []
+    for row in scores:
+        r = [f32(v) for v in row]
+        gmax = [max(r[g * gs:(g + 1) * gs]) for g in range(n_groups)]
+        best = None
+        for gset in itertools.combinations(range(n_groups), max_groups):
+            key = (sorted((-gmax[g], g) for g in gset))
+            if best is None or key < best[0]:
+                best = (key, gset)
+        allowed = [e for g in best[1] for e in range(g * gs, (g + 1) * gs)]
+        out.append(sorted(allowed, key=lambda e: (-r[e], e))[:k])
+    return out

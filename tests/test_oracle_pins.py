@@ -504,6 +504,29 @@ def pin_capacity_layer():
                    for i in range(k) if keep[t, i]) if keep[t].any() else np.zeros(d)
         assert np.allclose(out[t], want, rtol=1e-12, atol=1e-14)
 
+
+# ---------------------------------------------------------------------------
+# group-limited selection
+# ---------------------------------------------------------------------------
+
+def pin_group_limited_selection():
+    rng = np.random.default_rng(41)
+    T, N, k = 60, 24, 4
+    sc = rng.normal(0, 1, (T, N))
+    sc[5, :] = 0.25  # all tied: groups and experts fall to the lowest indices
+    # every group allowed: plain top-k
+    assert np.array_equal(O.group_limited_top_k(sc, k, 6, 6), O.top_k_select(sc, k))
+    # one group: the group of the best expert
+    one = O.group_limited_top_k(sc, k, 4, 1)
+    best = np.argmax(sc.astype(np.float32), axis=1)
+    assert np.array_equal(one // 6, np.repeat((best // 6)[:, None], k, axis=1))
+    for G, M in ((6, 2), (4, 3), (8, 3), (12, 4)):
+        got = O.group_limited_top_k(sc, k, G, M)
+        gs = N // G
+        assert all(len(set((got[t] // gs).tolist())) <= M for t in range(T))
+        bf = B.group_limited(sc.tolist(), k, G, M)
+        assert got.tolist() == bf, (G, M)
+
 ALL_PINS = [
     pin_router_worked_example_skillsuites, pin_router_worked_example_ai_infra,
     pin_softmax_placement_equivalence, pin_brute_force_routing,
@@ -514,6 +537,7 @@ ALL_PINS = [
     pin_experts_touched, pin_router_probabilities, pin_load_statistics_closed_forms,
     pin_load_statistics_brute, pin_bias_controller_rule, pin_bias_controller_balances,
     pin_capacity_limit, pin_capacity_dispatch_brute, pin_capacity_layer,
+    pin_group_limited_selection,
 ]
 
 
@@ -646,6 +670,29 @@ def _m_capacity_renormalise(x, w_router, experts, k, capacity, route="softmax", 
 _orig_cap_dispatch = O.capacity_dispatch
 
 
+def _m_group_score_sum(scores, k, n_groups, max_groups):
+    s32 = np.asarray(scores, dtype=np.float64).astype(np.float32)
+    T, N = s32.shape
+    gs = N // n_groups
+    gscore = s32.reshape(T, n_groups, gs).sum(axis=2)
+    keep_g = np.argsort(-gscore, axis=1, kind="stable")[:, :max_groups]
+    allowed = np.zeros((T, n_groups), dtype=bool)
+    np.put_along_axis(allowed, keep_g, True, axis=1)
+    masked = np.where(np.repeat(allowed, gs, axis=1), s32, np.float32(-np.inf))
+    return np.argsort(-masked, axis=1, kind="stable")[:, :k].astype(np.int64)
+
+
+def _m_group_strided(scores, k, n_groups, max_groups):
+    s = np.asarray(scores)
+    T, N = s.shape
+    perm = np.arange(N).reshape(N // n_groups, n_groups).T.reshape(-1)  # strided groups
+    got = _orig_group_topk(s[:, perm], k, n_groups, max_groups)
+    return perm[got]
+
+
+_orig_group_topk = O.group_limited_top_k
+
+
 _orig_perm = O.permute_assignments
 _orig_bf16 = O.bf16_bits_to_f64
 _orig_e4m3 = O.e4m3_bits_to_f64
@@ -673,6 +720,8 @@ MUTATIONS = {
     "capacity_float_ceiling": ("capacity_limit", lambda: _m_capacity_float_ceil),
     "capacity_keeps_last_arrivals": ("capacity_dispatch", lambda: _m_capacity_keeps_last),
     "capacity_renormalises_gates": ("moe_forward_capacity", lambda: _m_capacity_renormalise),
+    "group_score_is_sum": ("group_limited_top_k", lambda: _m_group_score_sum),
+    "groups_strided_not_contiguous": ("group_limited_top_k", lambda: _m_group_strided),
 }
 
 

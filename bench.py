@@ -270,6 +270,32 @@ def main():
     torch.cuda.synchronize()
     cap_layer_ms = e0.elapsed_time(e1) / a.steps
 
+    # Group-limited selection, DeepSeek-V3 style: 8 groups of N/8 experts,
+    # at most 4 groups per token (when the shape allows it)
+    grouped = None
+    if N_ % 8 == 0 and 4 * (N_ // 8) >= k:
+        gi = torch.empty_like(rb["topk_idx"])
+        gw_ = torch.empty_like(rb["topk_w"])
+        for _ in range(2):
+            moe.moe_router_topk_grouped(s, x, L.weights, 8, 4, gi, gw_, ws)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(a.steps):
+            moe.moe_router_topk_grouped(s, x, L.weights, 8, 4, gi, gw_, ws)
+        e1.record()
+        torch.cuda.synchronize()
+        g_router_ms = e0.elapsed_time(e1) / a.steps
+        e0.record()
+        for _ in range(a.steps):
+            moe.moe_layer_forward_grouped(s, L.weights, x, out_c, 8, 4, ws)
+        e1.record()
+        torch.cuda.synchronize()
+        g_layer_ms = e0.elapsed_time(e1) / a.steps
+        grouped = {"n_groups": 8, "max_groups": 4, "router_topk_ms": round(g_router_ms, 4),
+                   "layer_ms": round(g_layer_ms, 4),
+                   "layer_tokens_per_s": round(T / (g_layer_ms * 1e-3), 2),
+                   "what": "moe_router_topk_grouped and moe_layer_forward_grouped"}
+
     counts = rb["counts"].cpu()
     touched = int((counts > 0).sum())
     st, layer = accounting(cfg, touched)
@@ -310,7 +336,8 @@ def main():
                 "capacity_factor": 1.0, "capacity": cap, "kept": kept, "assignments": T * k,
                 "permute_capacity_ms": round(cap_ms, 4), "layer_ms": round(cap_layer_ms, 4),
                 "layer_tokens_per_s": round(T / (cap_layer_ms * 1e-3), 2),
-                "what": "moe_permute_capacity and moe_layer_forward_capacity, C = ceil(T*k/N)"}},
+                "what": "moe_permute_capacity and moe_layer_forward_capacity, C = ceil(T*k/N)"},
+            "group_limited": grouped},
     }
     if not a.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)

@@ -148,6 +148,22 @@ moe_status_t moe_router_topk(const moe_shape_t* s, const void* x,
                              float* topk_w, void* ws, size_t ws_bytes,
                              hipStream_t stream);
 
+/* moe_router_topk with group-limited selection ([MoE-LLM] "Three tricks
+ * that tame the all-to-alls": DeepSeek-V3 ranges experts into groups, one
+ * per node, and caps how many nodes a token may visit; [AIS-12] "How much
+ * traffic is that? A worked example": at most 4 servers).  The experts form
+ * n_groups groups of N / n_groups consecutive ids; a group scores as its best
+ * expert's selection score (a reading: the pages give no rule), the
+ * max_groups best groups are kept (exact ties to the lower group index) and
+ * the top-k runs over their experts.  Needs n_groups | N, n_groups <= 64
+ * (else MOE_ERR_UNSUPPORTED), 1 <= max_groups <= n_groups and
+ * top_k <= max_groups * N / n_groups (else MOE_ERR_INVALID_ARG). */
+moe_status_t moe_router_topk_grouped(const moe_shape_t* s, const void* x,
+                                     const moe_weights_t* w, int32_t n_groups,
+                                     int32_t max_groups, int32_t* topk_idx,
+                                     float* topk_w, void* ws, size_t ws_bytes,
+                                     hipStream_t stream);
+
 /* a3+a4: per-expert counts, offsets, and the stable expert-contiguous
  * permutation of (token, slot) assignments, ordered by (expert, token, slot)
  * ([CH19] 19.6.3 "Route and pack").  Ids outside [0, N) are not counted and
@@ -250,6 +266,13 @@ moe_status_t moe_layer_forward_capacity(const moe_shape_t* s, const moe_weights_
                                         const void* x, void* out, int32_t capacity,
                                         moe_routing_t* routing_out, void* ws,
                                         size_t ws_bytes, hipStream_t stream);
+
+/* moe_layer_forward with group-limited selection (see
+ * moe_router_topk_grouped).  n_groups = max_groups gives moe_layer_forward. */
+moe_status_t moe_layer_forward_grouped(const moe_shape_t* s, const moe_weights_t* w,
+                                       const void* x, void* out, int32_t n_groups,
+                                       int32_t max_groups, moe_routing_t* routing_out,
+                                       void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Static description of a status code. */
 const char* moe_status_string(moe_status_t st);

@@ -141,8 +141,26 @@ moe_status_t check_weights(const moe_shape_t* s, const moe_weights_t* w, bool ro
   return MOE_OK;
 }
 
+// Group limit of the selection: 0 groups = none.  Checked on the host.
+struct GroupLimit {
+  int n_groups = 0, max_groups = 0;
+};
+
+moe_status_t check_groups(const moe_shape_t* s, const GroupLimit& g) {
+  if (g.n_groups == 0) return MOE_OK;
+  if (g.n_groups < 1 || s->n_experts % g.n_groups)
+    return fail(MOE_ERR_INVALID_ARG, "n_groups must divide n_experts");
+  if (g.n_groups > 64) return fail(MOE_ERR_UNSUPPORTED, "n_groups > 64");
+  if (g.max_groups < 1 || g.max_groups > g.n_groups)
+    return fail(MOE_ERR_INVALID_ARG, "need 1 <= max_groups <= n_groups");
+  if ((long long)s->top_k > (long long)g.max_groups * (s->n_experts / g.n_groups))
+    return fail(MOE_ERR_INVALID_ARG, "top_k exceeds the experts of max_groups groups");
+  return MOE_OK;
+}
+
 moe_status_t run_router(const moe_shape_t* s, const void* x, const moe_weights_t* w,
-                        int32_t* idx, float* gw, float* logits, hipStream_t st) {
+                        int32_t* idx, float* gw, float* logits, hipStream_t st,
+                        const GroupLimit& g = GroupLimit()) {
   HIP_TRY("router_logits", launch_router_logits(x, s->act_dtype == MOE_BF16, w->w_router, logits,
                                                 s->n_tokens, s->d_model, s->n_experts, st));
   HIP_TRY("router_topk",
@@ -152,7 +170,8 @@ moe_status_t run_router(const moe_shape_t* s, const void* x, const moe_weights_t
                              w->logit_offset,
                              s->route == MOE_ROUTE_SIGMOID_BIAS ? w->select_bias : nullptr,
                              s->route == MOE_ROUTE_SIGMOID_BIAS, s->n_tokens, s->n_experts,
-                             s->top_k, idx, gw, st));
+                             s->top_k, g.n_groups ? s->n_experts / g.n_groups : 0,
+                             g.max_groups, idx, gw, st));
   return MOE_OK;
 }
 
@@ -256,18 +275,36 @@ size_t moe_workspace_bytes(const moe_shape_t* s) {
   return ws_layout(s).total;
 }
 
-moe_status_t moe_router_topk(const moe_shape_t* s, const void* x, const moe_weights_t* w,
-                             int32_t* topk_idx, float* topk_w, void* ws, size_t ws_bytes,
-                             hipStream_t stream) {
+static moe_status_t router_topk(const moe_shape_t* s, const void* x, const moe_weights_t* w,
+                                const GroupLimit& g, int32_t* topk_idx, float* topk_w, void* ws,
+                                size_t ws_bytes, hipStream_t stream) {
   moe_status_t st = check_shape(s);
   if (st != MOE_OK) return st;
+  if ((st = check_groups(s, g)) != MOE_OK) return st;
   if (s->n_tokens == 0) return MOE_OK;
   if ((st = check_weights(s, w, true, false)) != MOE_OK) return st;
   if (!x || !topk_idx || !topk_w) return fail(MOE_ERR_INVALID_ARG, "x / topk_idx / topk_w is NULL");
   if ((st = check_ws(s, ws, ws_bytes)) != MOE_OK) return st;
   const WsLayout L = ws_layout(s);
   return run_router(s, x, w, topk_idx, topk_w,
-                    reinterpret_cast<float*>(static_cast<char*>(ws) + L.logits), stream);
+                    reinterpret_cast<float*>(static_cast<char*>(ws) + L.logits), stream, g);
+}
+
+moe_status_t moe_router_topk(const moe_shape_t* s, const void* x, const moe_weights_t* w,
+                             int32_t* topk_idx, float* topk_w, void* ws, size_t ws_bytes,
+                             hipStream_t stream) {
+  return router_topk(s, x, w, GroupLimit(), topk_idx, topk_w, ws, ws_bytes, stream);
+}
+
+moe_status_t moe_router_topk_grouped(const moe_shape_t* s, const void* x, const moe_weights_t* w,
+                                     int32_t n_groups, int32_t max_groups, int32_t* topk_idx,
+                                     float* topk_w, void* ws, size_t ws_bytes,
+                                     hipStream_t stream) {
+  if (n_groups < 1) return fail(MOE_ERR_INVALID_ARG, "n_groups must be >= 1");
+  GroupLimit g;
+  g.n_groups = n_groups;
+  g.max_groups = max_groups;
+  return router_topk(s, x, w, g, topk_idx, topk_w, ws, ws_bytes, stream);
 }
 
 moe_status_t moe_permute(const moe_shape_t* s, const int32_t* topk_idx, const void* x,
@@ -423,10 +460,12 @@ moe_status_t moe_load_stats(const moe_shape_t* s, const void* x, const moe_weigh
 }
 
 static moe_status_t layer_forward(const moe_shape_t* s, const moe_weights_t* w, const void* x,
-                                  void* out, moe_routing_t* r, int32_t capacity, void* ws,
-                                  size_t ws_bytes, hipStream_t stream) {
+                                  void* out, moe_routing_t* r, int32_t capacity,
+                                  const GroupLimit& g, void* ws, size_t ws_bytes,
+                                  hipStream_t stream) {
   moe_status_t st = check_shape(s);
   if (st != MOE_OK) return st;
+  if ((st = check_groups(s, g)) != MOE_OK) return st;
   if (s->n_tokens == 0) return MOE_OK;
   if ((st = check_weights(s, w, true, true)) != MOE_OK) return st;
   if (!x || !out) return fail(MOE_ERR_INVALID_ARG, "x / out is NULL");
@@ -446,7 +485,8 @@ static moe_status_t layer_forward(const moe_shape_t* s, const moe_weights_t* w, 
   int32_t* perm = (r && r->perm_token) ? r->perm_token : wsi(capped ? L.cperm : L.perm);
   int32_t* inv = (r && r->inv_perm) ? r->inv_perm : wsi(capped ? L.cinv : L.inv);
 
-  if ((st = run_router(s, x, w, idx, gw, reinterpret_cast<float*>(b + L.logits), stream)) != MOE_OK)
+  if ((st = run_router(s, x, w, idx, gw, reinterpret_cast<float*>(b + L.logits), stream, g)) !=
+      MOE_OK)
     return st;
   if (!capped) {
     HIP_TRY("permute", launch_permute(idx, s->n_tokens, s->top_k, s->n_experts, wsi(L.hist),
@@ -471,7 +511,18 @@ static moe_status_t layer_forward(const moe_shape_t* s, const moe_weights_t* w, 
 moe_status_t moe_layer_forward(const moe_shape_t* s, const moe_weights_t* w, const void* x,
                                void* out, moe_routing_t* r, void* ws, size_t ws_bytes,
                                hipStream_t stream) {
-  return layer_forward(s, w, x, out, r, -1, ws, ws_bytes, stream);
+  return layer_forward(s, w, x, out, r, -1, GroupLimit(), ws, ws_bytes, stream);
+}
+
+moe_status_t moe_layer_forward_grouped(const moe_shape_t* s, const moe_weights_t* w,
+                                       const void* x, void* out, int32_t n_groups,
+                                       int32_t max_groups, moe_routing_t* r, void* ws,
+                                       size_t ws_bytes, hipStream_t stream) {
+  if (n_groups < 1) return fail(MOE_ERR_INVALID_ARG, "n_groups must be >= 1");
+  GroupLimit g;
+  g.n_groups = n_groups;
+  g.max_groups = max_groups;
+  return layer_forward(s, w, x, out, r, -1, g, ws, ws_bytes, stream);
 }
 
 moe_status_t moe_layer_forward_capacity(const moe_shape_t* s, const moe_weights_t* w,
@@ -479,7 +530,7 @@ moe_status_t moe_layer_forward_capacity(const moe_shape_t* s, const moe_weights_
                                         moe_routing_t* r, void* ws, size_t ws_bytes,
                                         hipStream_t stream) {
   if (capacity < 0) return fail(MOE_ERR_INVALID_ARG, "capacity is negative");
-  return layer_forward(s, w, x, out, r, capacity, ws, ws_bytes, stream);
+  return layer_forward(s, w, x, out, r, capacity, GroupLimit(), ws, ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -20,9 +20,11 @@ hipError_t launch_load_stats(const float* partial, int S, const float* offset, i
                              int N, int k, const int32_t* counts, float alpha, float step,
                              float* bp, float* frac, float* prob, float* aux, float* bias,
                              hipStream_t st);
+// gsize > 0: at most max_groups groups of gsize consecutive experts per token
 hipError_t launch_router_topk(const float* partial, int S, const float* offset,
                               const float* select_bias, int sigmoid, int T, int N, int k,
-                              int32_t* topk_idx, float* topk_w, hipStream_t st);
+                              int gsize, int max_groups, int32_t* topk_idx, float* topk_w,
+                              hipStream_t st);
 
 // Counts, offsets and the stable (expert, token) permutation.  hist is
 // scratch of permute_blocks(T) * N int32 (unused when that is 1).

@@ -263,10 +263,18 @@ __device__ __forceinline__ bool better(float s1, int i1, float s2, int i2) {
 // One wave scores and selects for one token.  Lane l holds the logits of
 // experts l + 64 j (j < NJ) in lg; on return lanes i < k hold the i-th
 // selected expert (best first, the lower index winning ties) and its gate.
+// With gsize > 0 the experts form N / gsize groups of gsize consecutive ids
+// (at most 64 groups) and a token may use at most max_groups of them: a
+// group's score is its best expert's selection score, the max_groups best
+// groups are kept (exact ties to the lower group index), and the selection
+// runs over their experts only ("Mixture of Experts for LLM Inference",
+// "Three tricks that tame the all-to-alls": node-limited routing).  gscr is
+// this wave's LDS scratch of N floats.
 template <int NJ>
 __device__ __forceinline__ void select_topk(const float (&lg)[NJ], int N, int k, int sigmoid,
-                                            const float* __restrict__ bias, int lane,
-                                            int& my_idx, float& my_w) {
+                                            const float* __restrict__ bias, int lane, int gsize,
+                                            int max_groups, float* gscr, int& my_idx,
+                                            float& my_w) {
   float sc[NJ];
   bool live[NJ];
 #pragma unroll
@@ -279,6 +287,36 @@ __device__ __forceinline__ void select_topk(const float (&lg)[NJ], int N, int k,
       if (bias && live[j]) s += bias[e];
     }
     sc[j] = s;
+  }
+  if (gsize > 0) {
+    const int G = N / gsize;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+      if (live[j]) gscr[lane + 64 * j] = sc[j];
+    __builtin_amdgcn_wave_barrier();
+    float gm = -INFINITY;
+    if (lane < G)
+      for (int e = lane * gsize; e < (lane + 1) * gsize; ++e) gm = fmaxf(gm, gscr[e]);
+    bool gl = lane < G;
+    uint64_t allowed = 0;
+    for (int r = 0; r < max_groups; ++r) {
+      float bs = gl ? gm : -INFINITY;
+      int bi = gl ? lane : 0x7fffffff;
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) {
+        const float os = __shfl_xor(bs, off);
+        const int oi = __shfl_xor(bi, off);
+        if (better(os, oi, bs, bi)) {
+          bs = os;
+          bi = oi;
+        }
+      }
+      allowed |= 1ull << bi;
+      if (lane == bi) gl = false;
+    }
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+      live[j] = live[j] && ((allowed >> ((lane + 64 * j) / gsize)) & 1ull);
   }
   float my_logit = 0.f;
   float sel_logit0 = 0.f;
@@ -332,8 +370,10 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
                                                           int S, const float* __restrict__ offset,
                                                           const float* __restrict__ bias,
                                                           int sigmoid, int T, int N, int k,
+                                                          int gsize, int max_groups,
                                                           int32_t* __restrict__ topk_idx,
                                                           float* __restrict__ topk_w) {
+  __shared__ float gscr[4][NJ * 64];
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
@@ -351,7 +391,8 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
   }
   int my_idx;
   float my_w;
-  select_topk<NJ>(lg, N, k, sigmoid, bias, lane, my_idx, my_w);
+  select_topk<NJ>(lg, N, k, sigmoid, bias, lane, gsize, max_groups, gscr[threadIdx.x >> 6],
+                  my_idx, my_w);
   if (lane < k) {
     topk_idx[(size_t)t * k + lane] = my_idx;
     topk_w[(size_t)t * k + lane] = my_w;
@@ -416,12 +457,13 @@ hipError_t launch_router_logits(const void* x, bool act_bf16, const float* w_rou
 
 hipError_t launch_router_topk(const float* partial, int S, const float* offset,
                               const float* select_bias, int sigmoid, int T, int N, int k,
-                              int32_t* topk_idx, float* topk_w, hipStream_t st) {
+                              int gsize, int max_groups, int32_t* topk_idx, float* topk_w,
+                              hipStream_t st) {
   dim3 grid(ceil_div(T, 4));
   int nj = ceil_div(N, 64);
 #define RT_CASE(NJ)                                                                  \
   router_topk_kernel<NJ><<<grid, 256, 0, st>>>(partial, S, offset, select_bias, sigmoid, T, N, \
-                                               k, topk_idx, topk_w)
+                                               k, gsize, max_groups, topk_idx, topk_w)
   if (nj <= 1) RT_CASE(1);
   else if (nj <= 2) RT_CASE(2);
   else if (nj <= 4) RT_CASE(4);

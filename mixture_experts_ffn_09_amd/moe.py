@@ -27,8 +27,8 @@ ROUTE_CODES = {"softmax": MOE_ROUTE_SOFTMAX_TOPK, "sigmoid": MOE_ROUTE_SIGMOID_B
 EXPORTS = ["moe_packed_weight_bytes", "moe_pack_weights", "moe_workspace_bytes",
            "moe_router_topk", "moe_permute", "moe_grouped_ffn", "moe_expert_gate_up",
            "moe_expert_down", "moe_combine", "moe_layer_forward", "moe_load_stats",
-           "moe_permute_capacity", "moe_layer_forward_capacity", "moe_status_string",
-           "moe_last_error"]
+           "moe_permute_capacity", "moe_layer_forward_capacity", "moe_router_topk_grouped",
+           "moe_layer_forward_grouped", "moe_status_string", "moe_last_error"]
 
 
 class MoEError(RuntimeError):
@@ -84,9 +84,14 @@ def lib() -> C.CDLL:
         L.moe_permute_capacity.argtypes = [S, P, C.c_int32, C.POINTER(Routing), P, C.c_size_t, P]
         L.moe_layer_forward_capacity.argtypes = [S, C.POINTER(Weights), P, P, C.c_int32,
                                                  C.POINTER(Routing), P, C.c_size_t, P]
+        L.moe_router_topk_grouped.argtypes = [S, P, C.POINTER(Weights), C.c_int32, C.c_int32, P, P,
+                                              P, C.c_size_t, P]
+        L.moe_layer_forward_grouped.argtypes = [S, C.POINTER(Weights), P, P, C.c_int32, C.c_int32,
+                                                C.POINTER(Routing), P, C.c_size_t, P]
         for f in ("moe_pack_weights", "moe_router_topk", "moe_permute", "moe_grouped_ffn",
                   "moe_expert_gate_up", "moe_expert_down", "moe_combine", "moe_layer_forward",
-                  "moe_load_stats", "moe_permute_capacity", "moe_layer_forward_capacity"):
+                  "moe_load_stats", "moe_permute_capacity", "moe_layer_forward_capacity",
+                  "moe_router_topk_grouped", "moe_layer_forward_grouped"):
             getattr(L, f).restype = C.c_int
         L.moe_status_string.argtypes = [C.c_int]
         L.moe_status_string.restype = C.c_char_p
@@ -234,3 +239,21 @@ def moe_layer_forward_capacity(shape: Shape, weights: Weights, x: torch.Tensor,
                                             C.c_int32(capacity),
                                             C.byref(routing) if routing is not None else None,
                                             _ptr(ws), ws.numel() * ws.element_size(), _stream()))
+
+
+def moe_router_topk_grouped(shape: Shape, x: torch.Tensor, weights: Weights, n_groups: int,
+                            max_groups: int, topk_idx: torch.Tensor, topk_w: torch.Tensor,
+                            ws: torch.Tensor):
+    _check(lib().moe_router_topk_grouped(C.byref(shape), _ptr(x), C.byref(weights),
+                                         C.c_int32(n_groups), C.c_int32(max_groups),
+                                         _ptr(topk_idx), _ptr(topk_w), _ptr(ws),
+                                         ws.numel() * ws.element_size(), _stream()))
+
+
+def moe_layer_forward_grouped(shape: Shape, weights: Weights, x: torch.Tensor, out: torch.Tensor,
+                              n_groups: int, max_groups: int, ws: torch.Tensor,
+                              routing: Optional[Routing] = None):
+    _check(lib().moe_layer_forward_grouped(C.byref(shape), C.byref(weights), _ptr(x), _ptr(out),
+                                           C.c_int32(n_groups), C.c_int32(max_groups),
+                                           C.byref(routing) if routing is not None else None,
+                                           _ptr(ws), ws.numel() * ws.element_size(), _stream()))

@@ -231,3 +231,20 @@ def test_capacity_argument_checks():
     w = moe.Weights(w_router=FAKE.value, w13=FAKE.value, w2=FAKE.value)
     assert _status("moe_layer_forward_capacity", C.byref(s), C.byref(w), FAKE,
                    C.c_void_p(0x2000), -3, None, FAKE, ws, None) == moe.MOE_ERR_INVALID_ARG
+
+
+def test_grouped_argument_checks():
+    s = shape(T=16, n_experts=256, top_k=8, d_model=7168, d_ff=2048, n_shared=1, route="sigmoid")
+    ws = C.c_size_t(moe.moe_workspace_bytes(s))
+    w = moe.Weights(w_router=FAKE.value, w13=FAKE.value, w2=FAKE.value, w13_shared=FAKE.value,
+                    w2_shared=FAKE.value)
+    call = lambda G, M: _status("moe_router_topk_grouped", C.byref(s), FAKE, C.byref(w), G, M,
+                                FAKE, FAKE, FAKE, ws, None)
+    assert call(0, 1) == moe.MOE_ERR_INVALID_ARG      # no groups
+    assert call(7, 2) == moe.MOE_ERR_INVALID_ARG      # 7 does not divide 256
+    assert call(128, 4) == moe.MOE_ERR_UNSUPPORTED    # more than 64 groups
+    assert call(8, 0) == moe.MOE_ERR_INVALID_ARG      # max_groups < 1
+    assert call(8, 9) == moe.MOE_ERR_INVALID_ARG      # max_groups > n_groups
+    assert call(64, 1) == moe.MOE_ERR_INVALID_ARG     # 4 experts per group < top_k = 8
+    assert _status("moe_layer_forward_grouped", C.byref(s), C.byref(w), FAKE, C.c_void_p(0x2000),
+                   7, 2, None, FAKE, ws, None) == moe.MOE_ERR_INVALID_ARG

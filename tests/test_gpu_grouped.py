@@ -1,0 +1,102 @@
+"""Group-limited selection on the GPU against the oracle: at most
+max_groups groups of consecutive experts per token."""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.moe_oracle as O
+from mixture_experts_ffn_09_amd import moe, workloads as W
+from mixture_experts_ffn_09_amd.layer import build_device_layer
+from tests import _harness as H
+
+pytestmark = pytest.mark.gpu
+C = W.CONFIGS
+EPS = H.TIE_EPS
+
+
+def _log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _check_grouped(scores, gpu_idx, k, G, M):
+    """Tokens without near-ties (group scores M-th vs M+1-th, expert scores
+    k-th vs k+1-th inside the kept groups, both >= EPS apart) must match the
+    oracle exactly; near-tie tokens must still be valid: at most M groups,
+    each scoring within EPS of the M-th best."""
+    ref = O.group_limited_top_k(scores, k, G, M)
+    s32 = scores.astype(np.float32).astype(np.float64)
+    T, N = s32.shape
+    gs = N // G
+    gsc = s32.reshape(T, G, gs).max(axis=2)
+    ties = 0
+    for t in range(T):
+        if set(gpu_idx[t].tolist()) == set(ref[t].tolist()):
+            continue
+        go = np.sort(gsc[t])[::-1]
+        kept = np.argsort(-gsc[t], kind="stable")[:M]
+        allowed = np.concatenate([np.arange(g * gs, (g + 1) * gs) for g in kept])
+        es = np.sort(s32[t, allowed])[::-1]
+        gap_g = go[M - 1] - go[M] if M < G else np.inf
+        gap_e = es[k - 1] - es[k] if k < len(es) else np.inf
+        assert min(gap_g, gap_e) < EPS, f"token {t}: GPU {sorted(gpu_idx[t])} vs {sorted(ref[t])}"
+        groups = set((gpu_idx[t] // gs).tolist())
+        assert len(groups) <= M and all(gsc[t, g] >= go[M - 1] - EPS for g in groups), t
+        ties += 1
+    return ref, ties
+
+
+CASES = {
+    # DeepSeek-V3 shape: 256 experts in 8 groups, at most 4 per token, top-8
+    "v3_groups8_max4": (H.small_config(C[3], 140, T=300, d_model=256, d_ff=128), 8, 4),
+    "v3_groups8_max1": (H.small_config(C[3], 141, T=64, d_model=256, d_ff=128), 8, 1),
+    "softmax_N16_G4_M2": (H.small_config(C[2], 142, T=200, d_model=256, d_ff=256, n_experts=16,
+                                         top_k=3), 4, 2),
+    "skewed_offsets_G16_M3": (H.small_config(C[4], 143, T=256, d_model=256, d_ff=256,
+                                             w_dtype="bf16"), 16, 3),
+}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_grouped_layer_against_oracle(name):
+    cfg, G, M = CASES[name]
+    _log(f"[case] grouped {name} T={cfg.T} N={cfg.n_experts} k={cfg.top_k} G={G} M={M}")
+    L = build_device_layer(cfg)
+    x = W.make_x(cfg)
+    xd = x.to("cuda")
+    rb = L.routing_buffers()
+    out = torch.empty_like(xd)
+    moe.moe_layer_forward_grouped(L.shape_for(cfg.T), L.weights, xd, out, G, M, L.workspace(),
+                                  moe.make_routing(**rb))
+    torch.cuda.synchronize()
+    g = {kk: v.cpu().numpy() for kk, v in rb.items()}
+    xo = H.x_f64(cfg, x)
+    w_r, off, bias = H.oracle_router(cfg)
+    logits = O.router_logits(xo, w_r, off)
+    scores = O.selection_scores(logits, cfg.route, bias)
+    _, ties = _check_grouped(scores, g["topk_idx"], cfg.top_k, G, M)
+    gates = O.gate_weights(logits, g["topk_idx"], cfg.route)
+    H.check_gates(g["topk_idx"], g["topk_w"], g["topk_idx"], gates)
+    H.check_permutation(g, g["topk_idx"], cfg.n_experts)
+    shared = H.oracle_expert(cfg, cfg.n_experts) if cfg.n_shared else None
+    ref, _, _, _ = O.moe_forward_with_routing(xo, g["topk_idx"], gates,
+                                              lambda e: H.oracle_expert(cfg, e),
+                                              cfg.n_experts, shared)
+    err = H.assert_close(H.to_np(out), ref, H.TOL[cfg.w_dtype])
+    _log(f"  ok: near-tie tokens {ties}, max abs err {err[0]:.3e}")
+
+
+def test_all_groups_allowed_is_the_plain_router():
+    cfg = H.small_config(C[3], 144, T=100, d_model=256, d_ff=128)
+    L = build_device_layer(cfg)
+    xd = W.make_x(cfg).to("cuda")
+    s, ws = L.shape_for(cfg.T), L.workspace()
+    a = [torch.empty(cfg.T, cfg.top_k, dtype=t, device="cuda") for t in (torch.int32, torch.float32)]
+    b = [torch.empty_like(v) for v in a]
+    moe.moe_router_topk(s, xd, L.weights, a[0], a[1], ws)
+    moe.moe_router_topk_grouped(s, xd, L.weights, 8, 8, b[0], b[1], ws)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])

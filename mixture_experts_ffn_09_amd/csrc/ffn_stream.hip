@@ -66,30 +66,13 @@ __device__ __forceinline__ void fp8_block_to_bf16(const u32x4_t& q, u32x4_t& lo,
 // the group's end are clamped to its last row: row m of an MFMA result
 // depends only on row m of A, and those rows are not stored.
 template <int MB, int NP, int D, bool FP8, bool GATED>
-__global__ __launch_bounds__(256) void ffn_stream_kernel(StreamParams p) {
+__device__ __forceinline__ void stream_body(const StreamParams& p, int nb0, int g, bool shared,
+                                            int row_base, int rows, int m_first) {
   constexpr int NH = GATED ? 2 : 1;
   constexpr int AF = FP8 ? 2 : 1;  // activation fragments per K step
   static_assert(!FP8 || D % 2 == 0, "FP8 needs an even ring depth");
   static_assert(8 % NP == 0, "the NP blocks of a wave share one 128-row scale block");
   const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int NB = p.n_out / 16;  // a multiple of NP
-  const int nb0 = (blockIdx.x * SW_WAVES + wave) * NP;
-  if (nb0 >= NB) return;
-
-  // grid rows: routed groups, then slices of the shared expert's T rows
-  const bool shared = (int)blockIdx.y >= p.n_routed;
-  const int g = shared ? p.N : p.g0 + blockIdx.y;
-  int row_base, rows, m_first = 0;
-  if (!shared) {
-    row_base = p.offsets[g];
-    rows = p.offsets[g + 1] - row_base;
-  } else {
-    row_base = 0;
-    m_first = (blockIdx.y - p.n_routed) * p.sh_rows;
-    rows = min(p.T, m_first + p.sh_rows);
-  }
-  if (rows <= m_first) return;
   uint16_t* out = shared ? p.out_sh : p.out;
 
   const size_t wbytes = (size_t)NH * p.n_out * p.K * (FP8 ? 1 : 2);
@@ -222,20 +205,57 @@ __global__ __launch_bounds__(256) void ffn_stream_kernel(StreamParams p) {
   }
 }
 
+// HOT: a routed group with more than 16 rows takes passes of 32 rows (MB =
+// 2, half the ring depth) and one with more than 32 rows passes of 64 (MB =
+// 4, a quarter of it), so the registers stay within the 16-row form's,
+// instead of streaming its weights once per 16 rows: with skewed routing a
+// few hot experts hold many of the rows (on the skewed fp8 decode workload
+// this cut the gate/up time by 12%).
+template <int MB, int NP, int D, bool FP8, bool GATED, bool HOT>
+__global__ __launch_bounds__(256) void ffn_stream_kernel(StreamParams p) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int NB = p.n_out / 16;  // a multiple of NP
+  const int nb0 = (blockIdx.x * SW_WAVES + wave) * NP;
+  if (nb0 >= NB) return;
+
+  // grid rows: routed groups, then slices of the shared expert's T rows
+  const bool shared = (int)blockIdx.y >= p.n_routed;
+  const int g = shared ? p.N : p.g0 + blockIdx.y;
+  int row_base, rows, m_first = 0;
+  if (!shared) {
+    row_base = p.offsets[g];
+    rows = p.offsets[g + 1] - row_base;
+  } else {
+    row_base = 0;
+    m_first = (blockIdx.y - p.n_routed) * p.sh_rows;
+    rows = min(p.T, m_first + p.sh_rows);
+  }
+  if (rows <= m_first) return;
+  if (HOT && !shared && rows > 32)
+    stream_body<4, NP, (D >= 8 ? D / 4 : 2), FP8, GATED>(p, nb0, g, shared, row_base, rows,
+                                                          m_first);
+  else if (HOT && !shared && rows > 16)
+    stream_body<2, NP, (D >= 4 ? D / 2 : D), FP8, GATED>(p, nb0, g, shared, row_base, rows,
+                                                          m_first);
+  else
+    stream_body<MB, NP, D, FP8, GATED>(p, nb0, g, shared, row_base, rows, m_first);
+}
+
 template <int MB, int NP, int D, bool FP8, bool GATED>
 hipError_t launch_stream_d(const StreamParams& sp, int groups, hipStream_t st) {
   // groups = grid rows (routed groups + shared slices)
   const int NW = sp.n_out / 16 / NP;  // waves per group
   dim3 grid(ceil_div(NW, SW_WAVES), groups);
-  ffn_stream_kernel<MB, NP, D, FP8, GATED><<<grid, SW_WAVES * 64, 0, st>>>(sp);
+  ffn_stream_kernel<MB, NP, D, FP8, GATED, MB == 1><<<grid, SW_WAVES * 64, 0, st>>>(sp);
   return hipGetLastError();
 }
 
-// The ring depth must divide the number of K steps; it shrinks as NP grows
-// so that a wave keeps about 8 KB of weights in flight.
+// The ring depth must divide the number of K steps; it shrinks as NP or MB
+// grow (down to 2) so that the registers of the ring stay within an
+// occupancy of two or more waves per SIMD.
 template <int MB, int NP, bool FP8, bool GATED>
 hipError_t launch_stream(const StreamParams& sp, int groups, hipStream_t st) {
-  constexpr int DMAX = 8 / NP;
+  constexpr int DMAX = 8 / (NP * MB) < 2 ? 2 : 8 / (NP * MB);
   const int KS = FP8 ? sp.K / 64 : sp.K / 32;
   if (DMAX >= 8 && KS % 8 == 0) return launch_stream_d<MB, NP, (DMAX >= 8 ? 8 : 2), FP8, GATED>(sp, groups, st);
   if (DMAX >= 4 && KS % 4 == 0) return launch_stream_d<MB, NP, (DMAX >= 4 ? 4 : 2), FP8, GATED>(sp, groups, st);
@@ -281,6 +301,7 @@ hipError_t launch_ffn_stream(const FfnArgs& a, int pass, int g0, int g1, int row
                              hipStream_t st) {
   if (g1 <= g0) return hipSuccess;
   const int mb = rows_hint <= 16 ? 1 : (rows_hint <= 32 ? 2 : 4);
+
   const bool with_shared = g1 > a.N;
   const int n_routed = (g1 > a.N ? a.N : g1) - g0;
   // the shared expert's rows are cut into slices of one pass each, run

@@ -6,9 +6,11 @@
 // A first kernel writes each block's per-expert counts (order-free LDS adds).
 // The second kernel gives every block its row bases - expert offset plus the
 // counts of earlier blocks plus those of earlier waves in the block - and
-// ranks each assignment among earlier same-expert assignments of its wave
-// with ballots over the bits of the expert id.  Every position follows from
-// counts and ballots alone, never from the order in which atomics land.
+// ranks each assignment among earlier same-expert assignments of its wave:
+// from per-expert masks of the wave's lanes (OR-ed in LDS), or, when a token
+// lists an expert twice, with ballots over the bits of the expert id.  Every
+// position follows from counts, masks and ballots alone, never from the
+// order in which atomics land.
 // With a single block the first kernel is skipped.
 
 #include "common.h"
@@ -79,9 +81,10 @@ __global__ __launch_bounds__(256) void permute_kernel(const int32_t* __restrict_
                                                       int32_t* __restrict__ offsets,
                                                       int32_t* __restrict__ perm_token,
                                                       int32_t* __restrict__ inv_perm) {
-  extern __shared__ int32_t sm[];
-  int32_t* wh = sm;                       // [PB_WAVES][N] wave counts, then wave bases
-  int32_t* tot = sm + PB_WAVES * N;       // [N] totals, then exclusive offsets
+  extern __shared__ __attribute__((aligned(8))) int32_t sm[];
+  uint64_t* msk = reinterpret_cast<uint64_t*>(sm);  // [PB_WAVES][N] lane masks per expert
+  int32_t* wh = sm + 2 * PB_WAVES * N;    // [PB_WAVES][N] wave counts, then wave bases
+  int32_t* tot = wh + PB_WAVES * N;       // [N] totals, then exclusive offsets
   int32_t* bef = tot + N;                 // [N] counts of earlier blocks
   int32_t* wtot = bef + N;                // [PB_WAVES] scan scratch
   int32_t* sid = wtot + PB_WAVES;         // [PB_TOK][k] the block's expert ids
@@ -143,6 +146,41 @@ __global__ __launch_bounds__(256) void permute_kernel(const int32_t* __restrict_
 
   // ranks within the wave's 64 tokens
   const uint64_t lt = lanemask_lt();
+  // Usual case, no token listing an expert twice: the rank of (t, i) is the
+  // number of earlier lanes whose token lists the same expert, read from a
+  // per-expert mask of lanes (LDS OR of each lane's bit; the result does not
+  // depend on the order the ORs land in).
+  bool dup = false;
+  if (tv)
+    for (int i = 1; i < k; ++i)
+      for (int i2 = 0; i2 < i; ++i2) dup |= my[i] == my[i2];
+  if (__ballot(dup) == 0) {
+    uint64_t* wm = msk + (size_t)w * N;
+    for (int e = lane; e < N; e += 64) wm[e] = 0ull;
+    __builtin_amdgcn_wave_barrier();
+    if (tv)
+      for (int i = 0; i < k; ++i) {
+        const int e = my[i];
+        if (e >= 0 && e < N) atomicOr(reinterpret_cast<unsigned long long*>(&wm[e]), 1ull << lane);
+      }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): every lane's OR has landed
+    __builtin_amdgcn_wave_barrier();
+    if (tv)
+      for (int i = 0; i < k; ++i) {
+        const int e = my[i];
+        if (e >= 0 && e < N) {
+          const int pos = wh[w * N + e] + __popcll(wm[e] & lt);
+          perm_token[pos] = t;
+          inv_perm[(size_t)t * k + i] = pos;
+        } else {
+          inv_perm[(size_t)t * k + i] = -1;
+        }
+      }
+    return;
+  }
+  // a token lists an expert twice: ranks from ballots over the bits of the
+  // expert ids, slot by slot
   for (int i = 0; i < k; ++i) {
     const int e = tv ? my[i] : -1;
     const bool ok = e >= 0 && e < N;
@@ -244,7 +282,8 @@ hipError_t launch_permute(const int32_t* topk_idx, int T, int k, int N, int32_t*
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const size_t lds = ((size_t)(PB_WAVES + 2) * N + PB_WAVES + (size_t)PB_TOK * k) * sizeof(int32_t);
+  const size_t lds =
+      ((size_t)(3 * PB_WAVES + 2) * N + PB_WAVES + (size_t)PB_TOK * k) * sizeof(int32_t);
   permute_kernel<<<nblk, 256, lds, st>>>(topk_idx, T, k, N, nbits, nblk > 1 ? hist : nullptr,
                                          nblk, counts, offsets, perm_token, inv_perm);
   return hipGetLastError();

@@ -32,23 +32,27 @@ def accounting(cfg, touched: int):
     """Algorithmic bytes and flops of each stage (each weight byte of a
     touched expert counted once; activations in and out once)."""
     T, k, N, d, f = cfg.T, cfg.top_k, cfg.n_experts, cfg.d_model, cfg.d_ff
-    wb = {"f32": 4, "bf16": 2, "fp8": 1}[cfg.w_dtype]
+    wb = {"f32": 4, "bf16": 2, "fp8": 1, "mxfp4": 0.5}[cfg.w_dtype]
     ab = 4 if cfg.act_dtype == "f32" else 2
     sh = cfg.n_shared
     rows = T * k + sh * T
     mats = touched + sh
-    sc13 = 2 * (f // 128) * (d // 128) * 4 if cfg.w_dtype == "fp8" else 0
-    sc2 = (f // 128) * (d // 128) * 4 if cfg.w_dtype == "fp8" else 0
+    if cfg.w_dtype == "fp8":      # float32 per 128x128 block
+        sc13, sc2 = 2 * (f // 128) * (d // 128) * 4, (f // 128) * (d // 128) * 4
+    elif cfg.w_dtype == "mxfp4":  # one byte per 32 inputs
+        sc13, sc2 = 2 * f * (d // 32), d * (f // 32)
+    else:
+        sc13 = sc2 = 0
     st = {
         "router": dict(bytes=T * d * ab + d * N * 4 + T * k * 8, flops=2 * T * d * N),
         "permute": dict(bytes=T * k * 4 + (2 * N + 1) * 4 + 2 * T * k * 4, flops=0),
-        "gate_up": dict(bytes=mats * (2 * f * d * wb + sc13) + rows * d * ab + rows * f * ab,
+        "gate_up": dict(bytes=int(mats * (2 * f * d * wb + sc13)) + rows * d * ab + rows * f * ab,
                         flops=2 * rows * d * 2 * f),
-        "down": dict(bytes=mats * (d * f * wb + sc2) + rows * f * ab + rows * d * ab,
+        "down": dict(bytes=int(mats * (d * f * wb + sc2)) + rows * f * ab + rows * d * ab,
                      flops=2 * rows * f * d),
         "combine": dict(bytes=rows * d * ab + T * d * ab + T * k * 8, flops=2 * T * k * d),
     }
-    layer = dict(bytes=mats * (3 * f * d * wb + sc13 + sc2) + d * N * 4 + 2 * T * d * ab,
+    layer = dict(bytes=int(mats * (3 * f * d * wb + sc13 + sc2)) + d * N * 4 + 2 * T * d * ab,
                  flops=sum(v["flops"] for v in st.values()))
     return st, layer
 
@@ -123,7 +127,7 @@ def cpu_baseline(cfg, x_cpu, n_tokens: int):
                       f"decoded from stored bits, float64 NumPy, {secs:.2f} s"}
 
 
-CPU_SAMPLE = {0: 64, 1: 16, 2: 16, 3: 4, 4: 8}
+CPU_SAMPLE = {0: 64, 1: 16, 2: 16, 3: 4, 4: 8, 5: 16}
 CPU_SECONDS = 10.0
 
 
@@ -316,7 +320,8 @@ def main():
         "metric": METRIC, "value": round(T / (ms_step * 1e-3), 2), "unit": "tokens/s",
         "n_gpus": 1, "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": {"f32": "f32", "bf16": "bf16", "fp8": "fp8-e4m3 weights, bf16 activations"}[cfg.w_dtype],
+        "dtype": {"f32": "f32", "bf16": "bf16", "fp8": "fp8-e4m3 weights, bf16 activations",
+                  "mxfp4": "mxfp4 (e2m1 + e8m0) weights, bf16 activations"}[cfg.w_dtype],
         "data": "synthetic (seeded random weights and inputs)",
         "config": {"workload": cfg.name, "T": T, "d_model": d, "n_experts": N, "top_k": k,
                    "d_ff": f, "n_shared": cfg.n_shared, "route": cfg.route,

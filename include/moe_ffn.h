@@ -28,13 +28,16 @@
  *     indices are int32.  Entry points hold no state and may be called from
  *     several host threads.
  *   - Supported types: x/out float32 or bfloat16; expert weights float32
- *     (with float32 activations), bfloat16, or OCP FP8 E4M3 with one float32
- *     scale per 128x128 block (both with bfloat16 activations).  The router
- *     weight, offset and bias are always float32.
+ *     (with float32 activations), bfloat16, OCP FP8 E4M3 with one float32
+ *     scale per 128x128 block, or MXFP4 (E2M1 codes, one E8M0 scale byte per
+ *     32 consecutive inputs; [AIS-12] "Quantize the experts first": gpt-oss
+ *     ships its experts in MXFP4) - the last three with bfloat16
+ *     activations.  The router weight, offset and bias are always float32.
  *   - Shape limits (else MOE_ERR_UNSUPPORTED): N <= 512, k <= 64;
  *     n_shared in {0,1}; bfloat16 weights need d_model % 32 == 0 and
- *     d_ff % 32 == 0; FP8 weights need d_model % 128 == 0 and
- *     d_ff % 128 == 0; bfloat16 activations need d_model % 8 == 0.
+ *     d_ff % 32 == 0; FP8 and MXFP4 weights need d_model % 128 == 0 and
+ *     d_ff % 128 == 0; bfloat16 activations need d_model % 8 == 0.  MXFP4
+ *     runs through the weight-streaming kernels at every batch size.
  *     float32 weights need n_tokens * top_k <= 1048560.  Invalid values
  *     (k < 1, k > N, negative sizes, ...) are MOE_ERR_INVALID_ARG.
  *     n_tokens == 0 is a valid no-op.
@@ -58,7 +61,7 @@ typedef enum {
   MOE_ERR_HIP = 4                  /* a HIP call failed; see last_error    */
 } moe_status_t;
 
-typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2 } moe_dtype_t;
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2, MOE_MXFP4 = 3 } moe_dtype_t;
 
 /* softmax over the top-k logits ([CH19] 19.3.2; [MoE-EXP] "The router, with
  * real numbers"), or sigmoid affinities with a selection-only per-expert
@@ -78,24 +81,28 @@ typedef struct {
                          expert?")                                         */
   int32_t route;      /* moe_route_t                                      */
   int32_t act_dtype;  /* MOE_F32 | MOE_BF16 : x, out                       */
-  int32_t w_dtype;    /* MOE_F32 | MOE_BF16 | MOE_FP8_E4M3 : expert weights */
+  int32_t w_dtype;    /* MOE_F32 | MOE_BF16 | MOE_FP8_E4M3 | MOE_MXFP4 :
+                         expert weights                                    */
 } moe_shape_t;
 
 /* Device pointers to the layer's parameters.  Expert weights are in the
  * packed layout written by moe_pack_weights(); scales stay in their natural
- * [E][rows/128][cols/128] float32 layout. */
+ * layout: FP8 float32 [E][rows/128][cols/128], MXFP4 E8M0 bytes
+ * [E][rows][cols/32] (value 2^(byte - 127)). */
 typedef struct {
   const float* w_router;     /* [d][N]                                    */
   const float* logit_offset; /* [N] added to the logits, or NULL          */
   const float* select_bias;  /* [N] selection-only bias (sigmoid), or NULL */
   const void* w13;           /* packed gate+up of the N routed experts     */
   const void* w2;            /* packed down of the N routed experts        */
-  const float* w13_scale;    /* FP8: [N][2][d_ff/128][d/128] gate, up      */
-  const float* w2_scale;     /* FP8: [N][d/128][d_ff/128]                  */
+  const void* w13_scale;     /* FP8: f32 [N][2][d_ff/128][d/128] gate, up;
+                                MXFP4: u8 [N][2][d_ff][d/32]               */
+  const void* w2_scale;      /* FP8: f32 [N][d/128][d_ff/128];
+                                MXFP4: u8 [N][d][d_ff/32]                  */
   const void* w13_shared;    /* packed gate+up of the shared expert / NULL */
   const void* w2_shared;     /* packed down of the shared expert / NULL    */
-  const float* w13_shared_scale; /* FP8 scales of the shared expert / NULL */
-  const float* w2_shared_scale;
+  const void* w13_shared_scale; /* scales of the shared expert / NULL      */
+  const void* w2_shared_scale;
 } moe_weights_t;
 
 /* Routing results (all device pointers; each may be NULL in
@@ -117,7 +124,8 @@ size_t moe_packed_weight_bytes(const moe_shape_t* s, int which, int n_mats);
  * (run once, not part of the forward).  which = 0: src_a = W_gate
  * [n_mats][d_ff][d], src_b = W_up [n_mats][d_ff][d]; which = 1: src_a =
  * W_down [n_mats][d][d_ff], src_b = NULL.  Elements are of s->w_dtype (FP8:
- * uint8 E4M3 codes).  dst must hold moe_packed_weight_bytes(s, which,
+ * uint8 E4M3 codes; MXFP4: [out][in/2] bytes of two E2M1 codes, input 2j in
+ * the low nibble).  dst must hold moe_packed_weight_bytes(s, which,
  * n_mats) bytes and must not overlap the sources.  Each expert is a
  * separately addressed block, so an unselected expert's bytes are never
  * read ([MoE-EXP] "Why heads cannot be sparsified the same way"). */

@@ -41,9 +41,12 @@ size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 int act_size(const moe_shape_t* s) { return s->act_dtype == MOE_F32 ? 4 : 2; }
 
+// bytes per weight element; 0 marks MXFP4 (two elements per byte)
 int w_size(const moe_shape_t* s) {
-  return s->w_dtype == MOE_F32 ? 4 : (s->w_dtype == MOE_BF16 ? 2 : 1);
+  return s->w_dtype == MOE_F32 ? 4 : (s->w_dtype == MOE_BF16 ? 2 : (s->w_dtype == MOE_MXFP4 ? 0 : 1));
 }
+
+bool scaled(const moe_shape_t* s) { return s->w_dtype == MOE_FP8_E4M3 || s->w_dtype == MOE_MXFP4; }
 
 moe_status_t check_shape(const moe_shape_t* s) {
   if (!s) return fail(MOE_ERR_INVALID_ARG, "shape is NULL");
@@ -57,7 +60,8 @@ moe_status_t check_shape(const moe_shape_t* s) {
     return fail(MOE_ERR_INVALID_ARG, "unknown route %d", s->route);
   if (s->act_dtype != MOE_F32 && s->act_dtype != MOE_BF16)
     return fail(MOE_ERR_INVALID_ARG, "act_dtype must be MOE_F32 or MOE_BF16");
-  if (s->w_dtype != MOE_F32 && s->w_dtype != MOE_BF16 && s->w_dtype != MOE_FP8_E4M3)
+  if (s->w_dtype != MOE_F32 && s->w_dtype != MOE_BF16 && s->w_dtype != MOE_FP8_E4M3 &&
+      s->w_dtype != MOE_MXFP4)
     return fail(MOE_ERR_INVALID_ARG, "unknown w_dtype %d", s->w_dtype);
   if (s->n_experts > kMaxExperts) return fail(MOE_ERR_UNSUPPORTED, "n_experts > %d", kMaxExperts);
   if (s->top_k > kMaxTopK) return fail(MOE_ERR_UNSUPPORTED, "top_k > %d", kMaxTopK);
@@ -67,6 +71,8 @@ moe_status_t check_shape(const moe_shape_t* s) {
     return fail(MOE_ERR_UNSUPPORTED, "bfloat16 weights need d_model %% 32 == 0 and d_ff %% 32 == 0");
   if (s->w_dtype == MOE_FP8_E4M3 && (s->d_model % 128 || s->d_ff % 128))
     return fail(MOE_ERR_UNSUPPORTED, "FP8 weights need d_model %% 128 == 0 and d_ff %% 128 == 0");
+  if (s->w_dtype == MOE_MXFP4 && (s->d_model % 128 || s->d_ff % 128))
+    return fail(MOE_ERR_UNSUPPORTED, "MXFP4 weights need d_model %% 128 == 0 and d_ff %% 128 == 0");
   const long long tk = (long long)s->n_tokens * s->top_k;
   if (tk > INT_MAX / 2) return fail(MOE_ERR_UNSUPPORTED, "n_tokens * top_k too large");
   if (s->act_dtype == MOE_F32 && (tk + 15) / 16 > 65535)
@@ -129,13 +135,13 @@ moe_status_t check_weights(const moe_shape_t* s, const moe_weights_t* w, bool ro
   }
   if (ffn) {
     if (!w->w13 || !w->w2) return fail(MOE_ERR_INVALID_ARG, "w13 / w2 is NULL");
-    if (s->w_dtype == MOE_FP8_E4M3 && (!w->w13_scale || !w->w2_scale))
-      return fail(MOE_ERR_INVALID_ARG, "FP8 weights need w13_scale and w2_scale");
+    if (scaled(s) && (!w->w13_scale || !w->w2_scale))
+      return fail(MOE_ERR_INVALID_ARG, "FP8 / MXFP4 weights need w13_scale and w2_scale");
     if (s->n_shared) {
       if (!w->w13_shared || !w->w2_shared)
         return fail(MOE_ERR_INVALID_ARG, "n_shared == 1 needs w13_shared / w2_shared");
-      if (s->w_dtype == MOE_FP8_E4M3 && (!w->w13_shared_scale || !w->w2_shared_scale))
-        return fail(MOE_ERR_INVALID_ARG, "FP8 shared expert needs its scales");
+      if (scaled(s) && (!w->w13_shared_scale || !w->w2_shared_scale))
+        return fail(MOE_ERR_INVALID_ARG, "FP8 / MXFP4 shared expert needs its scales");
     }
   }
   return MOE_OK;
@@ -214,6 +220,7 @@ moe_status_t run_ffn(const moe_shape_t* s, const void* x, const void* x_rows,
   a.d = s->d_model;
   a.d_ff = s->d_ff;
   a.fp8 = s->w_dtype == MOE_FP8_E4M3;
+  a.mxfp4 = s->w_dtype == MOE_MXFP4;
   a.sched = static_cast<int32_t*>(sched);
   a.w13 = w->w13;
   a.w2 = w->w2;
@@ -250,7 +257,8 @@ const char* moe_last_error(void) { return g_err; }
 
 size_t moe_packed_weight_bytes(const moe_shape_t* s, int which, int n_mats) {
   if (check_shape(s) != MOE_OK || (which != 0 && which != 1) || n_mats < 1) return 0;
-  const size_t per = (size_t)s->d_model * s->d_ff * w_size(s) * (which == 0 ? 2 : 1);
+  const size_t elems = (size_t)s->d_model * s->d_ff * (which == 0 ? 2 : 1);
+  const size_t per = w_size(s) ? elems * w_size(s) : elems / 2;
   return per * (size_t)n_mats;
 }
 

@@ -601,8 +601,8 @@ hipError_t launch_ffn_gemm(const FfnArgs& a, int pass, int g0, int g1, int bm, i
     p.NT = gated ? (2 * a.d_ff) / GM_BN : a.d / GM_BN;
     p.w = static_cast<const uint8_t*>(gated ? a.w13 : a.w2);
     p.w_sh = static_cast<const uint8_t*>(gated ? a.w13_sh : a.w2_sh);
-    p.s = gated ? a.s13 : a.s2;
-    p.s_sh = gated ? a.s13_sh : a.s2_sh;
+    p.s = static_cast<const float*>(gated ? a.s13 : a.s2);
+    p.s_sh = static_cast<const float*>(gated ? a.s13_sh : a.s2_sh);
     p.out = gated ? a.H : a.Y;
     p.out_sh = gated ? a.H_sh : a.Y_sh;
     tile_schedule_kernel<<<1, 1024, 0, st>>>(p, bm, const_cast<int32_t*>(p.tiles));

@@ -42,8 +42,8 @@ struct StreamParams {
   int n_out;   // output width
   const uint8_t* w;           // packed routed weights
   const uint8_t* w_sh;        // packed shared weights
-  const float* s;             // fp8 scales (routed)
-  const float* s_sh;          // fp8 scales (shared)
+  const void* s;              // fp8 (float32) or MXFP4 (E8M0 byte) scales, routed
+  const void* s_sh;           // the same, shared expert
   uint16_t* out;              // routed output rows
   uint16_t* out_sh;           // shared output rows
 };
@@ -59,31 +59,64 @@ __device__ __forceinline__ void fp8_block_to_bf16(const u32x4_t& q, u32x4_t& lo,
   hi[3] = e4m3x2_to_bf16x2<true>(q[3]);
 }
 
+// Weight formats of the streaming kernel
+constexpr int WF_BF16 = 0, WF_FP8 = 1, WF_MXFP4 = 2;
+
+// E8M0 scale byte -> float 2^(e - 127) (e = 0 is the subnormal 2^-127)
+__device__ __forceinline__ float e8m0_to_f32(uint32_t e) {
+  return __uint_as_float(e ? (e << 23) : 0x00400000u);
+}
+
+// 8 E2M1 codes (one 32-bit word, element 2i in the low nibble of byte i) ->
+// 8 bf16 = one MFMA operand, each times 2^(e - 127)
+__device__ __forceinline__ u32x4_t fp4_word_to_bf16(uint32_t q, uint32_t e) {
+  const float sc = e8m0_to_f32(e);
+  u32x4_t r;
+  r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, sc, 0));
+  r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, sc, 1));
+  r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, sc, 2));
+  r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, sc, 3));
+  return r;
+}
+
 // GATED: pass 1 (gate+up, SwiGLU) else pass 2 (down).  One wave owns NP
 // consecutive 16-row output blocks and walks K with a ring of D K-steps of
 // loads in flight (each step: NP * NH weight blocks of 1 KB plus MB
 // activation fragments, which serve all NP blocks).  Activation rows past
 // the group's end are clamped to its last row: row m of an MFMA result
 // depends only on row m of A, and those rows are not stored.
-template <int MB, int NP, int D, bool FP8, bool GATED>
+template <int MB, int NP, int D, int FMT, bool GATED>
 __device__ __forceinline__ void stream_body(const StreamParams& p, int nb0, int g, bool shared,
                                             int row_base, int rows, int m_first) {
+  constexpr bool FP8 = FMT == WF_FP8, FP4 = FMT == WF_MXFP4;
   constexpr int NH = GATED ? 2 : 1;
-  constexpr int AF = FP8 ? 2 : 1;  // activation fragments per K step
+  constexpr int AF = FP4 ? 4 : (FP8 ? 2 : 1);  // 32-wide activation fragments per K step
   static_assert(!FP8 || D % 2 == 0, "FP8 needs an even ring depth");
   static_assert(8 % NP == 0, "the NP blocks of a wave share one 128-row scale block");
   const int lane = threadIdx.x & 63;
   uint16_t* out = shared ? p.out_sh : p.out;
 
-  const size_t wbytes = (size_t)NH * p.n_out * p.K * (FP8 ? 1 : 2);
+  // bytes of one group's weights: bf16 2, fp8 1, MXFP4 1/2 per element
+  const size_t wbytes = (size_t)NH * p.n_out * p.K * (FP8 ? 2 : (FP4 ? 1 : 4)) / 2;
   const uint8_t* W = shared ? p.w_sh : p.w + (size_t)g * wbytes;
-  const int KS = FP8 ? p.K / 64 : p.K / 32;
+  const int KS = p.K / (32 * AF);                 // K steps of one 1 KB block
   const size_t bstride = (size_t)KS * NH * 1024;  // one 16-row block, all K
   const uint8_t* Wnb = W + (size_t)nb0 * bstride + lane * 16;
   const int SK = p.K / MOE_FP8_BLOCK;
   const int SR = p.n_out / MOE_FP8_BLOCK;
   const float* S = nullptr;
-  if (FP8) S = (shared ? p.s_sh : p.s + (size_t)g * NH * SR * SK) + (size_t)((nb0 * 16) / MOE_FP8_BLOCK) * SK;
+  if (FP8)
+    S = (shared ? static_cast<const float*>(p.s_sh)
+                : static_cast<const float*>(p.s) + (size_t)g * NH * SR * SK) +
+        (size_t)((nb0 * 16) / MOE_FP8_BLOCK) * SK;
+  // MXFP4: one E8M0 byte per 32 inputs of a row, [NH][n_out][K/32] per
+  // group; a lane reads the 4 bytes of its row for one 128-wide step
+  const int SK32 = p.K / 32;
+  const uint8_t* S4 = nullptr;
+  if (FP4)
+    S4 = (shared ? static_cast<const uint8_t*>(p.s_sh)
+                 : static_cast<const uint8_t*>(p.s) + (size_t)g * NH * p.n_out * SK32) +
+         (size_t)(nb0 * 16 + (lane & 15)) * SK32;
 
   const int lrow = lane & 15;
   const int lk = (lane >> 4) * 8;
@@ -117,13 +150,18 @@ __device__ __forceinline__ void stream_body(const StreamParams& p, int nb0, int 
 
     u32x4_t bq[D][NP][NH];
     u32x4_t aq[D][MB][AF];
+    uint32_t sq[FP4 ? D : 1][NP][NH];
     auto load_step = [&](int u, int ks) {
 #pragma unroll
       for (int j = 0; j < NP; ++j)
 #pragma unroll
-        for (int h = 0; h < NH; ++h)
+        for (int h = 0; h < NH; ++h) {
           bq[u][j][h] =
               *reinterpret_cast<const u32x4_t*>(Wnb + j * bstride + ((size_t)ks * NH + h) * 1024);
+          if (FP4)
+            sq[FP4 ? u : 0][j][h] = *reinterpret_cast<const uint32_t*>(
+                S4 + ((size_t)h * p.n_out + j * 16) * SK32 + ks * 4);
+        }
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -139,7 +177,22 @@ __device__ __forceinline__ void stream_body(const StreamParams& p, int nb0, int 
 #pragma unroll
       for (int u = 0; u < D; ++u) {
         const int ks = ks0 + u;  // KS is a multiple of D: no bounds branch
-        if (!FP8) {
+        if (FP4) {
+          // four 32-wide K steps per block: word s4 of a lane's 16 bytes holds
+          // its 8 codes of step s4, decoded with the step's scale straight to
+          // bf16 (a power of two times an E2M1 value is exact in bf16)
+#pragma unroll
+          for (int j = 0; j < NP; ++j)
+#pragma unroll
+            for (int h = 0; h < NH; ++h)
+#pragma unroll
+              for (int s4 = 0; s4 < 4; ++s4) {
+                const u32x4_t b = fp4_word_to_bf16(bq[u][j][h][s4], (sq[FP4 ? u : 0][j][h] >> (8 * s4)) & 0xffu);
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb)
+                  acc[j][h][mb] = mfma16x16x32(aq[u][mb][s4], b, acc[j][h][mb]);
+              }
+        } else if (!FP8) {
 #pragma unroll
           for (int j = 0; j < NP; ++j)
 #pragma unroll
@@ -211,7 +264,7 @@ __device__ __forceinline__ void stream_body(const StreamParams& p, int nb0, int 
 // instead of streaming its weights once per 16 rows: with skewed routing a
 // few hot experts hold many of the rows (on the skewed fp8 decode workload
 // this cut the gate/up time by 12%).
-template <int MB, int NP, int D, bool FP8, bool GATED, bool HOT>
+template <int MB, int NP, int D, int FMT, bool GATED, bool HOT>
 __global__ __launch_bounds__(256) void ffn_stream_kernel(StreamParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int NB = p.n_out / 16;  // a multiple of NP
@@ -232,36 +285,41 @@ __global__ __launch_bounds__(256) void ffn_stream_kernel(StreamParams p) {
   }
   if (rows <= m_first) return;
   if (HOT && !shared && rows > 32)
-    stream_body<4, NP, (D >= 8 ? D / 4 : 2), FP8, GATED>(p, nb0, g, shared, row_base, rows,
+    stream_body<4, NP, (D >= 8 ? D / 4 : 2), FMT, GATED>(p, nb0, g, shared, row_base, rows,
                                                           m_first);
   else if (HOT && !shared && rows > 16)
-    stream_body<2, NP, (D >= 4 ? D / 2 : D), FP8, GATED>(p, nb0, g, shared, row_base, rows,
+    stream_body<2, NP, (D >= 4 ? D / 2 : D), FMT, GATED>(p, nb0, g, shared, row_base, rows,
                                                           m_first);
   else
-    stream_body<MB, NP, D, FP8, GATED>(p, nb0, g, shared, row_base, rows, m_first);
+    stream_body<MB, NP, D, FMT, GATED>(p, nb0, g, shared, row_base, rows, m_first);
 }
 
-template <int MB, int NP, int D, bool FP8, bool GATED>
+template <int MB, int NP, int D, int FMT, bool GATED>
 hipError_t launch_stream_d(const StreamParams& sp, int groups, hipStream_t st) {
   // groups = grid rows (routed groups + shared slices)
   const int NW = sp.n_out / 16 / NP;  // waves per group
   dim3 grid(ceil_div(NW, SW_WAVES), groups);
-  ffn_stream_kernel<MB, NP, D, FP8, GATED, MB == 1><<<grid, SW_WAVES * 64, 0, st>>>(sp);
+  // the per-group 32- and 64-row passes need the 16-row form's register room;
+  // the MXFP4 form (four activation fragments per step) has none to spare
+  constexpr bool HOT = MB == 1 && FMT != WF_MXFP4;
+  ffn_stream_kernel<MB, NP, D, FMT, GATED, HOT><<<grid, SW_WAVES * 64, 0, st>>>(sp);
   return hipGetLastError();
 }
 
 // The ring depth must divide the number of K steps; it shrinks as NP or MB
 // grow (down to 2) so that the registers of the ring stay within an
-// occupancy of two or more waves per SIMD.
-template <int MB, int NP, bool FP8, bool GATED>
+// occupancy of two or more waves per SIMD.  An MXFP4 step carries four
+// activation fragments, so its ring is half as deep.
+template <int MB, int NP, int FMT, bool GATED>
 hipError_t launch_stream(const StreamParams& sp, int groups, hipStream_t st) {
-  constexpr int DMAX = 8 / (NP * MB) < 2 ? 2 : 8 / (NP * MB);
-  const int KS = FP8 ? sp.K / 64 : sp.K / 32;
-  if (DMAX >= 8 && KS % 8 == 0) return launch_stream_d<MB, NP, (DMAX >= 8 ? 8 : 2), FP8, GATED>(sp, groups, st);
-  if (DMAX >= 4 && KS % 4 == 0) return launch_stream_d<MB, NP, (DMAX >= 4 ? 4 : 2), FP8, GATED>(sp, groups, st);
-  if (KS % 2 == 0) return launch_stream_d<MB, NP, 2, FP8, GATED>(sp, groups, st);
+  constexpr int DR = (FMT == WF_MXFP4 ? 4 : 8) / (NP * MB);
+  constexpr int DMAX = DR < 2 ? 2 : DR;
+  const int KS = sp.K / (FMT == WF_MXFP4 ? 128 : (FMT == WF_FP8 ? 64 : 32));
+  if (DMAX >= 8 && KS % 8 == 0) return launch_stream_d<MB, NP, (DMAX >= 8 ? 8 : 2), FMT, GATED>(sp, groups, st);
+  if (DMAX >= 4 && KS % 4 == 0) return launch_stream_d<MB, NP, (DMAX >= 4 ? 4 : 2), FMT, GATED>(sp, groups, st);
+  if (KS % 2 == 0) return launch_stream_d<MB, NP, 2, FMT, GATED>(sp, groups, st);
   // FP8 K is a multiple of 128, so KS is even there
-  return launch_stream_d<MB, NP, (FP8 ? 2 : 1), FP8, GATED>(sp, groups, st);
+  return launch_stream_d<MB, NP, (FMT == WF_FP8 ? 2 : 1), FMT, GATED>(sp, groups, st);
 }
 
 // Weight blocks per wave.  The activation fragments of a K step are loaded
@@ -272,35 +330,39 @@ hipError_t launch_stream(const StreamParams& sp, int groups, hipStream_t st) {
 // on the 7168 x 2048 fp8 down projection; four blocks, with the ring depth
 // halved again, reach only 60%).  Everywhere else one block per wave with
 // the deepest ring measured fastest.
-int stream_np(bool fp8, bool gated, int n_out) {
+int stream_np(int fmt, bool gated, int n_out) {
   const int NB = n_out / 16;
-  int np = (fp8 && !gated) ? 2 : 1;
+  int np = (fmt == WF_FP8 && !gated) ? 2 : 1;
   while (np > 1 && NB % np) np >>= 1;
   return np;
 }
 
 }  // namespace
 
+template <int MB, int FMT>
+static hipError_t stream_pass_fmt(bool gated, const StreamParams& sp, int groups,
+                                  hipStream_t st) {
+  const int np = stream_np(FMT, gated, sp.n_out);
+  if (np == 2)
+    return gated ? launch_stream<MB, 2, FMT, true>(sp, groups, st)
+                 : launch_stream<MB, 2, FMT, false>(sp, groups, st);
+  return gated ? launch_stream<MB, 1, FMT, true>(sp, groups, st)
+               : launch_stream<MB, 1, FMT, false>(sp, groups, st);
+}
+
 template <int MB>
-static hipError_t stream_pass(bool fp8, bool gated, const StreamParams& sp, int groups,
+static hipError_t stream_pass(int fmt, bool gated, const StreamParams& sp, int groups,
                               hipStream_t st) {
-  const int np = stream_np(fp8, gated, sp.n_out);
-#define SP_CASE(NP)                                                                 \
-  if (np == NP)                                                                     \
-    return fp8 ? (gated ? launch_stream<MB, NP, true, true>(sp, groups, st)        \
-                        : launch_stream<MB, NP, true, false>(sp, groups, st))      \
-               : (gated ? launch_stream<MB, NP, false, true>(sp, groups, st)       \
-                        : launch_stream<MB, NP, false, false>(sp, groups, st));
-  SP_CASE(2)
-  SP_CASE(1)
-#undef SP_CASE
-  return hipErrorInvalidValue;
+  if (fmt == WF_FP8) return stream_pass_fmt<MB, WF_FP8>(gated, sp, groups, st);
+  if (fmt == WF_MXFP4) return stream_pass_fmt<MB, WF_MXFP4>(gated, sp, groups, st);
+  return stream_pass_fmt<MB, WF_BF16>(gated, sp, groups, st);
 }
 
 hipError_t launch_ffn_stream(const FfnArgs& a, int pass, int g0, int g1, int rows_hint,
                              hipStream_t st) {
   if (g1 <= g0) return hipSuccess;
   const int mb = rows_hint <= 16 ? 1 : (rows_hint <= 32 ? 2 : 4);
+  const int fmt = a.fp8 ? WF_FP8 : (a.mxfp4 ? WF_MXFP4 : WF_BF16);
 
   const bool with_shared = g1 > a.N;
   const int n_routed = (g1 > a.N ? a.N : g1) - g0;
@@ -347,17 +409,19 @@ hipError_t launch_ffn_stream(const FfnArgs& a, int pass, int g0, int g1, int row
     if (!(pass & ps)) continue;
     const StreamParams& sp = ps == 1 ? up : dn;
     if (mb == 1)
-      e = stream_pass<1>(a.fp8, ps == 1, sp, groups, st);
+      e = stream_pass<1>(fmt, ps == 1, sp, groups, st);
     else if (mb == 2)
-      e = stream_pass<2>(a.fp8, ps == 1, sp, groups, st);
+      e = stream_pass<2>(fmt, ps == 1, sp, groups, st);
     else
-      e = stream_pass<4>(a.fp8, ps == 1, sp, groups, st);
+      e = stream_pass<4>(fmt, ps == 1, sp, groups, st);
   }
   return e;
 }
 
 hipError_t launch_ffn_lowp(const FfnArgs& a, int pass, hipStream_t st) {
-  const bool gemm_ok = gemm_shape_ok(a.d, a.d_ff);
+  // MXFP4 weights run through the streaming kernel at every size (the
+  // tiled GEMM has no E2M1 operand path)
+  const bool gemm_ok = gemm_shape_ok(a.d, a.d_ff) && !a.mxfp4;
   const int avg = (int)(((long long)a.T * a.k + a.N - 1) / a.N);  // rows per routed expert
   const bool routed_gemm = gemm_ok && avg >= 64;
   // the shared expert joins a routed streaming launch up to a few hundred

@@ -53,16 +53,17 @@ struct FfnArgs {
   const uint16_t* x_sh;
   const int32_t* offsets;
   int T, k, N, n_shared, d, d_ff;
-  bool fp8;
+  bool fp8;                   // OCP E4M3 weights, float32 scale per 128x128 block
+  bool mxfp4;                 // E2M1 weights, E8M0 scale byte per 32 inputs
   int32_t* sched;             // 2048 int32 of scratch for the GEMM tile schedule
   const void* w13;
   const void* w2;
-  const float* s13;
-  const float* s2;
+  const void* s13;
+  const void* s2;
   const void* w13_sh;
   const void* w2_sh;
-  const float* s13_sh;
-  const float* s2_sh;
+  const void* s13_sh;
+  const void* s2_sh;
   uint16_t* H;
   uint16_t* H_sh;
   uint16_t* Y;

@@ -2,9 +2,11 @@
 // streaming kernels' block layout.
 //
 // A block covers 16 output rows and one K step (32 inputs for bf16, 64 for
-// FP8) and is 1 KB: 64 lanes x 16 bytes, lane l holding row l % 16 and the
-// 8 (bf16) or 2 x 8 (FP8: k-steps 2s and 2s+1 of 32) consecutive inputs
-// starting at 8 * (l / 16) - exactly its MFMA B operand.  Blocks are ordered
+// FP8, 128 for MXFP4) and is 1 KB: 64 lanes x 16 bytes, lane l holding row
+// l % 16 and the 8 (bf16), 2 x 8 (FP8: k-steps 2s and 2s+1 of 32) or 4 x 8
+// (MXFP4: k-steps 4s .. 4s+3, 4 bytes each) consecutive inputs starting at
+// 8 * (l / 16) - exactly its MFMA B operand(s).  MXFP4 scales keep their
+// natural [out][in/32] layout.  Blocks are ordered
 // (expert, row block, K step, matrix) with matrix = gate, up for the fused
 // gate/up weight, so one row block's stream along K is contiguous.
 
@@ -22,17 +24,26 @@ __global__ __launch_bounds__(256) void pack_kernel(const uint8_t* __restrict__ a
   if (c >= total_chunks) return;
   const int lane = (int)(c & 63);
   size_t blk = c >> 6;
-  const int ksteps = esize == 2 ? cols / 32 : cols / 64;
+  const int ksteps = esize == 2 ? cols / 32 : (esize == 1 ? cols / 64 : cols / 128);
   const int h = (int)(blk % nh);
   blk /= nh;
   const int ks = (int)(blk % ksteps);
   blk /= ksteps;
   const int nb = (int)(blk % (rows / 16));
   const size_t e = blk / (rows / 16);
-  const uint8_t* src = (h ? b : a) + e * (size_t)rows * cols * esize;
+  // bytes per matrix: esize 0 marks MXFP4 (two codes per byte)
+  const size_t mat_bytes = esize ? (size_t)rows * cols * esize : (size_t)rows * cols / 2;
+  const uint8_t* src = (h ? b : a) + e * mat_bytes;
   const int row = nb * 16 + (lane & 15);
   uint8_t* out = dst + c * 16;
-  if (esize == 2) {
+  if (esize == 0) {
+    // 4 steps of 32 inputs: word s holds the lane's 8 codes of step s
+    const int col = ks * 128 + (lane >> 4) * 8;
+    const uint8_t* s = src + (size_t)row * (cols / 2) + col / 2;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      *reinterpret_cast<uint32_t*>(out + 4 * q) = *reinterpret_cast<const uint32_t*>(s + 16 * q);
+  } else if (esize == 2) {
     const int col = ks * 32 + (lane >> 4) * 8;
     *reinterpret_cast<uint4*>(out) =
         *reinterpret_cast<const uint4*>(src + ((size_t)row * cols + col) * 2);
@@ -49,7 +60,8 @@ __global__ __launch_bounds__(256) void pack_kernel(const uint8_t* __restrict__ a
 hipError_t launch_pack(const void* src_a, const void* src_b, void* dst, int n_mats, int rows,
                        int cols, int esize, hipStream_t st) {
   const int nh = src_b ? 2 : 1;
-  const size_t bytes = (size_t)n_mats * nh * rows * cols * esize;
+  const size_t bytes = esize ? (size_t)n_mats * nh * rows * cols * esize
+                             : (size_t)n_mats * nh * rows * cols / 2;
   if (esize == 4) {
     // float32 weights keep the natural layout: gate block then up block
     const size_t one = (size_t)rows * cols * 4;

@@ -74,17 +74,24 @@ def build_device_layer(cfg: MoEConfig, threads: int = 16) -> DeviceLayer:
     t["w13"] = torch.empty(N * b13, dtype=torch.uint8, device=dev)
     t["w2"] = torch.empty(N * b2, dtype=torch.uint8, device=dev)
     fp8 = cfg.w_dtype == "fp8"
-    if fp8:
+    scaled = cfg.w_dtype in ("fp8", "mxfp4")
+    if fp8:   # float32 per 128x128 block
         sr13 = 2 * (cfg.d_ff // 128) * (cfg.d_model // 128)
         sr2 = (cfg.d_model // 128) * (cfg.d_ff // 128)
-        t["w13_scale"] = torch.empty(N * sr13, dtype=torch.float32, device=dev)
-        t["w2_scale"] = torch.empty(N * sr2, dtype=torch.float32, device=dev)
+        sdt = torch.float32
+    else:     # MXFP4: one E8M0 byte per 32 inputs of a row
+        sr13 = 2 * cfg.d_ff * (cfg.d_model // 32)
+        sr2 = cfg.d_model * (cfg.d_ff // 32)
+        sdt = torch.uint8
+    if scaled:
+        t["w13_scale"] = torch.empty(N * sr13, dtype=sdt, device=dev)
+        t["w2_scale"] = torch.empty(N * sr2, dtype=sdt, device=dev)
     if cfg.n_shared:
         t["w13_shared"] = torch.empty(b13, dtype=torch.uint8, device=dev)
         t["w2_shared"] = torch.empty(b2, dtype=torch.uint8, device=dev)
-        if fp8:
-            t["w13_shared_scale"] = torch.empty(sr13, dtype=torch.float32, device=dev)
-            t["w2_shared_scale"] = torch.empty(sr2, dtype=torch.float32, device=dev)
+        if scaled:
+            t["w13_shared_scale"] = torch.empty(sr13, dtype=sdt, device=dev)
+            t["w2_shared_scale"] = torch.empty(sr2, dtype=sdt, device=dev)
 
     def upload(e, w):
         shared = e == N
@@ -95,7 +102,7 @@ def build_device_layer(cfg: MoEConfig, threads: int = 16) -> DeviceLayer:
         dst2 = t["w2_shared"] if shared else t["w2"][e * b2:(e + 1) * b2]
         moe.moe_pack_weights(one, 0, 1, g, u, dst13)
         moe.moe_pack_weights(one, 1, 1, dn, None, dst2)
-        if fp8:
+        if scaled:
             s13 = torch.cat([w["gate_scale"].reshape(-1), w["up_scale"].reshape(-1)]).to(dev)
             s2 = w["down_scale"].reshape(-1).to(dev)
             if shared:

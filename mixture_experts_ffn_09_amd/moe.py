@@ -18,10 +18,10 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("MOE_FFN_LIB", os.path.join(_HERE, "libmoe_ffn.so"))
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE_TOO_SMALL, MOE_ERR_HIP = range(5)
-MOE_F32, MOE_BF16, MOE_FP8_E4M3 = range(3)
+MOE_F32, MOE_BF16, MOE_FP8_E4M3, MOE_MXFP4 = range(4)
 MOE_ROUTE_SOFTMAX_TOPK, MOE_ROUTE_SIGMOID_BIAS = range(2)
 
-DTYPE_CODES = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8": MOE_FP8_E4M3}
+DTYPE_CODES = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8": MOE_FP8_E4M3, "mxfp4": MOE_MXFP4}
 ROUTE_CODES = {"softmax": MOE_ROUTE_SOFTMAX_TOPK, "sigmoid": MOE_ROUTE_SIGMOID_BIAS}
 
 EXPORTS = ["moe_packed_weight_bytes", "moe_pack_weights", "moe_workspace_bytes",

@@ -60,7 +60,7 @@ class MoEConfig:
     route: str           # "softmax" | "sigmoid"
     n_shared: int        # 0 or 1
     act_dtype: str       # "f32" | "bf16"  (x and out)
-    w_dtype: str         # "f32" | "bf16" | "fp8"
+    w_dtype: str         # "f32" | "bf16" | "fp8" | "mxfp4"
     select_bias: bool    # U(-0.1, 0.1) selection-only bias (sigmoid router)
     zipf_c: Optional[float] = None  # router offset -c*ln(rank)
 
@@ -74,6 +74,9 @@ CONFIGS = [
     MoEConfig(2, "mixtral-prefill", 8192, 4096, 8, 2, 14336, "softmax", 0, "bf16", "bf16", False),
     MoEConfig(3, "dsv3-prefill", 4096, 7168, 256, 8, 2048, "sigmoid", 1, "bf16", "bf16", True),
     MoEConfig(4, "dsv3-decode-fp8", 256, 7168, 256, 8, 2048, "sigmoid", 1, "bf16", "fp8", True, 0.25),
+    # the Mixtral decode shape with its experts in MXFP4
+    MoEConfig(5, "mixtral-decode-mxfp4", 16, 4096, 8, 2, 14336, "softmax", 0, "bf16", "mxfp4",
+              False),
 ]
 
 
@@ -109,6 +112,32 @@ def quantize_fp8_block(w: torch.Tensor):
     return q.view(torch.uint8).contiguous(), scale.float().contiguous()
 
 
+MX_BLOCK = 32
+_FP4_GRID = torch.tensor([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+
+def quantize_mxfp4(w: torch.Tensor):
+    """float32 [R][C] (C % 32 == 0) -> (packed E2M1 codes uint8 [R][C/2],
+    element 2j in the low nibble; E8M0 scales uint8 [R][C/32]).  Data
+    preparation only: per 32-element block the shared exponent is
+    floor(log2(amax)) - 2 (the largest E2M1 magnitude is 1.5 * 2^2), values
+    are divided by 2^exponent and rounded to the nearest E2M1 value (ties to
+    the even code), saturating at 6."""
+    R, C = w.shape
+    b = w.float().reshape(R, C // MX_BLOCK, MX_BLOCK)
+    amax = b.abs().amax(dim=2)
+    ex = torch.where(amax > 0, torch.floor(torch.log2(amax)) - 2, torch.full_like(amax, -127.0))
+    ex = ex.clamp(-127, 127)
+    v = (b / torch.exp2(ex)[..., None]).clamp(-6.0, 6.0)
+    diff = (v.abs()[..., None] - _FP4_GRID).abs()
+    best = diff == diff.min(dim=-1, keepdim=True).values
+    pref = best.to(torch.int32) * (2 - torch.arange(8) % 2)  # ties: even code
+    mag = pref.argmax(dim=-1).to(torch.uint8)
+    codes = (mag | torch.where(v < 0, 8, 0).to(torch.uint8)).reshape(R, C)
+    packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).contiguous()
+    return packed, (ex + 127).to(torch.uint8).contiguous()
+
+
 def make_x(cfg: MoEConfig) -> torch.Tensor:
     """Token hidden states [T][d] in the activation storage type."""
     x = torch.randn(cfg.T, cfg.d_model, generator=_gen(seed_for(cfg, TID_X)))
@@ -136,7 +165,8 @@ def make_expert(cfg: MoEConfig, e: int) -> Dict[str, torch.Tensor]:
 
     e in [0, N) is a routed expert, e == N the shared expert.  Keys: gate
     [d_ff][d], up [d_ff][d], down [d][d_ff]; for fp8 also gate_scale,
-    up_scale, down_scale (float32 per 128x128 block).
+    up_scale, down_scale (float32 per 128x128 block); for mxfp4 the matrices
+    are packed codes [out][in/2] and the scales E8M0 bytes [out][in/32].
     """
     d, f = cfg.d_model, cfg.d_ff
     out = {}
@@ -147,6 +177,9 @@ def make_expert(cfg: MoEConfig, e: int) -> Dict[str, torch.Tensor]:
         w.mul_(1.0 / math.sqrt(fan_in))
         if cfg.w_dtype == "fp8":
             q, s = quantize_fp8_block(w)
+            out[key], out[key + "_scale"] = q, s
+        elif cfg.w_dtype == "mxfp4":
+            q, s = quantize_mxfp4(w)
             out[key], out[key + "_scale"] = q, s
         else:
             out[key] = _to_storage(w, cfg.w_dtype)
@@ -172,6 +205,8 @@ def for_each_expert(cfg: MoEConfig, fn, experts=None, threads: int = 16):
 def storage_bytes_per_expert(cfg: MoEConfig) -> int:
     """Bytes of one expert's three matrices (plus FP8 scales)."""
     n = 3 * cfg.d_ff * cfg.d_model
+    if cfg.w_dtype == "mxfp4":
+        return n // 2 + n // MX_BLOCK
     if cfg.w_dtype == "fp8":
         nb = 3 * (-(-cfg.d_ff // FP8_BLOCK)) * (-(-cfg.d_model // FP8_BLOCK))
         return n + 4 * nb

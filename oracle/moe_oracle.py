@@ -48,6 +48,7 @@ import numpy as np
 
 __all__ = [
     "bf16_bits_to_f64", "e4m3_bits_to_f64", "dequant_fp8_block",
+    "e2m1_bits_to_f64", "e8m0_bits_to_f64", "dequant_mxfp4",
     "router_logits", "sigmoid", "selection_scores", "top_k_select",
     "gate_weights", "Routing", "route_tokens",
     "expert_counts", "expert_offsets", "Permutation", "permute_assignments",
@@ -63,6 +64,10 @@ PARITY_PINS = {
     "bf16_bits_to_f64": "exhaustive 65536 codes vs torch bfloat16 -> float",
     "e4m3_bits_to_f64": "exhaustive 256 codes vs torch float8_e4m3fn -> float",
     "dequant_fp8_block": "hand-built blocks with known scales; brute force",
+    "e8m0_bits_to_f64": "exhaustive 256 codes vs torch float8_e8m0fnu",
+    "e2m1_bits_to_f64": "all 16 codes re-encoded bit by bit as E4M3 and read "
+        "with the (torch-pinned) E4M3 decoder; the format's magnitude list",
+    "dequant_mxfp4": "pure-Python nibble loop; hand-built blocks",
     "router_logits": "pure-Python triple loop on tiny inputs",
     "top_k_select / gate_weights (softmax)": "page worked examples "
         "([MoE-EXP] router with real numbers; [AIS-12] worked example); "
@@ -138,6 +143,41 @@ _E4M3 = _e4m3_table()
 def e4m3_bits_to_f64(bits: np.ndarray) -> np.ndarray:
     """OCP FP8 E4M3 bit patterns (uint8) -> float64 (table from the format)."""
     return _E4M3[np.asarray(bits).astype(np.uint8)]
+
+
+def e2m1_bits_to_f64(codes: np.ndarray) -> np.ndarray:
+    """FP4 E2M1 codes (0..15) -> float64, from the format's definition: 1 sign
+    bit, 2 exponent bits with bias 1, 1 mantissa bit; exponent field 0 is
+    subnormal (m/2).  Magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6; no inf or NaN.
+    The MX element format of expert weights in MXFP4 ([AIS-12] "Quantize the
+    experts first": gpt-oss ships its experts in MXFP4; the format itself is
+    the OCP microscaling one)."""
+    c = np.asarray(codes).astype(np.int64) & 0xF
+    s = np.where(c & 0x8, -1.0, 1.0)
+    e = (c >> 1) & 0x3
+    m = (c & 0x1).astype(np.float64)
+    mag = np.where(e == 0, m * 0.5, (1.0 + m / 2.0) * np.exp2(e - 1.0))
+    return s * mag
+
+
+def e8m0_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """E8M0 shared scales (uint8) -> float64: 2^(e - 127), e = 255 is NaN."""
+    e = np.asarray(bits).astype(np.int64)
+    with np.errstate(invalid="ignore"):
+        return np.where(e == 255, math.nan, np.exp2(e - 127.0))
+
+
+def dequant_mxfp4(packed: np.ndarray, scales: np.ndarray, block: int = 32) -> np.ndarray:
+    """MXFP4 weight [out][in] -> float64: packed holds two E2M1 codes per byte
+    ([out][in/2], element 2j in the low nibble), scales one E8M0 per 32
+    consecutive elements of a row ([out][in/32]); w = e2m1 * 2^(e - 127)."""
+    p = np.asarray(packed).astype(np.uint8)
+    out, half = p.shape
+    codes = np.empty((out, 2 * half), dtype=np.uint8)
+    codes[:, 0::2] = p & 0xF
+    codes[:, 1::2] = p >> 4
+    sc = e8m0_bits_to_f64(scales)
+    return e2m1_bits_to_f64(codes) * np.repeat(sc, block, axis=1)
 
 
 def dequant_fp8_block(q_bits: np.ndarray, scales: np.ndarray,

@@ -20,7 +20,7 @@ import oracle.moe_oracle as O
 from mixture_experts_ffn_09_amd import workloads as W
 
 TIE_EPS = 1e-5
-TOL = {"bf16": 2e-2, "fp8": 6e-2, "f32": 2e-2}
+TOL = {"bf16": 2e-2, "fp8": 6e-2, "f32": 2e-2, "mxfp4": 2e-2}
 TOL_F32_INTERNAL = 1e-4
 
 
@@ -43,6 +43,8 @@ def decode_weight(cfg: W.MoEConfig, w: dict, key: str) -> np.ndarray:
         return w[key].double().numpy()
     if cfg.w_dtype == "bf16":
         return O.bf16_bits_to_f64(bits16(w[key]))
+    if cfg.w_dtype == "mxfp4":
+        return O.dequant_mxfp4(w[key].numpy(), w[key + "_scale"].numpy())
     return O.dequant_fp8_block(bits8(w[key]), w[key + "_scale"].numpy())
 
 

@@ -47,6 +47,14 @@ SMALL = {
     "decode_sigmoid_T16": H.small_config(C[4], 112, T=16, d_model=128, n_experts=8, top_k=3,
                                          d_ff=128, w_dtype="bf16"),
     "decode_f32_N7": H.small_config(C[0], 113, T=11, d_model=96, n_experts=7, top_k=2),
+    # MXFP4 expert weights (E2M1 codes, E8M0 scale per 32 inputs): decode,
+    # 256 experts + shared with the sigmoid router, and many rows per expert
+    # (streaming passes of 64 rows)
+    "mxfp4_decode": H.small_config(C[1], 150, T=16, d_model=512, d_ff=1024, w_dtype="mxfp4"),
+    "mxfp4_sigmoid_shared": H.small_config(C[3], 151, T=40, d_model=256, d_ff=256,
+                                           w_dtype="mxfp4"),
+    "mxfp4_many_rows": H.small_config(C[2], 152, T=300, d_model=256, d_ff=256, n_experts=4,
+                                      w_dtype="mxfp4"),
 }
 
 

@@ -527,6 +527,52 @@ def pin_group_limited_selection():
         bf = B.group_limited(sc.tolist(), k, G, M)
         assert got.tolist() == bf, (G, M)
 
+
+# ---------------------------------------------------------------------------
+# MXFP4 weights
+# ---------------------------------------------------------------------------
+
+def pin_e8m0_decoder():
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e8m0fnu).double().numpy()
+    got = O.e8m0_bits_to_f64(codes)
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    assert np.array_equal(got[~np.isnan(got)], ref[~np.isnan(ref)])
+
+
+def pin_e2m1_decoder():
+    """Every E2M1 value is an E4M3 value: sign kept, exponent field rebiased
+    (bias 1 -> 7; the subnormal 0.5 is E4M3 exponent field 6), the mantissa
+    bit moved to the top of the 3-bit field.  Decoded through the E4M3 table
+    (itself pinned against torch) the 16 codes must agree."""
+    got = O.e2m1_bits_to_f64(np.arange(16))
+    for c in range(16):
+        s, e, m = c >> 3, (c >> 1) & 3, c & 1
+        if e == 0 and m == 0:
+            e4 = 0
+        elif e == 0:
+            e4 = (s << 7) | (6 << 3)
+        else:
+            e4 = (s << 7) | ((e - 1 + 7) << 3) | (m << 2)
+        ref = float(O.e4m3_bits_to_f64(np.array([e4], np.uint8))[0])
+        assert got[c] == ref or (c == 8 and got[c] == 0.0), (c, got[c], ref)
+    assert sorted(set(abs(v) for v in got)) == [0, 0.5, 1, 1.5, 2, 3, 4, 6]
+
+
+def pin_mxfp4_dequant():
+    rng = np.random.default_rng(51)
+    out, inn = 3, 96
+    packed = rng.integers(0, 256, (out, inn // 2), dtype=np.uint8)
+    scales = rng.integers(115, 135, (out, inn // 32), dtype=np.uint8)
+    got = O.dequant_mxfp4(packed, scales)
+    mags = [0, 0.5, 1, 1.5, 2, 3, 4, 6]
+    for r in range(out):
+        for c in range(inn):
+            byte = int(packed[r, c // 2])
+            code = byte & 0xF if c % 2 == 0 else byte >> 4
+            v = (-1 if code & 8 else 1) * mags[code & 7] * 2.0 ** (int(scales[r, c // 32]) - 127)
+            assert got[r, c] == v, (r, c)
+
 ALL_PINS = [
     pin_router_worked_example_skillsuites, pin_router_worked_example_ai_infra,
     pin_softmax_placement_equivalence, pin_brute_force_routing,
@@ -537,7 +583,7 @@ ALL_PINS = [
     pin_experts_touched, pin_router_probabilities, pin_load_statistics_closed_forms,
     pin_load_statistics_brute, pin_bias_controller_rule, pin_bias_controller_balances,
     pin_capacity_limit, pin_capacity_dispatch_brute, pin_capacity_layer,
-    pin_group_limited_selection,
+    pin_group_limited_selection, pin_e8m0_decoder, pin_e2m1_decoder, pin_mxfp4_dequant,
 ]
 
 
@@ -693,6 +739,28 @@ def _m_group_strided(scores, k, n_groups, max_groups):
 _orig_group_topk = O.group_limited_top_k
 
 
+def _m_e2m1_bias0(codes):
+    c = np.asarray(codes).astype(np.int64) & 0xF
+    s = np.where(c & 0x8, -1.0, 1.0)
+    e = (c >> 1) & 0x3
+    m = (c & 0x1).astype(np.float64)
+    return s * np.where(e == 0, m * 0.5, (1.0 + m / 2.0) * np.exp2(e))
+
+
+def _m_mxfp4_high_nibble_first(packed, scales, block=32):
+    p = np.asarray(packed).astype(np.uint8)
+    swapped = ((p & 0xF) << 4) | (p >> 4)
+    return _orig_mxfp4(swapped, scales, block)
+
+
+def _m_e8m0_bias128(bits):
+    return _orig_e8m0(bits) / 2.0
+
+
+_orig_mxfp4 = O.dequant_mxfp4
+_orig_e8m0 = O.e8m0_bits_to_f64
+
+
 _orig_perm = O.permute_assignments
 _orig_bf16 = O.bf16_bits_to_f64
 _orig_e4m3 = O.e4m3_bits_to_f64
@@ -722,6 +790,9 @@ MUTATIONS = {
     "capacity_renormalises_gates": ("moe_forward_capacity", lambda: _m_capacity_renormalise),
     "group_score_is_sum": ("group_limited_top_k", lambda: _m_group_score_sum),
     "groups_strided_not_contiguous": ("group_limited_top_k", lambda: _m_group_strided),
+    "e2m1_wrong_bias": ("e2m1_bits_to_f64", lambda: _m_e2m1_bias0),
+    "mxfp4_high_nibble_first": ("dequant_mxfp4", lambda: _m_mxfp4_high_nibble_first),
+    "e8m0_wrong_bias": ("e8m0_bits_to_f64", lambda: _m_e8m0_bias128),
 }
 
 

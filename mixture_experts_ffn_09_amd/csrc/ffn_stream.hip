@@ -328,11 +328,13 @@ hipError_t launch_stream(const StreamParams& sp, int groups, hipStream_t st) {
 // pass (one weight block per step) makes the activation reads the larger
 // stream; there a wave takes two blocks (measured: 47% -> 64% of HBM peak
 // on the 7168 x 2048 fp8 down projection; four blocks, with the ring depth
-// halved again, reach only 60%).  Everywhere else one block per wave with
-// the deepest ring measured fastest.
+// halved again, reach only 60%).  MXFP4 steps carry four activation
+// fragments per 1 KB weight block, and two blocks per wave measured faster on
+// both passes (down 34% -> 42% of HBM peak).  Everywhere else one block per
+// wave with the deepest ring measured fastest.
 int stream_np(int fmt, bool gated, int n_out) {
   const int NB = n_out / 16;
-  int np = (fmt == WF_FP8 && !gated) ? 2 : 1;
+  int np = ((fmt == WF_FP8 && !gated) || fmt == WF_MXFP4) ? 2 : 1;
   while (np > 1 && NB % np) np >>= 1;
   return np;
 }

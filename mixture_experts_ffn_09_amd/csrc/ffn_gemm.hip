@@ -56,6 +56,20 @@ struct GemmParams {
   uint16_t* out_sh;
 };
 
+// Linear tile index of this workgroup, or -1 if it has none.  Workgroups are
+// dealt to the XCDs round-robin (XCD = blockIdx % 8) and dispatched in
+// blockIdx order; the grid is an upper bound of the tile count, so the real
+// count (known only on the device) is cut into 8 equal contiguous ranges, one
+// per XCD, and the workgroups past a range exit.  Every XCD gets the same
+// share of the work, and the live workgroups are the first ones dispatched.
+// Needs gridDim.x to be a multiple of 8 and at least the tile count.
+__device__ __forceinline__ int xcd_tile(int total) {
+  const int per = (total + NXCD - 1) / NXCD;
+  const int slot = blockIdx.x / NXCD;
+  const int L = (blockIdx.x % NXCD) * per + slot;
+  return (slot < per && L < total) ? L : -1;
+}
+
 __device__ __forceinline__ void fp8_half_to_bf16(const u32x4_t& q, int half, u32x4_t& o) {
   const uint32_t w0 = half ? q[2] : q[0];
   const uint32_t w1 = half ? q[3] : q[1];
@@ -169,9 +183,8 @@ __global__ __launch_bounds__(512, 1) void ffn_gemm_kernel(GemmParams p) {
   // ---- tile index: XCD remap, then groups of GM_GN weight tiles
   const int ngroups = p.g1 - p.g0;
   const int MT = p.tiles[ngroups];
-  const int per = gridDim.x / NXCD;
-  const int L = (blockIdx.x % NXCD) * per + blockIdx.x / NXCD;
-  if (L >= MT * p.NT) return;
+  const int L = xcd_tile(MT * p.NT);
+  if (L < 0) return;
   const int blk = L / (MT * GM_GN);
   const int gw = min(GM_GN, p.NT - blk * GM_GN);
   const int rr = L - blk * MT * GM_GN;
@@ -388,9 +401,8 @@ __global__ __launch_bounds__(256, 1) void ffn_gemm_big_kernel(GemmParams p) {
 
   const int ngroups = p.g1 - p.g0;
   const int MT = p.tiles[ngroups];
-  const int per = gridDim.x / NXCD;
-  const int L = (blockIdx.x % NXCD) * per + blockIdx.x / NXCD;
-  if (L >= MT * p.NT) return;
+  const int L = xcd_tile(MT * p.NT);
+  if (L < 0) return;
   const int blk = L / (MT * GM_GN);
   const int gw = min(GM_GN, p.NT - blk * GM_GN);
   const int rr = L - blk * MT * GM_GN;

@@ -9,11 +9,13 @@
 // slot it replaces": three matrices.)
 //
 // Two tilings for gfx950, both on v_mfma_f32_16x16x32_bf16:
-//  * 256-row tiles (bf16, many rows per group): 4 waves, one per SIMD, each
-//    128 x 128 with its accumulators in AGPRs (ffn_gemm_big_kernel below).
-//  * 128-row tiles (and FP8 weights): a 512-thread workgroup (8 waves, two
-//    per SIMD, so one wave's LDS or barrier wait is covered by the other's
-//    MFMAs), 2 x 4 waves of 64 x 64.
+//  * bf16 weights: 4 waves, one per SIMD, accumulators in AGPRs; tiles of
+//    256 weight rows x 256 activation rows, the last tile of a group cut to
+//    64 or 128 rows when that holds its remaining rows
+//    (ffn_gemm_big_kernel below).
+//  * FP8 weights (and shapes past 32-bit operand offsets): 128-row tiles in a
+//    512-thread workgroup (8 waves, two per SIMD, so one wave's LDS or
+//    barrier wait is covered by the other's MFMAs), 2 x 4 waves of 64 x 64.
 // Both operands reach LDS through direct global-to-LDS loads (each lane's 16
 // bytes land at lane * 16 of a 1 KB block), so no registers are spent on
 // staging.  Every 1 KB in LDS is one MFMA operand (lane l holds row l % 16,
@@ -24,7 +26,7 @@
 //
 // Tile order: workgroup ids are spread over the 8 XCDs round-robin, so the
 // linear tile index is remapped to give each XCD a contiguous range, and the
-// range is walked in groups of 8 weight tiles x all row tiles: workgroups
+// range is walked in groups of 4 weight tiles x all row tiles: workgroups
 // that run together on one XCD share their weight and activation slices in
 // that XCD's L2.  Row tiles are counted on the device (a one-workgroup scan
 // of ceil(rows_g / BM)), so no host synchronisation on the counts is needed.
@@ -35,8 +37,9 @@
 namespace {
 
 constexpr int GM_BN = 256;    // weight rows per workgroup tile
-constexpr int GM_GN = 8;      // weight tiles per tile-order group
+constexpr int GM_GN = 4;      // weight tiles per tile-order group
 constexpr int NXCD = 8;
+constexpr int FW_LDS = 128 * 1024;  // LDS of the four-wave kernel
 
 struct GemmParams {
   const uint16_t* a;          // routed activations (row r, or row perm[r])
@@ -372,51 +375,72 @@ __global__ __launch_bounds__(512, 1) void ffn_gemm_kernel(GemmParams p) {
   }
 }
 
-// Large-tile form for bf16 weights and many rows per group: 4 waves (one
-// per SIMD), 256 rows x 256 weight rows per workgroup, each wave 128 x 128
-// (256 accumulator registers, held in AGPRs).  Per 32-K stage a wave reads
-// 16 KB of operands from LDS for 64 MFMAs, a third less LDS traffic per flop
-// than the 8-wave form.  With a single wave per SIMD nothing hides a stall,
-// so each stage spreads its eight operand copies and sixteen fragment reads
-// evenly between its MFMAs instead of issuing them in bursts.
-template <bool GATED>
-__global__ __launch_bounds__(256, 1) void ffn_gemm_big_kernel(GemmParams p) {
-  constexpr int BM = 256;
-  constexpr int MBW = 8, NBW = 8;     // 16-row blocks per wave
-  constexpr int AFR = BM / 16;        // activation fragments per stage (one 32-K step)
+// Four-wave form for bf16 weights (one wave per SIMD, one workgroup per CU):
+// a tile is 256 weight rows wide and 64, 128 or 256 rows tall.  A group of r
+// rows takes ceil(r / 256) tiles; all are 256 rows tall except the last,
+// which is the smallest of 64, 128, 256 that holds the rows left.  So a group
+// never streams its weights more often than ceil(r / 256) times, and a small
+// group (most of them, with many experts) costs MFMA work in proportion to
+// its rows.  Tall and short tiles share one launch: short tiles are bound by
+// the weight stream, tall ones by the MFMAs, and running them side by side
+// lets the two limits overlap.
+//
+// Wave layout and work per 32-K stage (per wave):
+//   256 rows: 2 x 2 waves of 128 x 128; 8 copies, 16 fragment reads, 64 MFMAs
+//   128 rows: 1 x 4 waves of 128 x  64; 6 copies, 12 fragment reads, 32 MFMAs
+//    64 rows: 1 x 4 waves of  64 x  64; 5 copies,  8 fragment reads, 16 MFMAs
+// The accumulators live in AGPRs.  With a single wave per SIMD nothing hides
+// a stall, so each stage spreads its copies and fragment reads evenly between
+// its MFMAs instead of issuing them in bursts; shorter tiles (smaller stages)
+// keep more stages in flight.
+
+// Scheduling pattern of one stage: group q of LPS issues one copy, then its
+// share of the NRD fragment reads, each preceded by a slice of the NMF MFMAs.
+template <int Q, int LPS, int NRD, int NMF>
+__device__ __forceinline__ void stage_pattern() {
+  if constexpr (Q < LPS) {
+    constexpr int d = (Q + 1) * NRD / LPS - Q * NRD / LPS;   // reads in this group
+    constexpr int m = (Q + 1) * NMF / LPS - Q * NMF / LPS;   // MFMAs in this group
+    static_assert(d >= 1 && d <= 2 && m >= d + 1, "pattern");
+    __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);       // one copy
+    if constexpr (d == 1) {
+      __builtin_amdgcn_sched_group_barrier(0x008, m / 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, m - m / 2, 0);
+    } else {
+      __builtin_amdgcn_sched_group_barrier(0x008, m / 3, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, (m - m / 3) / 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, m - m / 3 - (m - m / 3) / 2, 0);
+    }
+    stage_pattern<Q + 1, LPS, NRD, NMF>();
+  }
+}
+
+// One tile: WM x (4 / WM) waves, each MBW x NBW blocks of 16 x 16; NS ring
+// stages of one 32-K step each.
+template <bool GATED, int WM, int MBW, int NBW, int NS>
+__device__ __forceinline__ void four_wave_tile(const GemmParams& p, uint8_t* lds, int g,
+                                               int row_base, int rows, int m0, int nt) {
+  constexpr int WN = 4 / WM;
+  constexpr int BM = WM * MBW * 16;
+  constexpr int AFR = BM / 16;        // activation fragments per stage
   constexpr int WBL = GM_BN / 16;     // weight blocks per stage
+  static_assert(WN * NBW == WBL, "tile width");
   constexpr int NH = GATED ? 2 : 1;
   constexpr int A_BYTES = AFR * 1024;
   constexpr int STAGE = A_BYTES + WBL * 1024;
-  constexpr int NS = 4;                 // ring depth: NS-1 stages in flight
   constexpr int A_PER_WAVE = AFR / 4, B_PER_WAVE = WBL / 4;
-  constexpr int LPS = A_PER_WAVE + B_PER_WAVE;
-  static_assert(NS * STAGE <= 160 * 1024, "LDS");
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[NS * STAGE];
+  constexpr int LPS = A_PER_WAVE + B_PER_WAVE;   // copies per wave per stage
+  constexpr int NRD = MBW + NBW;                 // fragment reads per wave per stage
+  constexpr int NMF = MBW * NBW;                 // MFMAs per wave per stage
+  static_assert(NS * STAGE <= FW_LDS, "LDS");
+  static_assert(NS >= 3 && (NS - 2) * LPS < 64, "ring");
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
-
-  const int ngroups = p.g1 - p.g0;
-  const int MT = p.tiles[ngroups];
-  const int L = xcd_tile(MT * p.NT);
-  if (L < 0) return;
-  const int blk = L / (MT * GM_GN);
-  const int gw = min(GM_GN, p.NT - blk * GM_GN);
-  const int rr = L - blk * MT * GM_GN;
-  const int mt = rr / gw;
-  const int nt = blk * GM_GN + rr % gw;
-  int lo = 0, hi = ngroups - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (p.tiles[mid] <= mt) lo = mid; else hi = mid - 1;
-  }
-  const int g = p.g0 + lo;
-  const int m0 = (mt - p.tiles[lo]) * BM;
-  int row_base, rows;
-  group_rows(p, g, row_base, rows);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave / WN, wn = wave % WN;
   const bool shared = g >= p.N;
   uint16_t* out = shared ? p.out_sh : p.out;
 
@@ -494,9 +518,9 @@ __global__ __launch_bounds__(256, 1) void ffn_gemm_big_kernel(GemmParams p) {
           base + A_BYTES + ((wn * NBW + f - MBW) * 64 + lane) * 16);
   };
   // Stage kt: wait until stage kt+1 has landed for every wave, then run
-  // stage kt's 64 MFMAs with two streams interleaved: the copy of stage
+  // stage kt's MFMAs with two streams interleaved: the copy of stage
   // kt+NS-1 into the buffer of stage kt-1 (whose fragments the previous stage's
-  // MFMAs consumed) and the 16 fragment reads of stage kt+1.  Every stage
+  // MFMAs consumed) and the fragment reads of stage kt+1.  Every stage
   // issues its copy, clamped to the last K step near the end, so that one
   // vmcnt threshold holds throughout and no branch splits the schedule; the
   // clamped copies only land in buffers no later stage reads, and the reads
@@ -511,27 +535,18 @@ __global__ __launch_bounds__(256, 1) void ffn_gemm_big_kernel(GemmParams p) {
 #pragma unroll
     for (int q = 0; q < LPS; ++q) {
       copy_one(q, min(kt + NS - 1, KT - 1), (kt + NS - 1) % NS);
-      read_one(ga, gb, 2 * q, kt + 1);
-      read_one(ga, gb, 2 * q + 1, kt + 1);
+#pragma unroll
+      for (int f = q * NRD / LPS; f < (q + 1) * NRD / LPS; ++f) read_one(ga, gb, f, kt + 1);
     }
 #pragma unroll
     for (int i = 0; i < MBW; ++i)
 #pragma unroll
       for (int j = 0; j < NBW; ++j) acc[i][j] = mfma16x16x32(fa[i], fb[j], acc[i][j]);
-#pragma unroll
-    for (int q = 0; q < LPS; ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);  // one copy
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // two MFMAs
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-      __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);  // three MFMAs
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-      __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);  // three MFMAs
-    }
+    stage_pattern<0, LPS, NRD, NMF>();
     __builtin_amdgcn_sched_barrier(0);
   };
-  static_assert(LPS * 8 == MBW * NBW && LPS * 2 == MBW + NBW, "interleave pattern");
 
-  // K/32 is even (and at least 2) for every accepted shape
+  // K/32 is even (and at least 4) for every accepted shape
 #pragma unroll
   for (int st = 0; st < NS - 1; ++st)
 #pragma unroll
@@ -539,7 +554,7 @@ __global__ __launch_bounds__(256, 1) void ffn_gemm_big_kernel(GemmParams p) {
   wait_vmcnt<(NS - 2) * LPS>();
   barrier_no_fence();
 #pragma unroll
-  for (int f = 0; f < MBW + NBW; ++f) read_one(ca, cb, f, 0);
+  for (int f = 0; f < NRD; ++f) read_one(ca, cb, f, 0);
 
   for (int kt = 0; kt < KT; kt += 2) {
     stage(ca, cb, na, nb, kt);
@@ -571,6 +586,36 @@ __global__ __launch_bounds__(256, 1) void ffn_gemm_big_kernel(GemmParams p) {
   }
 }
 
+template <bool GATED>
+__global__ __launch_bounds__(256, 1) void ffn_gemm_big_kernel(GemmParams p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[FW_LDS];
+  const int ngroups = p.g1 - p.g0;
+  const int MT = p.tiles[ngroups];
+  const int L = xcd_tile(MT * p.NT);
+  if (L < 0) return;
+  const int blk = L / (MT * GM_GN);
+  const int gw = min(GM_GN, p.NT - blk * GM_GN);
+  const int rr = L - blk * MT * GM_GN;
+  const int mt = rr / gw;
+  const int nt = blk * GM_GN + rr % gw;
+  int lo = 0, hi = ngroups - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (p.tiles[mid] <= mt) lo = mid; else hi = mid - 1;
+  }
+  const int g = p.g0 + lo;
+  const int m0 = (mt - p.tiles[lo]) * 256;
+  int row_base, rows;
+  group_rows(p, g, row_base, rows);
+  const int left = rows - m0;   // rows from this tile on (> 0)
+  if (left > 128)
+    four_wave_tile<GATED, 2, 8, 8, 4>(p, lds, g, row_base, rows, m0, nt);
+  else if (left > 64)
+    four_wave_tile<GATED, 1, 8, 4, 5>(p, lds, g, row_base, rows, m0, nt);
+  else
+    four_wave_tile<GATED, 1, 4, 4, 6>(p, lds, g, row_base, rows, m0, nt);
+}
+
 template <int BM, bool FP8>
 void launch_gemm_kernel(bool gated, long long nwg, const GemmParams& p, hipStream_t st) {
   if (gated)
@@ -581,20 +626,18 @@ void launch_gemm_kernel(bool gated, long long nwg, const GemmParams& p, hipStrea
 
 }  // namespace
 
-int gemm_row_tile(int avg_rows, bool fp8) { return (!fp8 && avg_rows >= 192) ? 256 : 128; }
-
 bool gemm_shape_ok(int d, int d_ff) { return d % 256 == 0 && d_ff % 128 == 0; }
 
-hipError_t launch_ffn_gemm(const FfnArgs& a, int pass, int g0, int g1, int bm, int max_rows,
+hipError_t launch_ffn_gemm(const FfnArgs& a, int pass, int g0, int g1, int max_rows,
                            int32_t* sched, hipStream_t st) {
   if (g1 <= g0) return hipSuccess;
-  if (bm == 256) {
-    // the 256-row kernel addresses operands through 32-bit buffer offsets
-    const long long lim = 0x7fffffffLL;
-    if ((long long)a.T * a.d * 2 > lim || (long long)a.T * a.k * a.d_ff * 2 > lim ||
-        4LL * a.d * a.d_ff > lim)
-      bm = 128;
-  }
+  // bf16 weights take the four-wave kernel (tiles of 64..256 rows), which
+  // addresses operands through 32-bit buffer offsets; FP8 weights, or shapes
+  // past those offsets, take the eight-wave kernel with 128-row tiles
+  const long long lim = 0x7fffffffLL;
+  const bool four_wave = !a.fp8 && (long long)a.T * a.d * 2 <= lim &&
+                         (long long)a.T * a.k * a.d_ff * 2 <= lim && 4LL * a.d * a.d_ff <= lim;
+  const int bm = four_wave ? 256 : 128;
   for (int ps = 1; ps <= 2; ++ps) {
     if (!(pass & ps)) continue;
     const bool gated = ps == 1;
@@ -626,7 +669,7 @@ hipError_t launch_ffn_gemm(const FfnArgs& a, int pass, int g0, int g1, int bm, i
     nwg = (nwg + NXCD - 1) / NXCD * NXCD;
     if (a.fp8)
       launch_gemm_kernel<128, true>(gated, nwg, p, st);
-    else if (bm == 256) {
+    else if (four_wave) {
       if (gated)
         ffn_gemm_big_kernel<true><<<dim3((unsigned)nwg), 256, 0, st>>>(p);
       else

@@ -435,13 +435,12 @@ hipError_t launch_ffn_lowp(const FfnArgs& a, int pass, hipStream_t st) {
     if (!(pass & ps)) continue;
     if (routed_gemm && shared_gemm) {
       // one launch over routed + shared groups: their tiles share the machine
-      e = launch_ffn_gemm(a, ps, 0, a.N + 1, gemm_row_tile(avg, a.fp8),
-                          a.T * a.k + a.T, a.sched, st);
+      e = launch_ffn_gemm(a, ps, 0, a.N + 1, a.T * a.k + a.T, a.sched, st);
       if (e != hipSuccess) return e;
       continue;
     }
     if (routed_gemm) {
-      e = launch_ffn_gemm(a, ps, 0, a.N, gemm_row_tile(avg, a.fp8), a.T * a.k, a.sched, st);
+      e = launch_ffn_gemm(a, ps, 0, a.N, a.T * a.k, a.sched, st);
       if (e != hipSuccess) return e;
       if (a.n_shared)  // shared_gemm is false only below 64 tokens
         e = launch_ffn_stream(a, ps, a.N, a.N + 1, a.T, st);
@@ -450,7 +449,7 @@ hipError_t launch_ffn_lowp(const FfnArgs& a, int pass, hipStream_t st) {
     } else {
       e = launch_ffn_stream(a, ps, 0, a.N, avg, st);
       if (e == hipSuccess && a.n_shared)
-        e = launch_ffn_gemm(a, ps, a.N, a.N + 1, gemm_row_tile(a.T, a.fp8), a.T, a.sched, st);
+        e = launch_ffn_gemm(a, ps, a.N, a.N + 1, a.T, a.sched, st);
     }
     if (e != hipSuccess) return e;
   }

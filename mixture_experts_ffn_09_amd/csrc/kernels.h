@@ -80,8 +80,7 @@ hipError_t launch_ffn_stream(const FfnArgs& a, int pass, int g0, int g1, int row
 // Tiled GEMM over groups [g0, g1) with row tile bm; max_rows bounds the total
 // rows of those groups.
 bool gemm_shape_ok(int d, int d_ff);
-int gemm_row_tile(int avg_rows, bool fp8);
-hipError_t launch_ffn_gemm(const FfnArgs& a, int pass, int g0, int g1, int bm, int max_rows,
+hipError_t launch_ffn_gemm(const FfnArgs& a, int pass, int g0, int g1, int max_rows,
                            int32_t* sched, hipStream_t st);
 
 // Float32 expert FFN (float32 activations and weights), same row scheme.

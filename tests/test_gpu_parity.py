@@ -38,6 +38,11 @@ SMALL = {
     # routed and shared experts in one GEMM launch (128-row tiles)
     "gemm_routed_plus_shared": H.small_config(C[3], 109, T=160, d_model=256, d_ff=128,
                                               n_experts=16),
+    # both row-tile classes in one layer: experts of 0..128 rows on 128-row
+    # tiles, larger ones (up to 640 rows, three ragged 256-row tiles) and the
+    # 640-row shared expert on 256-row tiles
+    "gemm_row_classes": H.small_config(C[3], 114, T=640, d_model=256, d_ff=128, n_experts=32,
+                                       zipf_c=1.5),
     # FP8 weights through the GEMM path (routed + shared)
     "gemm_fp8": H.small_config(C[4], 110, T=256, d_model=256, d_ff=256, n_experts=8, top_k=4),
     # decode-sized batches: ragged T, odd N, sigmoid + selection bias + logit

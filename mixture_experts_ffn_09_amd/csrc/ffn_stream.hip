@@ -85,7 +85,10 @@ __device__ __forceinline__ u32x4_t fp4_word_to_bf16(uint32_t q, uint32_t e) {
 // activation fragments, which serve all NP blocks).  Activation rows past
 // the group's end are clamped to its last row: row m of an MFMA result
 // depends only on row m of A, and those rows are not stored.
-template <int MB, int NP, int D, int FMT, bool GATED>
+// SQ4 (MXFP4 with K % 512 == 0): a lane's E8M0 scales of four consecutive
+// K steps are 16 contiguous bytes of its row, fetched with one load per four
+// steps instead of one per step; the loop then advances four steps at a time.
+template <int MB, int NP, int D, int FMT, bool GATED, bool SQ4 = false>
 __device__ __forceinline__ void stream_body(const StreamParams& p, int nb0, int g, bool shared,
                                             int row_base, int rows, int m_first) {
   constexpr bool FP8 = FMT == WF_FP8, FP4 = FMT == WF_MXFP4;
@@ -150,7 +153,18 @@ __device__ __forceinline__ void stream_body(const StreamParams& p, int nb0, int 
 
     u32x4_t bq[D][NP][NH];
     u32x4_t aq[D][MB][AF];
-    uint32_t sq[FP4 ? D : 1][NP][NH];
+    uint32_t sq[FP4 && !SQ4 ? D : 1][NP][NH];
+    u32x4_t sqc[SQ4 ? NP : 1][SQ4 ? NH : 1], sqn[SQ4 ? NP : 1][SQ4 ? NH : 1];
+    // scales of K steps ks .. ks+3, all NP blocks and both halves
+    auto load_sq4 = [&](u32x4_t (&q)[SQ4 ? NP : 1][SQ4 ? NH : 1], int ks) {
+#pragma unroll
+      for (int j = 0; j < (SQ4 ? NP : 0); ++j)
+#pragma unroll
+        for (int h = 0; h < NH; ++h)
+          q[j][h] = *reinterpret_cast<const u32x4_t*>(S4 + ((size_t)h * p.n_out + j * 16) * SK32 +
+                                                      ks * 4);
+    };
+    if (SQ4) load_sq4(sqn, 0);
     auto load_step = [&](int u, int ks) {
 #pragma unroll
       for (int j = 0; j < NP; ++j)
@@ -158,8 +172,8 @@ __device__ __forceinline__ void stream_body(const StreamParams& p, int nb0, int 
         for (int h = 0; h < NH; ++h) {
           bq[u][j][h] =
               *reinterpret_cast<const u32x4_t*>(Wnb + j * bstride + ((size_t)ks * NH + h) * 1024);
-          if (FP4)
-            sq[FP4 ? u : 0][j][h] = *reinterpret_cast<const uint32_t*>(
+          if (FP4 && !SQ4)
+            sq[FP4 && !SQ4 ? u : 0][j][h] = *reinterpret_cast<const uint32_t*>(
                 S4 + ((size_t)h * p.n_out + j * 16) * SK32 + ks * 4);
         }
 #pragma unroll
@@ -173,10 +187,20 @@ __device__ __forceinline__ void stream_body(const StreamParams& p, int nb0, int 
     // keep the ring: the scheduler must not sink loads next to their use
     __builtin_amdgcn_sched_barrier(0);
 
-    for (int ks0 = 0; ks0 < KS; ks0 += D) {
+    // steps per iteration: the ring depth, or four for the scale quads
+    constexpr int G = SQ4 ? (D > 4 ? D : 4) : D;
+    for (int ks0 = 0; ks0 < KS; ks0 += G) {
 #pragma unroll
-      for (int u = 0; u < D; ++u) {
-        const int ks = ks0 + u;  // KS is a multiple of D: no bounds branch
+      for (int i = 0; i < G; ++i) {
+        const int u = i % D;      // ring slot
+        const int ks = ks0 + i;   // KS is a multiple of G: no bounds branch
+        if (SQ4 && (i & 3) == 0) {
+#pragma unroll
+          for (int j = 0; j < (SQ4 ? NP : 0); ++j)
+#pragma unroll
+            for (int h = 0; h < NH; ++h) sqc[j][h] = sqn[j][h];
+          load_sq4(sqn, min(ks + 4, KS - 4));
+        }
         if (FP4) {
           // four 32-wide K steps per block: word s4 of a lane's 16 bytes holds
           // its 8 codes of step s4, decoded with the step's scale straight to
@@ -187,7 +211,9 @@ __device__ __forceinline__ void stream_body(const StreamParams& p, int nb0, int 
             for (int h = 0; h < NH; ++h)
 #pragma unroll
               for (int s4 = 0; s4 < 4; ++s4) {
-                const u32x4_t b = fp4_word_to_bf16(bq[u][j][h][s4], (sq[FP4 ? u : 0][j][h] >> (8 * s4)) & 0xffu);
+                const uint32_t sw = SQ4 ? sqc[SQ4 ? j : 0][SQ4 ? h : 0][i & 3]
+                                        : sq[FP4 && !SQ4 ? u : 0][j][h];
+                const u32x4_t b = fp4_word_to_bf16(bq[u][j][h][s4], (sw >> (8 * s4)) & 0xffu);
 #pragma unroll
                 for (int mb = 0; mb < MB; ++mb)
                   acc[j][h][mb] = mfma16x16x32(aq[u][mb][s4], b, acc[j][h][mb]);
@@ -290,6 +316,9 @@ __global__ __launch_bounds__(256) void ffn_stream_kernel(StreamParams p) {
   else if (HOT && !shared && rows > 16)
     stream_body<2, NP, (D >= 4 ? D / 2 : D), FMT, GATED>(p, nb0, g, shared, row_base, rows,
                                                           m_first);
+  else if (FMT == WF_MXFP4 && p.K % 512 == 0 &&
+           ((uintptr_t)(shared ? p.s_sh : p.s) & 15) == 0)
+    stream_body<MB, NP, D, FMT, GATED, true>(p, nb0, g, shared, row_base, rows, m_first);
   else
     stream_body<MB, NP, D, FMT, GATED>(p, nb0, g, shared, row_base, rows, m_first);
 }

@@ -55,4 +55,27 @@ __device__ __forceinline__ floatx4_t mfma16x16x32(const u32x4_t& a, const u32x4_
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
+// Fourth dword of a raw buffer resource on gfx950 (32-bit data format, no
+// swizzle), as used for bounds-checked byte-addressed loads.
+constexpr int BUF_DWORD3 = 0x00020000;
+
+// s_waitcnt vmcnt(N) leaving the other counters untouched (gfx9 encoding:
+// vmcnt low bits 3:0 and high bits 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier without the release/acquire fences of __syncthreads():
+// those would wait for every outstanding global-to-LDS copy (vmcnt(0)) and
+// drain the ring.  The copies are ordered by explicit wait_vmcnt() instead;
+// the empty asm statements keep the compiler from moving memory accesses
+// across the barrier.
+__device__ __forceinline__ void barrier_no_fence() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 __host__ __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }

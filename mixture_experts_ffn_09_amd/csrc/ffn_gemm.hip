@@ -116,18 +116,6 @@ __global__ __launch_bounds__(1024) void tile_schedule_kernel(GemmParams p, int b
   if (i == 0) tiles[0] = 0;
 }
 
-// Fourth dword of a raw buffer resource on gfx950 (32-bit data format, no
-// swizzle), as used for bounds-checked byte-addressed loads.
-constexpr int BUF_DWORD3 = 0x00020000;
-
-// s_waitcnt vmcnt(N) leaving the other counters untouched (gfx9 encoding:
-// vmcnt low bits 3:0 and high bits 15:14, expcnt 6:4, lgkmcnt 11:8).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
 // Wait until at most `later` stages of LPS copies each are still in flight
 // (later <= MAXL, a run-time value turned into an immediate).
 template <int LPS, int MAXL>
@@ -140,17 +128,6 @@ __device__ __forceinline__ void wait_stages(int later) {
   else if (MAXL >= 2 && later == 2) wait_vmcnt<(MAXL >= 2 ? 2 : 0) * LPS>();
   else if (MAXL >= 1 && later == 1) wait_vmcnt<LPS>();
   else wait_vmcnt<0>();
-}
-
-// Workgroup barrier without the release/acquire fences of __syncthreads():
-// those would wait for every outstanding global-to-LDS copy (vmcnt(0)) and
-// drain the ring.  The copies are ordered by explicit wait_vmcnt() instead;
-// the empty asm statements keep the compiler from moving memory accesses
-// across the barrier.
-__device__ __forceinline__ void barrier_no_fence() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
 }
 
 template <int BM, bool GATED, bool FP8>

@@ -36,6 +36,7 @@ struct StreamParams {
   const uint16_t* a_sh;       // shared-expert activations, row t
   const int32_t* offsets;     // [N+1]
   int T, N, g0;
+  int a_rows;    // rows of `a` (T with perm, else the assignments)
   int n_routed;  // routed groups in this launch (g0 .. g0+n_routed-1)
   int sh_rows;   // rows per shared-expert slice (grid rows past the routed ones)
   int K;       // reduction length
@@ -88,9 +89,20 @@ __device__ __forceinline__ u32x4_t fp4_word_to_bf16(uint32_t q, uint32_t e) {
 // SQ4 (MXFP4 with K % 512 == 0): a lane's E8M0 scales of four consecutive
 // K steps are 16 contiguous bytes of its row, fetched with one load per four
 // steps instead of one per step; the loop then advances four steps at a time.
-template <int MB, int NP, int D, int FMT, bool GATED, bool SQ4 = false>
+// LDSA: the activation fragments, the same for the workgroup's four waves,
+// are copied once per workgroup into LDS (global-to-LDS copies in fragment
+// order, a double buffer of CH K steps, each wave copying a quarter) and
+// read from there, instead of once per wave from L2: a quarter of the
+// activation load instructions, which otherwise outnumber the weight loads'
+// cache-line requests.  One barrier per chunk: after it every wave's copies
+// of this chunk have landed and every wave has finished reading the previous
+// one, whose buffer the next chunk's copies then reuse.  `store` is false for
+// a wave past the last weight block: it mirrors a valid block to take part in
+// the copies and barriers, and stores nothing.
+template <int MB, int NP, int D, int FMT, bool GATED, bool SQ4 = false, bool LDSA = false>
 __device__ __forceinline__ void stream_body(const StreamParams& p, int nb0, int g, bool shared,
-                                            int row_base, int rows, int m_first) {
+                                            int row_base, int rows, int m_first, uint8_t* alds,
+                                            bool store) {
   constexpr bool FP8 = FMT == WF_FP8, FP4 = FMT == WF_MXFP4;
   constexpr int NH = GATED ? 2 : 1;
   constexpr int AF = FP4 ? 4 : (FP8 ? 2 : 1);  // 32-wide activation fragments per K step
@@ -123,20 +135,31 @@ __device__ __forceinline__ void stream_body(const StreamParams& p, int nb0, int 
 
   const int lrow = lane & 15;
   const int lk = (lane >> 4) * 8;
+  // LDSA copies are buffer loads: a uniform resource over the activation
+  // rows and per-lane 32-bit byte offsets (the launch checks they fit); the
+  // buffer form keeps the compiler's own vmcnt waits exact
+  const uint16_t* abase = shared ? p.a_sh : p.a;
+  typedef __attribute__((address_space(3))) void* lds_ptr_t;
+  const __amdgpu_buffer_rsrc_t ares = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)abase, 0,
+      (int)(uint32_t)((size_t)(shared || p.perm ? p.T : row_base + rows) * p.K * 2),
+      BUF_DWORD3);
 
   for (int m0 = m_first; m0 < rows; m0 += 16 * MB) {
     const uint16_t* arow[MB];
+    uint32_t aoff[MB];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
       const int r = min(m0 + mb * 16 + lrow, rows - 1);
-      const uint16_t* ptr;
+      int src;
       if (shared)
-        ptr = p.a_sh + (size_t)r * p.K;
+        src = r;
       else if (p.perm)
-        ptr = p.a + (size_t)p.perm[row_base + r] * p.K;
+        src = p.perm[row_base + r];
       else
-        ptr = p.a + (size_t)(row_base + r) * p.K;
-      arow[mb] = ptr + lk;
+        src = row_base + r;
+      arow[mb] = abase + (size_t)src * p.K + lk;
+      aoff[mb] = ((uint32_t)src * (uint32_t)p.K + lk) * 2;
     }
 
     floatx4_t acc[NP][NH][MB];
@@ -151,8 +174,43 @@ __device__ __forceinline__ void stream_body(const StreamParams& p, int nb0, int 
           part[j][h][mb] = floatx4_t{0.f, 0.f, 0.f, 0.f};
         }
 
+    // steps per inner iteration: the ring depth, or four for the scale quads;
+    // with LDSA, steps per LDS chunk (at least 8 KB of fragments)
+    constexpr int G = SQ4 ? (D > 4 ? D : 4) : D;
+    constexpr int CH = LDSA ? (G > 8 / (MB * AF) ? G : 8 / (MB * AF)) : G;
+    constexpr int NF = CH * MB * AF;            // 1 KB fragments per chunk
+    constexpr int NPH = NP * NH;                // weight loads per step
+    static_assert(!LDSA || (NF % SW_WAVES == 0 && NF <= 16), "LDS chunk");
+    static_assert(!LDSA || !FP4 || SQ4, "per-step scale loads are not counted");
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    // issue this wave's share of the copies of chunk c into buffer c & 1
+    auto copy_chunk = [&](int c) {
+#pragma unroll
+      for (int t = 0; t < (LDSA ? NF / SW_WAVES : 0); ++t) {
+        const int fi = t * SW_WAVES + wave;     // fragment (step, row block, part)
+        const int cs = fi / (MB * AF), mb = (fi / AF) % MB, f = fi % AF;
+        uint32_t ro = aoff[0];
+#pragma unroll
+        for (int q = 1; q < MB; ++q)
+          if (mb == q) ro = aoff[q];
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            ares, (lds_ptr_t)(alds + (c & 1) * (NF * 1024) + fi * 1024), 16, ro,
+            ((c * CH + cs) * (32 * AF) + f * 32) * 2, 0, 0);
+      }
+    };
+    if (LDSA) {
+      barrier_no_fence();  // the previous pass has finished reading both buffers
+      copy_chunk(0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+
     u32x4_t bq[D][NP][NH];
     u32x4_t aq[D][MB][AF];
+    u32x4_t ach[LDSA ? CH : 1][MB][AF];   // the current chunk's fragments
+    // FP8 block scales ride in the ring with the weights (an odd slot holds
+    // an odd step, which closes a 128-wide block): loaded right before use,
+    // the wait for them would drain the whole ring every second step
+    float sfq[FP8 ? D : 1][NH];
     uint32_t sq[FP4 && !SQ4 ? D : 1][NP][NH];
     u32x4_t sqc[SQ4 ? NP : 1][SQ4 ? NH : 1], sqn[SQ4 ? NP : 1][SQ4 ? NH : 1];
     // scales of K steps ks .. ks+3, all NP blocks and both halves
@@ -176,8 +234,12 @@ __device__ __forceinline__ void stream_body(const StreamParams& p, int nb0, int 
             sq[FP4 && !SQ4 ? u : 0][j][h] = *reinterpret_cast<const uint32_t*>(
                 S4 + ((size_t)h * p.n_out + j * 16) * SK32 + ks * 4);
         }
+      if (FP8 && (u & 1)) {
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
+        for (int h = 0; h < NH; ++h) sfq[FP8 ? u : 0][h] = S[(size_t)h * SR * SK + (ks >> 1)];
+      }
+#pragma unroll
+      for (int mb = 0; mb < (LDSA ? 0 : MB); ++mb)
 #pragma unroll
         for (int f = 0; f < AF; ++f)
           aq[u][mb][f] = *reinterpret_cast<const u32x4_t*>(arow[mb] + ks * (32 * AF) + f * 32);
@@ -187,13 +249,47 @@ __device__ __forceinline__ void stream_body(const StreamParams& p, int nb0, int 
     // keep the ring: the scheduler must not sink loads next to their use
     __builtin_amdgcn_sched_barrier(0);
 
-    // steps per iteration: the ring depth, or four for the scale quads
-    constexpr int G = SQ4 ? (D > 4 ? D : 4) : D;
-    for (int ks0 = 0; ks0 < KS; ks0 += G) {
+    for (int ks0 = 0; ks0 < KS; ks0 += CH) {
+      if (LDSA) {
+        // this wave's copies of the chunk have landed once at most the loads
+        // issued after them are outstanding: the ring's prologue for the
+        // first chunk, the previous chunk's refills (and scale quads) later
+        // (a lower bound of the count: the weight loads and scale quads;
+        // any other vector load after the copies only makes the wait longer)
+        if (ks0 == 0)
+          wait_vmcnt<(SQ4 ? NPH : 0) + D * NPH>();
+        else
+          wait_vmcnt<CH * NPH + (SQ4 ? (CH / 4) * NPH : 0)>();
+        barrier_no_fence();
+        // read the whole chunk before the next chunk's copies are issued, so
+        // no LDS read has to wait for copies still in flight
+        const uint8_t* abuf = alds + ((ks0 / CH) & 1) * (NF * 1024) + lane * 16;
 #pragma unroll
-      for (int i = 0; i < G; ++i) {
+        for (int i = 0; i < CH; ++i)
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int f = 0; f < AF; ++f)
+              ach[LDSA ? i : 0][mb][f] =
+                  *reinterpret_cast<const u32x4_t*>(abuf + ((i * MB + mb) * AF + f) * 1024);
+        __builtin_amdgcn_sched_barrier(0);
+        // the last chunk copies itself again into the idle buffer: with no
+        // branch, the compiler's own waits stay exact across iterations; a
+        // fragment is always copied by the same wave, so its copies land in
+        // issue order
+        copy_chunk(min(ks0 / CH + 1, KS / CH - 1));
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int i = 0; i < CH; ++i) {
         const int u = i % D;      // ring slot
-        const int ks = ks0 + i;   // KS is a multiple of G: no bounds branch
+        const int ks = ks0 + i;   // KS is a multiple of CH: no bounds branch
+        if (LDSA) {
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int f = 0; f < AF; ++f) aq[u][mb][f] = ach[LDSA ? i : 0][mb][f];
+        }
         if (SQ4 && (i & 3) == 0) {
 #pragma unroll
           for (int j = 0; j < (SQ4 ? NP : 0); ++j)
@@ -242,10 +338,9 @@ __device__ __forceinline__ void stream_body(const StreamParams& p, int nb0, int 
           // every second 64-wide step closes a 128-wide scale block (D is
           // even and ks0 a multiple of D, so ks and u have the same parity)
           if (u & 1) {
-            const int kc = ks >> 1;
 #pragma unroll
             for (int h = 0; h < NH; ++h) {
-              const float sc = S[(size_t)h * SR * SK + kc];
+              const float sc = sfq[FP8 ? u : 0][h];
 #pragma unroll
               for (int j = 0; j < NP; ++j)
 #pragma unroll
@@ -263,7 +358,9 @@ __device__ __forceinline__ void stream_body(const StreamParams& p, int nb0, int 
       }
     }
 
+    if (LDSA) wait_vmcnt<0>();  // no copy outlives the pass
     // epilogue: lane holds rows 4*(lane/16)+e of column lane%16
+    if (LDSA && !store) continue;
 #pragma unroll
     for (int j = 0; j < NP; ++j) {
       const int n = (nb0 + j) * 16 + lrow;
@@ -290,12 +387,18 @@ __device__ __forceinline__ void stream_body(const StreamParams& p, int nb0, int 
 // instead of streaming its weights once per 16 rows: with skewed routing a
 // few hot experts hold many of the rows (on the skewed fp8 decode workload
 // this cut the gate/up time by 12%).
-template <int MB, int NP, int D, int FMT, bool GATED, bool HOT>
+template <int MB, int NP, int D, int FMT, bool GATED, bool HOT, bool LDSA>
 __global__ __launch_bounds__(256) void ffn_stream_kernel(StreamParams p) {
+  // activation chunks: two buffers of up to 8 KB (bf16) or 16 KB (FP8, MXFP4)
+  __shared__ __attribute__((aligned(1024))) uint8_t alds[LDSA ? (FMT == WF_BF16 ? 16384 : 32768) : 1024];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int NB = p.n_out / 16;  // a multiple of NP
-  const int nb0 = (blockIdx.x * SW_WAVES + wave) * NP;
-  if (nb0 >= NB) return;
+  int nb0 = (blockIdx.x * SW_WAVES + wave) * NP;
+  const bool store = nb0 < NB;
+  if (!store) {
+    if (!LDSA) return;
+    nb0 = NB - NP;  // mirror a valid block for the copies and barriers
+  }
 
   // grid rows: routed groups, then slices of the shared expert's T rows
   const bool shared = (int)blockIdx.y >= p.n_routed;
@@ -311,16 +414,18 @@ __global__ __launch_bounds__(256) void ffn_stream_kernel(StreamParams p) {
   }
   if (rows <= m_first) return;
   if (HOT && !shared && rows > 32)
-    stream_body<4, NP, (D >= 8 ? D / 4 : 2), FMT, GATED>(p, nb0, g, shared, row_base, rows,
-                                                          m_first);
+    stream_body<4, NP, (D >= 8 ? D / 4 : 2), FMT, GATED, false, LDSA && HOT>(
+        p, nb0, g, shared, row_base, rows, m_first, alds, store);
   else if (HOT && !shared && rows > 16)
-    stream_body<2, NP, (D >= 4 ? D / 2 : D), FMT, GATED>(p, nb0, g, shared, row_base, rows,
-                                                          m_first);
+    stream_body<2, NP, (D >= 4 ? D / 2 : D), FMT, GATED, false, LDSA && HOT>(
+        p, nb0, g, shared, row_base, rows, m_first, alds, store);
   else if (FMT == WF_MXFP4 && p.K % 512 == 0 &&
            ((uintptr_t)(shared ? p.s_sh : p.s) & 15) == 0)
-    stream_body<MB, NP, D, FMT, GATED, true>(p, nb0, g, shared, row_base, rows, m_first);
+    stream_body<MB, NP, D, FMT, GATED, FMT == WF_MXFP4, LDSA>(p, nb0, g, shared, row_base, rows,
+                                                              m_first, alds, store);
   else
-    stream_body<MB, NP, D, FMT, GATED>(p, nb0, g, shared, row_base, rows, m_first);
+    stream_body<MB, NP, D, FMT, GATED, false, LDSA && FMT != WF_MXFP4>(
+        p, nb0, g, shared, row_base, rows, m_first, alds, store);
 }
 
 template <int MB, int NP, int D, int FMT, bool GATED>
@@ -331,7 +436,15 @@ hipError_t launch_stream_d(const StreamParams& sp, int groups, hipStream_t st) {
   // the per-group 32- and 64-row passes need the 16-row form's register room;
   // the MXFP4 form (four activation fragments per step) has none to spare
   constexpr bool HOT = MB == 1 && FMT != WF_MXFP4;
-  ffn_stream_kernel<MB, NP, D, FMT, GATED, HOT><<<grid, SW_WAVES * 64, 0, st>>>(sp);
+  // activations through LDS where every pass width's chunk divides the K
+  // steps (chunks are at most 8 steps); MXFP4 only with 16-row passes
+  const int KS = sp.K / (FMT == WF_MXFP4 ? 128 : (FMT == WF_FP8 ? 64 : 32));
+  constexpr bool LOK = FMT != WF_MXFP4 || MB == 1;
+  const bool fits = (long long)(sp.a_rows > sp.T ? sp.a_rows : sp.T) * sp.K * 2 <= 0x7fffffffLL;
+  if (LOK && KS % 8 == 0 && fits)
+    ffn_stream_kernel<MB, NP, D, FMT, GATED, HOT, LOK><<<grid, SW_WAVES * 64, 0, st>>>(sp);
+  else
+    ffn_stream_kernel<MB, NP, D, FMT, GATED, HOT, false><<<grid, SW_WAVES * 64, 0, st>>>(sp);
   return hipGetLastError();
 }
 
@@ -407,6 +520,7 @@ hipError_t launch_ffn_stream(const FfnArgs& a, int pass, int g0, int g1, int row
   up.a_sh = a.x_sh;
   up.offsets = a.offsets;
   up.T = a.T;
+  up.a_rows = a.perm_token ? a.T : a.T * a.k;
   up.N = a.N;
   up.g0 = g0;
   up.n_routed = n_routed;
@@ -423,6 +537,7 @@ hipError_t launch_ffn_stream(const FfnArgs& a, int pass, int g0, int g1, int row
   StreamParams dn = up;
   dn.a = a.H;
   dn.perm = nullptr;
+  dn.a_rows = a.T * a.k;
   dn.a_sh = a.H_sh;
   dn.K = a.d_ff;
   dn.n_out = a.d;

@@ -31,6 +31,8 @@
 // that XCD's L2.  Row tiles are counted on the device (a one-workgroup scan
 // of ceil(rows_g / BM)), so no host synchronisation on the counts is needed.
 
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -39,7 +41,7 @@ namespace {
 constexpr int GM_BN = 256;    // weight rows per workgroup tile
 constexpr int GM_GN = 4;      // weight tiles per tile-order group
 constexpr int NXCD = 8;
-constexpr int FW_LDS = 128 * 1024;  // LDS of the four-wave kernel
+constexpr int FW_LDS = 160 * 1024;  // LDS of the four-wave kernel
 
 struct GemmParams {
   const uint16_t* a;          // routed activations (row r, or row perm[r])
@@ -362,73 +364,102 @@ __global__ __launch_bounds__(512, 1) void ffn_gemm_kernel(GemmParams p) {
 // the weight stream, tall ones by the MFMAs, and running them side by side
 // lets the two limits overlap.
 //
-// Wave layout and work per 32-K stage (per wave):
-//   256 rows: 2 x 2 waves of 128 x 128; 8 copies, 16 fragment reads, 64 MFMAs
-//   128 rows: 1 x 4 waves of 128 x  64; 6 copies, 12 fragment reads, 32 MFMAs
-//    64 rows: 1 x 4 waves of  64 x  64; 5 copies,  8 fragment reads, 16 MFMAs
+// Wave layout and work per 32-K step (per wave):
+//   256 rows: 2 x 2 waves of 128 x 128; 16 fragment reads, 64 MFMAs
+//   128 rows: 1 x 4 waves of 128 x  64; 12 fragment reads, 32 MFMAs
+//    64 rows: 1 x 4 waves of  64 x  64;  8 fragment reads, 16 MFMAs
 // The accumulators live in AGPRs.  With a single wave per SIMD nothing hides
-// a stall, so each stage spreads its copies and fragment reads evenly between
-// its MFMAs instead of issuing them in bursts; shorter tiles (smaller stages)
-// keep more stages in flight.
+// a stall, so each step spreads its copies and fragment reads evenly between
+// its MFMAs instead of issuing them in bursts.
+//
+// Operand copies.  The copy path is limited by the cache lines each copy
+// instruction touches more than by bytes: a 1 KB weight block touches 8 lines,
+// while a 16-row x 32-K activation fragment (64 bytes of each of 16 gathered
+// rows) touches 16.  So the activation rows are copied two K steps at a time,
+// 8 rows x 128 bytes (8 whole lines) per instruction, into a ring of "pair"
+// buffers holding steps 2p and 2p+1; the weights keep a ring of NS one-step
+// buffers.  Inside a fragment's 2 KB of a pair buffer, row r (of 16), K group
+// g (8 inputs) and step parity s sit at
+//   (r / 8) * 1024 + (r % 8) * 128 + ((4 s + g) ^ ((r / 2) % 8)) * 16,
+// so each row's 128 bytes of the pair are one 128-byte LDS line, filled by 8
+// consecutive lanes of a copy instruction (lane i writes offset 16 i and
+// fetches the piece that belongs there: 8 rows per instruction, one whole
+// cache line each), while the XOR spreads an MFMA operand read (lane l: row
+// l % 16, group l / 16) over all banks.
+//
+// Schedule: the copies issued at step kt are those of step j = kt + NS - 1
+// (clamped to the last step): its weight blocks and one half of an
+// activation pair (rows 0-7 of pair (j + 1) / 2 when j is odd, rows 8-15
+// when j is even), so every step issues the same number of copies.  At the
+// top of step kt a wave waits until the copies of steps up to kt + 1 have
+// landed, then a barrier makes every wave's copies visible; the fragments of
+// step kt + 1 are read during step kt.  A pair buffer is rewritten only after
+// the barrier that follows its last read (2 NPA >= NS + 1).
 
-// Scheduling pattern of one stage: group q of LPS issues one copy, then its
-// share of the NRD fragment reads, each preceded by a slice of the NMF MFMAs.
+// MFMA slices and LDS reads of one copy group: D reads, each preceded by a
+// share of M MFMAs, then the rest of the MFMAs.
+template <int I, int D, int M>
+__device__ __forceinline__ void group_pattern() {
+  if constexpr (I < D) {
+    constexpr int m = (I + 1) * M / (D + 1) - I * M / (D + 1);
+    if constexpr (m > 0) __builtin_amdgcn_sched_group_barrier(0x008, m, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    group_pattern<I + 1, D, M>();
+  } else {
+    constexpr int m = M - D * M / (D + 1);
+    if constexpr (m > 0) __builtin_amdgcn_sched_group_barrier(0x008, m, 0);
+  }
+}
+
+// Scheduling pattern of one step: group q of LPS issues one copy, then its
+// share of the NRD fragment reads interleaved with its share of the NMF MFMAs.
 template <int Q, int LPS, int NRD, int NMF>
 __device__ __forceinline__ void stage_pattern() {
   if constexpr (Q < LPS) {
     constexpr int d = (Q + 1) * NRD / LPS - Q * NRD / LPS;   // reads in this group
     constexpr int m = (Q + 1) * NMF / LPS - Q * NMF / LPS;   // MFMAs in this group
-    static_assert(d >= 1 && d <= 2 && m >= d + 1, "pattern");
     __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);       // one copy
-    if constexpr (d == 1) {
-      __builtin_amdgcn_sched_group_barrier(0x008, m / 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, m - m / 2, 0);
-    } else {
-      __builtin_amdgcn_sched_group_barrier(0x008, m / 3, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, (m - m / 3) / 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, m - m / 3 - (m - m / 3) / 2, 0);
-    }
+    group_pattern<0, d, m>();
     stage_pattern<Q + 1, LPS, NRD, NMF>();
   }
 }
 
-// One tile: WM x (4 / WM) waves, each MBW x NBW blocks of 16 x 16; NS ring
-// stages of one 32-K step each.
-template <bool GATED, int WM, int MBW, int NBW, int NS>
+// One tile: WM x (4 / WM) waves, each MBW x NBW blocks of 16 x 16; NS weight
+// steps and NPA activation pairs in LDS.
+template <bool GATED, int WM, int MBW, int NBW, int NS, int NPA>
 __device__ __forceinline__ void four_wave_tile(const GemmParams& p, uint8_t* lds, int g,
                                                int row_base, int rows, int m0, int nt) {
   constexpr int WN = 4 / WM;
   constexpr int BM = WM * MBW * 16;
-  constexpr int AFR = BM / 16;        // activation fragments per stage
-  constexpr int WBL = GM_BN / 16;     // weight blocks per stage
+  constexpr int AFR = BM / 16;        // activation fragments per step
+  constexpr int WBL = GM_BN / 16;     // weight blocks per step
   static_assert(WN * NBW == WBL, "tile width");
   constexpr int NH = GATED ? 2 : 1;
-  constexpr int A_BYTES = AFR * 1024;
-  constexpr int STAGE = A_BYTES + WBL * 1024;
-  constexpr int A_PER_WAVE = AFR / 4, B_PER_WAVE = WBL / 4;
-  constexpr int LPS = A_PER_WAVE + B_PER_WAVE;   // copies per wave per stage
-  constexpr int NRD = MBW + NBW;                 // fragment reads per wave per stage
-  constexpr int NMF = MBW * NBW;                 // MFMAs per wave per stage
-  static_assert(NS * STAGE <= FW_LDS, "LDS");
-  static_assert(NS >= 3 && (NS - 2) * LPS < 64, "ring");
+  constexpr int B_STEP = WBL * 1024;           // one weight step in LDS
+  constexpr int A_PAIR = AFR * 2048;           // one activation pair in LDS
+  constexpr int B_PER_WAVE = WBL / 4;          // weight copies per wave per step
+  constexpr int A_HALF = AFR / 4;              // activation copies per wave per step
+  constexpr int LPS = B_PER_WAVE + A_HALF;     // copies per wave per step
+  constexpr int NRD = MBW + NBW;               // fragment reads per wave per step
+  constexpr int NMF = MBW * NBW;               // MFMAs per wave per step
+  static_assert(NS * B_STEP + NPA * A_PAIR <= FW_LDS, "LDS");
+  static_assert(NS >= 3 && 2 * NPA >= NS + 1 && (NS - 2) * LPS < 64, "ring");
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave / WN, wn = wave % WN;
   const bool shared = g >= p.N;
   uint16_t* out = shared ? p.out_sh : p.out;
+  uint8_t* const bring = lds;
+  uint8_t* const aring = lds + NS * B_STEP;
 
   const int KT = p.K / 32;
   const size_t wbytes = (size_t)NH * p.n_out * p.K * 2;
   const uint8_t* W = shared ? p.w_sh : p.w + (size_t)g * wbytes;
   const size_t wstep = (size_t)NH * 1024;
 
-  // Operands are copied with buffer loads straight into LDS: the per-lane
-  // byte offsets stay in VGPRs for the whole loop and the K advance is a
-  // scalar offset, so a stage's copies need no address arithmetic.  Reads
+  // Copies are buffer loads straight into LDS: the per-lane byte offsets stay
+  // in VGPRs for the whole loop and the K advance is a scalar offset.  Reads
   // past a resource's size return zero.
   const __amdgpu_buffer_rsrc_t wres =
       __builtin_amdgcn_make_buffer_rsrc((void*)W, 0, (int)(uint32_t)wbytes, BUF_DWORD3);
@@ -445,18 +476,24 @@ __device__ __forceinline__ void four_wave_tile(const GemmParams& p, uint8_t* lds
       off = ((uint32_t)(nt * WBL + jb) * KT) * 1024;
     }
     boff[i] = off + lane * 16;
-    bdst[i] = A_BYTES + jb * 1024;
+    bdst[i] = jb * 1024;
   }
   const uint16_t* abase = shared ? p.a_sh : p.a;
   const uint32_t abytes = (uint32_t)((size_t)(shared ? rows : (p.perm ? p.T : row_base + rows)) * p.K * 2);
   const __amdgpu_buffer_rsrc_t ares =
       __builtin_amdgcn_make_buffer_rsrc((void*)abase, 0, (int)abytes, BUF_DWORD3);
-  uint32_t aoff[A_PER_WAVE];
-  int adst[A_PER_WAVE];
+  // activation copy (q, h) of this wave: fragment f = wave * A_HALF + q,
+  // rows 8 h .. 8 h + 7 of it, both steps of a pair; lane i fetches row
+  // r = 8 h + i / 8 and the 16 bytes (4 s + g) = (i % 8) ^ ((r / 2) % 8) of its
+  // 128 bytes
+  uint32_t aoff[A_HALF][2];
+  int adst[A_HALF][2];
 #pragma unroll
-  for (int i = 0; i < A_PER_WAVE; ++i) {
-    const int mb = wave * A_PER_WAVE + i;
-    const int r = min(m0 + mb * 16 + (lane & 15), rows - 1);  // rows past the end are not stored
+  for (int c = 0; c < 2 * A_HALF; ++c) {
+    const int q = c >> 1, h = c & 1;
+    const int f = wave * A_HALF + q;
+    const int rf = 8 * h + (lane >> 3);         // row within the fragment
+    const int r = min(m0 + f * 16 + rf, rows - 1);  // rows past the end are not stored
     int src;
     if (shared)
       src = r;
@@ -464,19 +501,33 @@ __device__ __forceinline__ void four_wave_tile(const GemmParams& p, uint8_t* lds
       src = p.perm[row_base + r];
     else
       src = row_base + r;
-    aoff[i] = (uint32_t)src * (uint32_t)p.K * 2 + (lane >> 4) * 16;
-    adst[i] = mb * 1024;
+    const int piece = (lane & 7) ^ ((rf >> 1) & 7);  // 4 s + g
+    aoff[q][h] = (uint32_t)src * (uint32_t)p.K * 2 + piece * 16;
+    adst[q][h] = f * 2048 + h * 1024;
   }
+  // operand read of lane l: row l % 16, K group l / 16 (activations: offset
+  // within a fragment's 2 KB for an even and an odd step)
+  const int rl = lane & 15, gl = lane >> 4;
+  const int a_rd0 = (rl >> 3) * 1024 + (rl & 7) * 128 + (gl ^ ((rl >> 1) & 7)) * 16;
+  const int a_rd1 = (rl >> 3) * 1024 + (rl & 7) * 128 + ((4 + gl) ^ ((rl >> 1) & 7)) * 16;
+
   typedef __attribute__((address_space(3))) void* lds_ptr_t;
-  // the q-th of a wave's LPS copies of stage kl into ring buffer buf
-  auto copy_one = [&](int q, int kl, int buf) {
-    uint8_t* base = lds + buf * STAGE;
-    if (q < A_PER_WAVE)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ares, (lds_ptr_t)(base + adst[q]), 16, aoff[q],
-                                               kl * 64, 0, 0);
-    else
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(wres, (lds_ptr_t)(base + bdst[q - A_PER_WAVE]), 16,
-                                               boff[q - A_PER_WAVE], kl * (int)wstep, 0, 0);
+  // copy number q of step j (weights first, then half (j + 1) % 2 of the
+  // activation pair (j + 1) / 2; j = -1 has only the latter)
+  auto copy_one = [&](int q, int j) {
+    if (q < B_PER_WAVE) {
+      const int kl = min(j, KT - 1);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          wres, (lds_ptr_t)(bring + (j % NS) * B_STEP + bdst[q]), 16, boff[q],
+          kl * (int)wstep, 0, 0);
+    } else {
+      const int pr = (j + 1) >> 1, h = (j + 1) & 1;
+      const int pl = min(pr, KT / 2 - 1);
+      const int qa = q - B_PER_WAVE;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          ares, (lds_ptr_t)(aring + (pr % NPA) * A_PAIR + adst[qa][h]), 16, aoff[qa][h],
+          pl * 128, 0, 0);
+    }
   };
 
   floatx4_t acc[MBW][NBW];
@@ -485,25 +536,25 @@ __device__ __forceinline__ void four_wave_tile(const GemmParams& p, uint8_t* lds
 #pragma unroll
     for (int j = 0; j < NBW; ++j) acc[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
   u32x4_t ca[MBW], cb[NBW], na[MBW], nb[NBW];
-  // fragment f of stage kt: f < MBW are activation blocks, the rest weight blocks
-  auto read_one = [&](u32x4_t (&fa)[MBW], u32x4_t (&fb)[NBW], int f, int kt) {
-    const uint8_t* base = lds + (kt % NS) * STAGE;
+  // fragment f of step kt: f < MBW are activation blocks, the rest weight blocks
+  // (odd: the parity of kt, known where it is called)
+  auto read_one = [&](u32x4_t (&fa)[MBW], u32x4_t (&fb)[NBW], int f, int kt, bool odd) {
     if (f < MBW)
-      fa[f] = *reinterpret_cast<const u32x4_t*>(base + ((wm * MBW + f) * 64 + lane) * 16);
+      fa[f] = *reinterpret_cast<const u32x4_t*>(aring + ((kt >> 1) % NPA) * A_PAIR +
+                                                (wm * MBW + f) * 2048 + (odd ? a_rd1 : a_rd0));
     else
       fb[f - MBW] = *reinterpret_cast<const u32x4_t*>(
-          base + A_BYTES + ((wn * NBW + f - MBW) * 64 + lane) * 16);
+          bring + (kt % NS) * B_STEP + ((wn * NBW + f - MBW) * 64 + lane) * 16);
   };
-  // Stage kt: wait until stage kt+1 has landed for every wave, then run
-  // stage kt's MFMAs with two streams interleaved: the copy of stage
-  // kt+NS-1 into the buffer of stage kt-1 (whose fragments the previous stage's
-  // MFMAs consumed) and the fragment reads of stage kt+1.  Every stage
-  // issues its copy, clamped to the last K step near the end, so that one
-  // vmcnt threshold holds throughout and no branch splits the schedule; the
-  // clamped copies only land in buffers no later stage reads, and the reads
-  // past the last stage land in registers that are never used.
-  auto stage = [&](const u32x4_t (&fa)[MBW], const u32x4_t (&fb)[NBW], u32x4_t (&ga)[MBW],
-                   u32x4_t (&gb)[NBW], int kt) {
+  // Step kt (PAR = kt & 1): wait until the copies of step kt+1 have landed for
+  // every wave, then run step kt's MFMAs with two streams interleaved: the
+  // copies of step kt+NS-1 and the fragment reads of step kt+1.  The clamped
+  // copies near the end only land in buffers no later step reads, and the
+  // reads past the last step land in registers that are never used.
+  auto stage = [&](auto par, const u32x4_t (&fa)[MBW], const u32x4_t (&fb)[NBW],
+                   u32x4_t (&ga)[MBW], u32x4_t (&gb)[NBW], int kt) {
+    constexpr int PAR = decltype(par)::value;
+    // copies still allowed in flight: those of steps kt+2 .. kt+NS-2
     wait_vmcnt<(NS - 3) * LPS>();
     barrier_no_fence();
     __builtin_amdgcn_sched_barrier(0);
@@ -511,9 +562,10 @@ __device__ __forceinline__ void four_wave_tile(const GemmParams& p, uint8_t* lds
     // not move an LDS read past a copy into LDS
 #pragma unroll
     for (int q = 0; q < LPS; ++q) {
-      copy_one(q, min(kt + NS - 1, KT - 1), (kt + NS - 1) % NS);
+      copy_one(q, kt + NS - 1);
 #pragma unroll
-      for (int f = q * NRD / LPS; f < (q + 1) * NRD / LPS; ++f) read_one(ga, gb, f, kt + 1);
+      for (int f = q * NRD / LPS; f < (q + 1) * NRD / LPS; ++f)
+        read_one(ga, gb, f, kt + 1, PAR == 0);
     }
 #pragma unroll
     for (int i = 0; i < MBW; ++i)
@@ -525,19 +577,21 @@ __device__ __forceinline__ void four_wave_tile(const GemmParams& p, uint8_t* lds
 
   // K/32 is even (and at least 4) for every accepted shape
 #pragma unroll
-  for (int st = 0; st < NS - 1; ++st)
+  for (int q = B_PER_WAVE; q < LPS; ++q) copy_one(q, -1);
 #pragma unroll
-    for (int q = 0; q < LPS; ++q) copy_one(q, min(st, KT - 1), st);
-  wait_vmcnt<(NS - 2) * LPS>();
+  for (int j = 0; j < NS - 1; ++j)
+#pragma unroll
+    for (int q = 0; q < LPS; ++q) copy_one(q, j);
+  wait_vmcnt<(NS - 2) * LPS>();  // the copies of steps -1 and 0 have landed
   barrier_no_fence();
 #pragma unroll
-  for (int f = 0; f < NRD; ++f) read_one(ca, cb, f, 0);
+  for (int f = 0; f < NRD; ++f) read_one(ca, cb, f, 0, false);
 
   for (int kt = 0; kt < KT; kt += 2) {
-    stage(ca, cb, na, nb, kt);
-    stage(na, nb, ca, cb, kt + 1);
+    stage(std::integral_constant<int, 0>{}, ca, cb, na, nb, kt);
+    stage(std::integral_constant<int, 1>{}, na, nb, ca, cb, kt + 1);
   }
-  wait_vmcnt<0>();  // the clamped copies of the last stages
+  wait_vmcnt<0>();  // the clamped copies of the last steps
 
 #pragma unroll
   for (int i = 0; i < MBW; ++i) {
@@ -586,11 +640,11 @@ __global__ __launch_bounds__(256, 1) void ffn_gemm_big_kernel(GemmParams p) {
   group_rows(p, g, row_base, rows);
   const int left = rows - m0;   // rows from this tile on (> 0)
   if (left > 128)
-    four_wave_tile<GATED, 2, 8, 8, 4>(p, lds, g, row_base, rows, m0, nt);
+    four_wave_tile<GATED, 2, 8, 8, 4, 3>(p, lds, g, row_base, rows, m0, nt);
   else if (left > 64)
-    four_wave_tile<GATED, 1, 8, 4, 5>(p, lds, g, row_base, rows, m0, nt);
+    four_wave_tile<GATED, 1, 8, 4, 5, 3>(p, lds, g, row_base, rows, m0, nt);
   else
-    four_wave_tile<GATED, 1, 4, 4, 6>(p, lds, g, row_base, rows, m0, nt);
+    four_wave_tile<GATED, 1, 4, 4, 6, 4>(p, lds, g, row_base, rows, m0, nt);
 }
 
 template <int BM, bool FP8>

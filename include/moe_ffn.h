@@ -86,9 +86,10 @@ typedef struct {
 } moe_shape_t;
 
 /* Device pointers to the layer's parameters.  Expert weights are in the
- * packed layout written by moe_pack_weights(); scales stay in their natural
- * layout: FP8 float32 [E][rows/128][cols/128], MXFP4 E8M0 bytes
- * [E][rows][cols/32] (value 2^(byte - 127)). */
+ * packed layout written by moe_pack_weights().  FP8 scales stay in their
+ * natural layout, float32 [E][rows/128][cols/128]; MXFP4 scales (E8M0 bytes,
+ * value 2^(byte - 127), one per 32 inputs of a row) are passed packed by
+ * moe_pack_weights() with which = 2 or 3. */
 typedef struct {
   const float* w_router;     /* [d][N]                                    */
   const float* logit_offset; /* [N] added to the logits, or NULL          */
@@ -96,9 +97,9 @@ typedef struct {
   const void* w13;           /* packed gate+up of the N routed experts     */
   const void* w2;            /* packed down of the N routed experts        */
   const void* w13_scale;     /* FP8: f32 [N][2][d_ff/128][d/128] gate, up;
-                                MXFP4: u8 [N][2][d_ff][d/32]               */
+                                MXFP4: packed (which = 2), 16-byte aligned */
   const void* w2_scale;      /* FP8: f32 [N][d/128][d_ff/128];
-                                MXFP4: u8 [N][d][d_ff/32]                  */
+                                MXFP4: packed (which = 3), 16-byte aligned */
   const void* w13_shared;    /* packed gate+up of the shared expert / NULL */
   const void* w2_shared;     /* packed down of the shared expert / NULL    */
   const void* w13_shared_scale; /* scales of the shared expert / NULL      */
@@ -116,8 +117,10 @@ typedef struct {
   int32_t* inv_perm;   /* [T][k] row of each (token, slot)                 */
 } moe_routing_t;
 
-/* Bytes of one packed expert-weight buffer for `n_mats` experts:
- * which = 0 -> gate+up (w13), which = 1 -> down (w2).  0 on a bad shape. */
+/* Bytes of one packed buffer for `n_mats` experts: which = 0 -> gate+up
+ * (w13), which = 1 -> down (w2); MXFP4 only: which = 2 -> gate+up scales,
+ * which = 3 -> down scales.  0 on a bad shape or a which the weight type
+ * does not have. */
 size_t moe_packed_weight_bytes(const moe_shape_t* s, int which, int n_mats);
 
 /* Repack expert weights from [out][in] row-major into the kernels' layout
@@ -125,7 +128,13 @@ size_t moe_packed_weight_bytes(const moe_shape_t* s, int which, int n_mats);
  * [n_mats][d_ff][d], src_b = W_up [n_mats][d_ff][d]; which = 1: src_a =
  * W_down [n_mats][d][d_ff], src_b = NULL.  Elements are of s->w_dtype (FP8:
  * uint8 E4M3 codes; MXFP4: [out][in/2] bytes of two E2M1 codes, input 2j in
- * the low nibble).  dst must hold moe_packed_weight_bytes(s, which,
+ * the low nibble).  MXFP4 scales: which = 2: src_a = [n_mats][2][d_ff][d/32]
+ * bytes (gate then up), which = 3: src_a = [n_mats][d][d_ff/32], src_b =
+ * NULL; they are regrouped so that the 16 rows of a weight block and four
+ * 128-wide K steps are 256 contiguous bytes (rows in order, 16 bytes each,
+ * a last partial group padded with zeros) - the streaming kernel then
+ * fetches a lane's scales of four steps with one 16-byte load.  Any other
+ * weight type returns MOE_ERR_UNSUPPORTED for which 2 and 3.  dst must hold moe_packed_weight_bytes(s, which,
  * n_mats) bytes and must not overlap the sources.  Each expert is a
  * separately addressed block, so an unselected expert's bytes are never
  * read ([MoE-EXP] "Why heads cannot be sparsified the same way"). */

@@ -256,7 +256,12 @@ const char* moe_status_string(moe_status_t st) {
 const char* moe_last_error(void) { return g_err; }
 
 size_t moe_packed_weight_bytes(const moe_shape_t* s, int which, int n_mats) {
-  if (check_shape(s) != MOE_OK || (which != 0 && which != 1) || n_mats < 1) return 0;
+  if (check_shape(s) != MOE_OK || which < 0 || which > 3 || n_mats < 1) return 0;
+  if (which >= 2) {
+    if (s->w_dtype != MOE_MXFP4) return 0;
+    return which == 2 ? packed_scale_bytes(n_mats, s->d_ff, s->d_model, 2)
+                      : packed_scale_bytes(n_mats, s->d_model, s->d_ff, 1);
+  }
   const size_t elems = (size_t)s->d_model * s->d_ff * (which == 0 ? 2 : 1);
   const size_t per = w_size(s) ? elems * w_size(s) : elems / 2;
   return per * (size_t)n_mats;
@@ -266,9 +271,19 @@ moe_status_t moe_pack_weights(const moe_shape_t* s, int which, int n_mats, const
                               const void* src_b, void* dst, hipStream_t stream) {
   moe_status_t st = check_shape(s);
   if (st != MOE_OK) return st;
-  if (which != 0 && which != 1) return fail(MOE_ERR_INVALID_ARG, "which must be 0 or 1");
+  if (which < 0 || which > 3) return fail(MOE_ERR_INVALID_ARG, "which must be 0, 1, 2 or 3");
   if (n_mats < 1) return fail(MOE_ERR_INVALID_ARG, "n_mats must be >= 1");
   if (!src_a || !dst) return fail(MOE_ERR_INVALID_ARG, "src_a / dst is NULL");
+  if (which >= 2) {
+    if (s->w_dtype != MOE_MXFP4)
+      return fail(MOE_ERR_UNSUPPORTED, "scale packing (which 2, 3) is for MXFP4 weights only");
+    if (src_b) return fail(MOE_ERR_INVALID_ARG, "src_b must be NULL for which 2 and 3");
+    const int rows = which == 2 ? s->d_ff : s->d_model;
+    const int cols = which == 2 ? s->d_model : s->d_ff;
+    HIP_TRY("pack scales", launch_pack_scales(src_a, dst, n_mats, rows, cols, which == 2 ? 2 : 1,
+                                              stream));
+    return MOE_OK;
+  }
   if ((which == 0) != (src_b != nullptr))
     return fail(MOE_ERR_INVALID_ARG, "src_b is W_up for which == 0 and NULL for which == 1");
   const int rows = which == 0 ? s->d_ff : s->d_model;

@@ -124,14 +124,19 @@ __device__ __forceinline__ void stream_body(const StreamParams& p, int nb0, int 
     S = (shared ? static_cast<const float*>(p.s_sh)
                 : static_cast<const float*>(p.s) + (size_t)g * NH * SR * SK) +
         (size_t)((nb0 * 16) / MOE_FP8_BLOCK) * SK;
-  // MXFP4: one E8M0 byte per 32 inputs of a row, [NH][n_out][K/32] per
-  // group; a lane reads the 4 bytes of its row for one 128-wide step
-  const int SK32 = p.K / 32;
+  // MXFP4: one E8M0 byte per 32 inputs of a row, packed per group as
+  // [row block][group of 4 K steps][NH][16 rows][16 bytes]; a lane's scales
+  // of four steps are one 16-byte chunk, of one step 4 bytes of it
+  const int KQ = (p.K / 32 + 15) / 16;
   const uint8_t* S4 = nullptr;
   if (FP4)
     S4 = (shared ? static_cast<const uint8_t*>(p.s_sh)
-                 : static_cast<const uint8_t*>(p.s) + (size_t)g * NH * p.n_out * SK32) +
-         (size_t)(nb0 * 16 + (lane & 15)) * SK32;
+                 : static_cast<const uint8_t*>(p.s) + (size_t)g * NH * p.n_out * KQ * 16) +
+         (size_t)nb0 * KQ * NH * 256 + (lane & 15) * 16;
+  // chunk of block nb0 + j, matrix h, K steps 4 kq .. 4 kq + 3
+  auto s4_chunk = [&](int j, int h, int kq) {
+    return S4 + ((size_t)(j * KQ + kq) * NH + h) * 256;
+  };
 
   const int lrow = lane & 15;
   const int lk = (lane >> 4) * 8;
@@ -219,8 +224,7 @@ __device__ __forceinline__ void stream_body(const StreamParams& p, int nb0, int 
       for (int j = 0; j < (SQ4 ? NP : 0); ++j)
 #pragma unroll
         for (int h = 0; h < NH; ++h)
-          q[j][h] = *reinterpret_cast<const u32x4_t*>(S4 + ((size_t)h * p.n_out + j * 16) * SK32 +
-                                                      ks * 4);
+          q[j][h] = *reinterpret_cast<const u32x4_t*>(s4_chunk(j, h, ks >> 2));
     };
     if (SQ4) load_sq4(sqn, 0);
     auto load_step = [&](int u, int ks) {
@@ -231,8 +235,8 @@ __device__ __forceinline__ void stream_body(const StreamParams& p, int nb0, int 
           bq[u][j][h] =
               *reinterpret_cast<const u32x4_t*>(Wnb + j * bstride + ((size_t)ks * NH + h) * 1024);
           if (FP4 && !SQ4)
-            sq[FP4 && !SQ4 ? u : 0][j][h] = *reinterpret_cast<const uint32_t*>(
-                S4 + ((size_t)h * p.n_out + j * 16) * SK32 + ks * 4);
+            sq[FP4 && !SQ4 ? u : 0][j][h] =
+                *reinterpret_cast<const uint32_t*>(s4_chunk(j, h, ks >> 2) + (ks & 3) * 4);
         }
       if (FP8 && (u & 1)) {
 #pragma unroll

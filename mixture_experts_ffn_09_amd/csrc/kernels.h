@@ -107,5 +107,10 @@ hipError_t launch_combine(const void* y_perm, const void* y_shared, const int32_
                           hipStream_t st);
 
 // Weight repack (see moe_pack_weights).  esize: 4 (f32), 2 (bf16), 1 (fp8).
+// MXFP4 scales: natural [n_mats][nh][rows][cols/32] bytes -> the packed
+// layout the streaming kernel reads (16 rows x 16 bytes per 256-byte chunk)
+size_t packed_scale_bytes(int n_mats, int rows, int cols, int nh);
+hipError_t launch_pack_scales(const void* src, void* dst, int n_mats, int rows, int cols, int nh,
+                              hipStream_t st);
 hipError_t launch_pack(const void* src_a, const void* src_b, void* dst, int n_mats, int rows,
                        int cols, int esize, hipStream_t st);

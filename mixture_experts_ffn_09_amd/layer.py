@@ -79,9 +79,9 @@ def build_device_layer(cfg: MoEConfig, threads: int = 16) -> DeviceLayer:
         sr13 = 2 * (cfg.d_ff // 128) * (cfg.d_model // 128)
         sr2 = (cfg.d_model // 128) * (cfg.d_ff // 128)
         sdt = torch.float32
-    else:     # MXFP4: one E8M0 byte per 32 inputs of a row
-        sr13 = 2 * cfg.d_ff * (cfg.d_model // 32)
-        sr2 = cfg.d_model * (cfg.d_ff // 32)
+    else:     # MXFP4: E8M0 bytes, repacked by the library (which = 2, 3)
+        sr13 = moe.moe_packed_weight_bytes(one, 2, 1)
+        sr2 = moe.moe_packed_weight_bytes(one, 3, 1)
         sdt = torch.uint8
     if scaled:
         t["w13_scale"] = torch.empty(N * sr13, dtype=sdt, device=dev)
@@ -105,12 +105,14 @@ def build_device_layer(cfg: MoEConfig, threads: int = 16) -> DeviceLayer:
         if scaled:
             s13 = torch.cat([w["gate_scale"].reshape(-1), w["up_scale"].reshape(-1)]).to(dev)
             s2 = w["down_scale"].reshape(-1).to(dev)
-            if shared:
-                t["w13_shared_scale"].copy_(s13)
-                t["w2_shared_scale"].copy_(s2)
-            else:
-                t["w13_scale"][e * sr13:(e + 1) * sr13].copy_(s13)
-                t["w2_scale"][e * sr2:(e + 1) * sr2].copy_(s2)
+            d13 = t["w13_shared_scale"] if shared else t["w13_scale"][e * sr13:(e + 1) * sr13]
+            d2 = t["w2_shared_scale"] if shared else t["w2_scale"][e * sr2:(e + 1) * sr2]
+            if fp8:   # natural layout
+                d13.copy_(s13)
+                d2.copy_(s2)
+            else:     # natural [2][d_ff][d/32] and [d][d_ff/32] bytes -> packed
+                moe.moe_pack_weights(one, 2, 1, s13, None, d13)
+                moe.moe_pack_weights(one, 3, 1, s2, None, d2)
         torch.cuda.current_stream().synchronize()  # sources may be freed next
 
     for_each_expert(cfg, upload, threads=threads)

@@ -118,8 +118,11 @@ def test_null_shape_and_pointers():
         moe.MOE_ERR_INVALID_ARG
     assert _status("moe_pack_weights", C.byref(s), 1, 1, FAKE, FAKE, FAKE, None) == \
         moe.MOE_ERR_INVALID_ARG
-    assert _status("moe_pack_weights", C.byref(s), 2, 1, FAKE, None, FAKE, None) == \
+    assert _status("moe_pack_weights", C.byref(s), 5, 1, FAKE, None, FAKE, None) == \
         moe.MOE_ERR_INVALID_ARG
+    # which = 2, 3 (scale packing) exists for MXFP4 weights only
+    assert _status("moe_pack_weights", C.byref(s), 2, 1, FAKE, None, FAKE, None) == \
+        moe.MOE_ERR_UNSUPPORTED
 
 
 def test_workspace_too_small():
@@ -170,6 +173,33 @@ def test_packed_sizes():
     assert moe.moe_packed_weight_bytes(s, 1, 1) == d * f * 2
     s8 = shape(w_dtype="fp8")
     assert moe.moe_packed_weight_bytes(s8, 1, 2) == 2 * 4096 * 14336
+    # scale packing exists for MXFP4 only
+    assert moe.moe_packed_weight_bytes(s, 2, 1) == 0
+    assert moe.moe_packed_weight_bytes(s8, 3, 1) == 0
+    assert moe.moe_packed_weight_bytes(s, 4, 1) == 0
+
+
+def test_packed_mxfp4_scale_sizes():
+    # rows x ceil(cols / 512) chunks of 16 bytes (one byte per 32 inputs,
+    # padded to a whole group of four 128-wide K steps)
+    s4 = shape(w_dtype="mxfp4")      # d 4096, d_ff 14336: no padding
+    assert moe.moe_packed_weight_bytes(s4, 2, 3) == 3 * 2 * 14336 * (4096 // 32)
+    assert moe.moe_packed_weight_bytes(s4, 3, 1) == 4096 * (14336 // 32)
+    s4p = shape(w_dtype="mxfp4", d_model=384, d_ff=640)
+    assert moe.moe_packed_weight_bytes(s4p, 2, 1) == 2 * 640 * 16
+    assert moe.moe_packed_weight_bytes(s4p, 3, 2) == 2 * 384 * 32
+    assert moe.moe_packed_weight_bytes(s4p, 0, 1) == 2 * 384 * 640 // 2
+
+
+def test_pack_scale_argument_checks():
+    call = lambda *a: _status("moe_pack_weights", *a)
+    s = shape()
+    assert call(C.byref(s), 2, 1, FAKE, None, FAKE, None) == moe.MOE_ERR_UNSUPPORTED
+    s4 = shape(w_dtype="mxfp4")
+    assert call(C.byref(s4), 2, 1, FAKE, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert call(C.byref(s4), 3, 1, None, None, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert call(C.byref(s4), 4, 1, FAKE, None, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert call(C.byref(s4), 2, 0, FAKE, None, FAKE, None) == moe.MOE_ERR_INVALID_ARG
 
 
 def test_zero_tokens_needs_no_device():

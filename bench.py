@@ -90,6 +90,33 @@ def measured_traffic(workload: str):
     return rec["traffic_bytes_per_launch"]
 
 
+def achievable(torch):
+    """Measured ceilings on this GPU beside the spec peaks: a plain device copy
+    of 1 GiB (read + write bytes over its time) and a dense 8192^3 bf16
+    matrix product (the vendor BLAS, contiguous operands)."""
+    n = 1 << 30
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    a = torch.randn(8192, 8192, device="cuda").to(torch.bfloat16)
+    b = torch.randn(8192, 8192, device="cuda").to(torch.bfloat16)
+    out = {}
+    for name, fn, work in (("hbm_copy_GBps", lambda: torch.mul(src, 1.0, out=dst), 2 * n / 1e9),
+                           ("mfma_bf16_TFLOPs", lambda: torch.matmul(a, b), 2 * 8192 ** 3 / 1e12)):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        out[name] = round(work / (e0.elapsed_time(e1) / 10 * 1e-3), 1)
+    del src, dst, a, b
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(cfg, x_cpu, n_tokens: int):
     """Time the CPU oracle (as it stands) on a bounded sample of the same
     workload: the first n_tokens tokens, weights decoded from their stored
@@ -313,6 +340,10 @@ def main():
     roof = roofline_for(cfg, st[dom], stage_ms[dom])
     roof["traffic"] = measured_traffic(cfg.name)
     roof["kernel"] = "expert gate/up + SwiGLU (moe_expert_gate_up)"
+    ach = achievable(torch)
+    ach_peak = ach["hbm_copy_GBps"] if roof["bound"] == "hbm" else ach["mfma_bf16_TFLOPs"]
+    if roof["bound"] in ("hbm", "mfma"):
+        ach["dominant_kernel_frac_of_achievable"] = round(roof["achieved"] / ach_peak, 4)
     layer_gbs = layer["bytes"] / (ms_step * 1e-3) / 1e9
     layer_tflops = layer["flops"] / (ms_step * 1e-3) / 1e12
 
@@ -328,6 +359,7 @@ def main():
                    "weights": cfg.w_dtype, "experts_touched": touched,
                    "max_over_mean_load": round(float(counts.max()) / max(1e-9, float(counts.float().mean())), 3)},
         "roofline": roof,
+        "achievable": ach,
         "layer": {"algorithmic_bytes": layer["bytes"], "flops": layer["flops"],
                   "hbm_GBps": round(layer_gbs, 1), "hbm_frac": round(layer_gbs / PEAK_HBM_GBS, 4),
                   "TFLOPs": round(layer_tflops, 2),

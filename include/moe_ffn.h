@@ -145,7 +145,9 @@ moe_status_t moe_pack_weights(const moe_shape_t* s, int which, int n_mats,
 /* Workspace bytes moe_layer_forward / moe_grouped_ffn / moe_router_topk need
  * for this shape (0 when n_tokens == 0); each of them checks ws_bytes against
  * it.  Returns (size_t)-1 on a bad shape.  Layout (256-byte aligned pieces):
- * router partial logits [S][T][N] f32 (S >= 1 K-splits), topk idx/w,
+ * router partial logits [S][T][N] f32 (S >= 1 K-splits; for N > 8 with
+ * bfloat16 x followed, 256-aligned, by the router weight split into three
+ * bfloat16 planes, ceil(d/32) * ceil(N/16) * 3 KB), topk idx/w,
  * counts, offsets, perm_token, inv_perm, per-256-token-block expert counts
  * [ceil(T/256)][N] int32, per-16-token-block probability sums
  * [ceil(T/16)][N] f32, a second counts / offsets / perm_token / inv_perm

@@ -95,8 +95,8 @@ WsLayout ws_layout(const moe_shape_t* s) {
   };
   const size_t T = s->n_tokens, k = s->top_k, N = s->n_experts, d = s->d_model, f = s->d_ff;
   const size_t es = act_size(s), sh = s->n_shared;
-  L.logits = take((size_t)router_splits(s->n_tokens, s->n_experts, s->d_model,
-                                        s->act_dtype == MOE_BF16) * T * N * 4);
+  L.logits = take(router_scratch_bytes(s->n_tokens, s->n_experts, s->d_model,
+                                       s->act_dtype == MOE_BF16));
   L.idx = take(T * k * 4);
   L.w = take(T * k * 4);
   L.counts = take(N * 4);

@@ -8,6 +8,9 @@
 // Router logits x[T][d] @ W[d][N] in float32 as router_splits() partial
 // sums over K: partial[S][T][N].  act_bf16: x is bfloat16 (else float32).
 int router_splits(int T, int N, int d, bool act_bf16);
+// bytes of router scratch: the partial logits, and for N > 8 with bf16 x the
+// router weight split into three bf16 planes (after the logits, 256-aligned)
+size_t router_scratch_bytes(int T, int N, int d, bool act_bf16);
 hipError_t launch_router_logits(const void* x, bool act_bf16, const float* w_router,
                                 float* partial, int T, int d, int N, hipStream_t st);
 

@@ -92,9 +92,11 @@ __global__ __launch_bounds__(256) void router_logits_small_n(const void* __restr
 // bf16 activations, N > 8: the float32 router weight is split exactly into
 // three bfloat16 planes (w = hi + mid + lo, 8 significand bits each), so each
 // product x * plane is exact in float32 (x is bf16) and three
-// v_mfma_f32_16x16x32_bf16 per step give the float32 dot product.  64 tokens
-// x 64 experts per workgroup (2 x 2 waves of 32 x 32); the weight slice is
-// split into the planes while it is staged in LDS in B-operand order;
+// v_mfma_f32_16x16x32_bf16 per step give the float32 dot product.  The split
+// runs once per call (router_split_kernel) into scratch, already in B-operand
+// order ([32-K step][16-expert block][plane][64 lanes][8 bf16], zero-padded),
+// instead of once per token tile.  64 tokens x 64 experts per workgroup
+// (2 x 2 waves of 32 x 32); the planes of the slice are staged in LDS;
 // activations load straight into A operands.  Optional split over K.
 // ---------------------------------------------------------------------------
 constexpr int RM_TM = 64, RM_TN = 64, RM_BK = 64;
@@ -107,10 +109,40 @@ __device__ __forceinline__ void split3_bf16(float w, uint32_t& h, uint32_t& m, u
   l = f32_to_bf16(r2);
 }
 
+// one thread per (32-K step, 16-expert block, lane): its 8 weights in the
+// three planes
+__global__ __launch_bounds__(256) void router_split_kernel(const float* __restrict__ w,
+                                                           uint16_t* __restrict__ planes, int d,
+                                                           int N, int NB, size_t total) {
+  const size_t c = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (c >= total) return;
+  const int l = (int)(c & 63);
+  const int nb = (int)((c >> 6) % NB);
+  const int ks = (int)((c >> 6) / NB);
+  const int e = nb * 16 + (l & 15);
+  const int kb = ks * 32 + (l >> 4) * 8;
+  uint32_t hh[4], mm[4], ll[4];
+#pragma unroll
+  for (int j = 0; j < 8; j += 2) {
+    const float w0 = (e < N && kb + j < d) ? w[(size_t)(kb + j) * N + e] : 0.f;
+    const float w1 = (e < N && kb + j + 1 < d) ? w[(size_t)(kb + j + 1) * N + e] : 0.f;
+    uint32_t h0, m0, l0, h1, m1, l1;
+    split3_bf16(w0, h0, m0, l0);
+    split3_bf16(w1, h1, m1, l1);
+    hh[j / 2] = h0 | (h1 << 16);
+    mm[j / 2] = m0 | (m1 << 16);
+    ll[j / 2] = l0 | (l1 << 16);
+  }
+  uint16_t* out = planes + (((size_t)ks * NB + nb) * 3 * 64 + l) * 8;
+  *reinterpret_cast<u32x4_t*>(out) = u32x4_t{hh[0], hh[1], hh[2], hh[3]};
+  *reinterpret_cast<u32x4_t*>(out + 64 * 8) = u32x4_t{mm[0], mm[1], mm[2], mm[3]};
+  *reinterpret_cast<u32x4_t*>(out + 2 * 64 * 8) = u32x4_t{ll[0], ll[1], ll[2], ll[3]};
+}
+
 __global__ __launch_bounds__(256) void router_logits_mfma(const uint16_t* __restrict__ x,
-                                                          const float* __restrict__ w,
+                                                          const uint16_t* __restrict__ planes,
                                                           float* __restrict__ partial, int T,
-                                                          int d, int N, int KC) {
+                                                          int d, int N, int NB, int KC) {
   // [plane][k step][n block][64 lanes][8 bf16]
   __shared__ __attribute__((aligned(16))) uint16_t wl[3][RM_BK / 32][RM_TN / 16][64 * 8];
   const int tid = threadIdx.x;
@@ -131,40 +163,50 @@ __global__ __launch_bounds__(256) void router_logits_mfma(const uint16_t* __rest
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
-  for (int k0 = k_begin; k0 < k_end; k0 += RM_BK) {
-    // stage: each thread fills two B-operand lane slots (8 K values of one
-    // expert) in all three planes
+  // Operands of one 64-K chunk in registers: this lane's A fragments (2 K
+  // steps x its 2 token blocks; d is a multiple of 8, so a lane's 8 inputs
+  // are all in range or all out) and its two B-operand lane slots of all
+  // three planes (steps past this split's end and expert blocks past the last
+  // are zero).  The next chunk's are loaded while this one is multiplied.
+  auto load_chunk = [&](int k0, u32x4_t (&a)[2][2], u32x4_t (&b)[2][3]) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int kk = k0 + ks * 32;
+      const bool ain = kk + (lane >> 4) * 8 < k_end;
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        a[ks][i] = ain ? *reinterpret_cast<const u32x4_t*>(arow[i] + kk) : u32x4_t{0, 0, 0, 0};
+    }
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
       const int slot = tid + 256 * r;          // 0 .. 511
       const int frag = slot >> 6, l = slot & 63;
       const int ks = frag / (RM_TN / 16), nb = frag % (RM_TN / 16);
-      const int e = e0 + nb * 16 + (l & 15);
-      const int kb = k0 + ks * 32 + (l >> 4) * 8;
-      uint32_t hh[4], mm[4], ll[4];
+      const int gks = k0 / 32 + ks, gnb = e0 / 16 + nb;
+      const bool in = gks * 32 < k_end && gnb < NB;
+      const uint16_t* src = planes + (((size_t)gks * NB + gnb) * 3 * 64 + l) * 8;
 #pragma unroll
-      for (int j = 0; j < 8; j += 2) {
-        const float w0 = (e < N && kb + j < k_end) ? w[(size_t)(kb + j) * N + e] : 0.f;
-        const float w1 = (e < N && kb + j + 1 < k_end) ? w[(size_t)(kb + j + 1) * N + e] : 0.f;
-        uint32_t h0, m0, l0, h1, m1, l1;
-        split3_bf16(w0, h0, m0, l0);
-        split3_bf16(w1, h1, m1, l1);
-        hh[j / 2] = h0 | (h1 << 16);
-        mm[j / 2] = m0 | (m1 << 16);
-        ll[j / 2] = l0 | (l1 << 16);
-      }
-      *reinterpret_cast<u32x4_t*>(&wl[0][ks][nb][l * 8]) = u32x4_t{hh[0], hh[1], hh[2], hh[3]};
-      *reinterpret_cast<u32x4_t*>(&wl[1][ks][nb][l * 8]) = u32x4_t{mm[0], mm[1], mm[2], mm[3]};
-      *reinterpret_cast<u32x4_t*>(&wl[2][ks][nb][l * 8]) = u32x4_t{ll[0], ll[1], ll[2], ll[3]};
+      for (int pl = 0; pl < 3; ++pl)
+        b[r][pl] = in ? *reinterpret_cast<const u32x4_t*>(src + pl * 64 * 8) : u32x4_t{0, 0, 0, 0};
     }
+  };
+  u32x4_t ac[2][2], bc[2][3], an[2][2], bn[2][3];
+  load_chunk(k_begin, ac, bc);
+  for (int k0 = k_begin; k0 < k_end; k0 += RM_BK) {
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int slot = tid + 256 * r;
+      const int frag = slot >> 6, l = slot & 63;
+      const int ks = frag / (RM_TN / 16), nb = frag % (RM_TN / 16);
+#pragma unroll
+      for (int pl = 0; pl < 3; ++pl) *reinterpret_cast<u32x4_t*>(&wl[pl][ks][nb][l * 8]) = bc[r][pl];
+    }
+    // the next chunk (clamped: the last one is loaded again and not used)
+    load_chunk(min(k0 + RM_BK, k_end - 1) / 32 * 32, an, bn);
     __syncthreads();
 #pragma unroll
     for (int ks = 0; ks < RM_BK / 32; ++ks) {
-      const int kk = k0 + ks * 32;
-      if (kk >= k_end) break;  // K chunks are multiples of 32
-      u32x4_t a[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i) a[i] = *reinterpret_cast<const u32x4_t*>(arow[i] + kk);
+      if (k0 + ks * 32 >= k_end) break;  // K chunks are multiples of 32
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int nb = wn * 2 + j;
@@ -172,11 +214,19 @@ __global__ __launch_bounds__(256) void router_logits_mfma(const uint16_t* __rest
         for (int pl = 0; pl < 3; ++pl) {
           const u32x4_t b = *reinterpret_cast<const u32x4_t*>(&wl[pl][ks][nb][lane * 8]);
 #pragma unroll
-          for (int i = 0; i < 2; ++i) acc[i][j] = mfma16x16x32(a[i], b, acc[i][j]);
+          for (int i = 0; i < 2; ++i) acc[i][j] = mfma16x16x32(ac[ks][i], b, acc[i][j]);
         }
       }
     }
     __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int i = 0; i < 2; ++i) ac[ks][i] = an[ks][i];
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+      for (int pl = 0; pl < 3; ++pl) bc[r][pl] = bn[r][pl];
   }
   // lane holds rows 4*(lane/16)+q of column lane%16
 #pragma unroll
@@ -420,6 +470,18 @@ int router_splits(int T, int N, int d, bool act_bf16) {
   return ceil_div(d, KC);
 }
 
+// bytes of the pre-split weight planes (MFMA path only)
+static size_t router_plane_bytes(int N, int d) {
+  return (size_t)ceil_div(d, 32) * ceil_div(N, 16) * 3 * 1024;
+}
+
+static size_t align256_sz(size_t v) { return (v + 255) / 256 * 256; }
+
+size_t router_scratch_bytes(int T, int N, int d, bool act_bf16) {
+  const size_t logits = (size_t)router_splits(T, N, d, act_bf16) * T * N * 4;
+  return N > 8 && act_bf16 ? align256_sz(logits) + router_plane_bytes(N, d) : logits;
+}
+
 static int router_chunk(int T, int N, int d, bool act_bf16) {
   const int S = router_splits(T, N, d, act_bf16);
   return ceil_div(ceil_div(d, S), 64) * 64;
@@ -446,8 +508,15 @@ hipError_t launch_router_logits(const void* x, bool act_bf16, const float* w_rou
     }
   } else if (act_bf16) {
     dim3 grid(ceil_div(T, RM_TM), ceil_div(N, RM_TN), S);
-    router_logits_mfma<<<grid, 256, 0, st>>>(static_cast<const uint16_t*>(x), w_router, partial,
-                                             T, d, N, KC);
+    // planes live after the partial logits in the router's scratch
+    const int NB = ceil_div(N, 16);
+    uint16_t* planes = reinterpret_cast<uint16_t*>(reinterpret_cast<char*>(partial) +
+                                                   align256_sz((size_t)S * T * N * 4));
+    const size_t total = (size_t)ceil_div(d, 32) * NB * 64;
+    router_split_kernel<<<dim3((unsigned)ceil_div((int)total, 256)), 256, 0, st>>>(
+        w_router, planes, d, N, NB, total);
+    router_logits_mfma<<<grid, 256, 0, st>>>(static_cast<const uint16_t*>(x), planes, partial,
+                                             T, d, N, NB, KC);
   } else {
     dim3 grid(ceil_div(T, RL_TM), ceil_div(N, RL_TN), S);
     router_logits_tiled<false><<<grid, 256, 0, st>>>(x, w_router, partial, T, d, N, KC);

@@ -158,7 +158,9 @@ def test_workspace_size_formula(T, N, k, d, f, sh):
               route="sigmoid" if sh else "softmax")
     a = lambda v: (v + 255) // 256 * 256
     S = _router_splits(T, N, d)
-    want = (a(S * T * N * 4) + 2 * a(T * k * 4) + a(N * 4) + a((N + 1) * 4) + 2 * a(T * k * 4)
+    # router scratch: partial logits, then (N > 8, bf16 x) the three weight planes
+    planes = a(S * T * N * 4) + (-(-d // 32)) * (-(-N // 16)) * 3 * 1024 if N > 8 else S * T * N * 4
+    want = (a(planes) + 2 * a(T * k * 4) + a(N * 4) + a((N + 1) * 4) + 2 * a(T * k * 4)
             + a(-(-T // 256) * N * 4) + a(-(-T // 16) * N * 4)
             + a(N * 4) + a((N + 1) * 4) + 2 * a(T * k * 4) + a(2048 * 4) + a(T * k * f * 2)
             + a(sh * T * f * 2) + a(T * k * d * 2)

@@ -17,7 +17,11 @@
  * Conventions for every entry point:
  *   - Pointers are DEVICE pointers unless stated otherwise, owned by the
  *     caller.  The library never allocates device memory; scratch space is
- *     the caller's workspace, sized by moe_workspace_bytes().
+ *     the caller's workspace, sized by moe_workspace_bytes().  Activation,
+ *     weight, scale and workspace buffers must be 16-byte aligned (every
+ *     hipMalloc result is); a misaligned one returns MOE_ERR_INVALID_ARG.
+ *     Index and gate arrays (int32 / float32) need only their natural
+ *     alignment.
  *   - Calls are asynchronous on `stream`; results are valid once the stream
  *     has synchronised.  No entry point copies device data to the host or
  *     synchronises the stream.

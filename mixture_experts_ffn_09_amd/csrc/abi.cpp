@@ -1,6 +1,8 @@
 // C ABI of the MoE FFN library: argument checks (all on the host, before any
 // HIP call), workspace carving, and kernel orchestration.  See moe_ffn.h.
 
+#include <initializer_list>
+
 #include "moe_ffn.h"
 
 #include <hip/hip_runtime.h>
@@ -118,9 +120,24 @@ WsLayout ws_layout(const moe_shape_t* s) {
   return L;
 }
 
+// The kernels move activations, weights and workspace pieces with 16-byte
+// vector loads and stores, so those buffers must be 16-byte aligned (every
+// hipMalloc and torch allocation is).
+bool misaligned(std::initializer_list<const void*> ps) {
+  for (const void* q : ps)
+    if (q && (reinterpret_cast<uintptr_t>(q) & 15)) return true;
+  return false;
+}
+
+moe_status_t check_aligned(std::initializer_list<const void*> ps) {
+  if (misaligned(ps)) return fail(MOE_ERR_INVALID_ARG, "device buffers must be 16-byte aligned");
+  return MOE_OK;
+}
+
 moe_status_t check_ws(const moe_shape_t* s, void* ws, size_t ws_bytes) {
   const size_t need = ws_layout(s).total;
   if (!ws) return fail(MOE_ERR_INVALID_ARG, "workspace is NULL");
+  if (misaligned({ws})) return fail(MOE_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
   if (ws_bytes < need)
     return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", ws_bytes, need);
   return MOE_OK;
@@ -143,6 +160,9 @@ moe_status_t check_weights(const moe_shape_t* s, const moe_weights_t* w, bool ro
       if (scaled(s) && (!w->w13_shared_scale || !w->w2_shared_scale))
         return fail(MOE_ERR_INVALID_ARG, "FP8 / MXFP4 shared expert needs its scales");
     }
+    if (misaligned({w->w13, w->w2, w->w13_shared, w->w2_shared, w->w13_scale, w->w2_scale,
+                    w->w13_shared_scale, w->w2_shared_scale}))
+      return fail(MOE_ERR_INVALID_ARG, "weights and scales must be 16-byte aligned");
   }
   return MOE_OK;
 }
@@ -274,6 +294,7 @@ moe_status_t moe_pack_weights(const moe_shape_t* s, int which, int n_mats, const
   if (which < 0 || which > 3) return fail(MOE_ERR_INVALID_ARG, "which must be 0, 1, 2 or 3");
   if (n_mats < 1) return fail(MOE_ERR_INVALID_ARG, "n_mats must be >= 1");
   if (!src_a || !dst) return fail(MOE_ERR_INVALID_ARG, "src_a / dst is NULL");
+  if ((st = check_aligned({src_a, src_b, dst})) != MOE_OK) return st;
   if (which >= 2) {
     if (s->w_dtype != MOE_MXFP4)
       return fail(MOE_ERR_UNSUPPORTED, "scale packing (which 2, 3) is for MXFP4 weights only");
@@ -307,6 +328,7 @@ static moe_status_t router_topk(const moe_shape_t* s, const void* x, const moe_w
   if (s->n_tokens == 0) return MOE_OK;
   if ((st = check_weights(s, w, true, false)) != MOE_OK) return st;
   if (!x || !topk_idx || !topk_w) return fail(MOE_ERR_INVALID_ARG, "x / topk_idx / topk_w is NULL");
+  if ((st = check_aligned({x})) != MOE_OK) return st;
   if ((st = check_ws(s, ws, ws_bytes)) != MOE_OK) return st;
   const WsLayout L = ws_layout(s);
   return run_router(s, x, w, topk_idx, topk_w,
@@ -339,6 +361,7 @@ moe_status_t moe_permute(const moe_shape_t* s, const int32_t* topk_idx, const vo
     return fail(MOE_ERR_INVALID_ARG, "routing counts / offsets / perm_token / inv_perm is NULL");
   if (!topk_idx) return fail(MOE_ERR_INVALID_ARG, "topk_idx is NULL");
   if (x_perm && !x) return fail(MOE_ERR_INVALID_ARG, "x_perm needs x");
+  if ((st = check_aligned({x, x_perm})) != MOE_OK) return st;
   if (s->n_tokens > 0 && (st = check_ws(s, ws, ws_bytes)) != MOE_OK) return st;
   // T == 0 still yields well-defined (zero) counts and offsets
   int32_t* hist = s->n_tokens > 0
@@ -396,6 +419,7 @@ moe_status_t moe_grouped_ffn(const moe_shape_t* s, const void* x, const void* x_
     return fail(MOE_ERR_INVALID_ARG, "without x_perm, x and perm_token are required");
   if (s->n_shared && (!x || !y_shared))
     return fail(MOE_ERR_INVALID_ARG, "the shared expert needs x and y_shared");
+  if ((st = check_aligned({x, x_perm, y_perm, y_shared})) != MOE_OK) return st;
   if ((st = check_ws(s, ws, ws_bytes)) != MOE_OK) return st;
   const WsLayout L = ws_layout(s);
   char* b = static_cast<char*>(ws);
@@ -416,6 +440,7 @@ moe_status_t moe_expert_gate_up(const moe_shape_t* s, const void* x, const void*
     return fail(MOE_ERR_INVALID_ARG, "without x_perm, x and perm_token are required");
   if (s->n_shared && (!x || !h_shared))
     return fail(MOE_ERR_INVALID_ARG, "the shared expert needs x and h_shared");
+  if ((st = check_aligned({x, x_perm, h, h_shared})) != MOE_OK) return st;
   if ((st = check_ws(s, ws, ws_bytes)) != MOE_OK) return st;
   return run_ffn(s, x, x_perm ? x_perm : x, x_perm ? nullptr : perm_token, offsets, w, h,
                  h_shared, nullptr, nullptr, static_cast<char*>(ws) + ws_layout(s).sched, 1,
@@ -432,6 +457,7 @@ moe_status_t moe_expert_down(const moe_shape_t* s, const void* h, const void* h_
   if (!offsets || !h || !y_perm) return fail(MOE_ERR_INVALID_ARG, "offsets / h / y_perm is NULL");
   if (s->n_shared && (!h_shared || !y_shared))
     return fail(MOE_ERR_INVALID_ARG, "the shared expert needs h_shared and y_shared");
+  if ((st = check_aligned({h, h_shared, y_perm, y_shared})) != MOE_OK) return st;
   if ((st = check_ws(s, ws, ws_bytes)) != MOE_OK) return st;
   return run_ffn(s, nullptr, nullptr, nullptr, offsets, w, const_cast<void*>(h),
                  const_cast<void*>(h_shared), y_perm, y_shared,
@@ -447,6 +473,7 @@ moe_status_t moe_combine(const moe_shape_t* s, const void* y_perm, const void* y
   if (!y_perm || !inv_perm || !topk_w || !out)
     return fail(MOE_ERR_INVALID_ARG, "y_perm / inv_perm / topk_w / out is NULL");
   if (s->n_shared && !y_shared) return fail(MOE_ERR_INVALID_ARG, "n_shared == 1 needs y_shared");
+  if ((st = check_aligned({y_perm, y_shared, out})) != MOE_OK) return st;
   HIP_TRY("combine", launch_combine(y_perm, s->n_shared ? y_shared : nullptr, inv_perm, topk_w,
                                     out, s->n_tokens, s->top_k, s->d_model,
                                     s->act_dtype == MOE_BF16, stream));
@@ -462,6 +489,7 @@ moe_status_t moe_load_stats(const moe_shape_t* s, const void* x, const moe_weigh
   if (s->n_tokens == 0) return MOE_OK;
   if ((st = check_weights(s, w, true, false)) != MOE_OK) return st;
   if (!x || !counts) return fail(MOE_ERR_INVALID_ARG, "x / counts is NULL");
+  if ((st = check_aligned({x})) != MOE_OK) return st;
   if (!(alpha == alpha) || !(step == step)) return fail(MOE_ERR_INVALID_ARG, "alpha / step is NaN");
   if (bias && s->route != MOE_ROUTE_SIGMOID_BIAS)
     return fail(MOE_ERR_INVALID_ARG, "the selection bias belongs to the sigmoid router");
@@ -493,6 +521,7 @@ static moe_status_t layer_forward(const moe_shape_t* s, const moe_weights_t* w, 
   if ((st = check_weights(s, w, true, true)) != MOE_OK) return st;
   if (!x || !out) return fail(MOE_ERR_INVALID_ARG, "x / out is NULL");
   if (x == out) return fail(MOE_ERR_INVALID_ARG, "x and out must not overlap");
+  if ((st = check_aligned({x, out})) != MOE_OK) return st;
   if ((st = check_ws(s, ws, ws_bytes)) != MOE_OK) return st;
   const WsLayout L = ws_layout(s);
   char* b = static_cast<char*>(ws);

@@ -125,6 +125,29 @@ def test_null_shape_and_pointers():
         moe.MOE_ERR_UNSUPPORTED
 
 
+def test_misaligned_buffers_are_rejected():
+    """Buffers moved with 16-byte vector accesses must be 16-byte aligned."""
+    MIS = C.c_void_p(0x1008)
+    s = shape()
+    ws_n = C.c_size_t(moe.moe_workspace_bytes(s))
+    w = moe.Weights(w_router=FAKE.value, w13=FAKE.value, w2=FAKE.value)
+    err = moe.MOE_ERR_INVALID_ARG
+    # misaligned x, out, workspace
+    assert _status("moe_layer_forward", C.byref(s), C.byref(w), MIS, C.c_void_p(0x4000), None,
+                   FAKE, ws_n, None) == err
+    assert _status("moe_layer_forward", C.byref(s), C.byref(w), FAKE, MIS, None,
+                   C.c_void_p(0x4000), ws_n, None) == err
+    assert _status("moe_layer_forward", C.byref(s), C.byref(w), FAKE, C.c_void_p(0x4000), None,
+                   MIS, ws_n, None) == err
+    # misaligned expert weight
+    wm = moe.Weights(w_router=FAKE.value, w13=FAKE.value, w2=MIS.value)
+    assert _status("moe_layer_forward", C.byref(s), C.byref(wm), FAKE, C.c_void_p(0x4000), None,
+                   C.c_void_p(0x8000), ws_n, None) == err
+    # combine output, pack destination
+    assert _status("moe_combine", C.byref(s), FAKE, None, FAKE, FAKE, MIS, None) == err
+    assert _status("moe_pack_weights", C.byref(s), 1, 1, FAKE, None, MIS, None) == err
+
+
 def test_workspace_too_small():
     s = shape()
     w = moe.Weights(w_router=FAKE.value, w13=FAKE.value, w2=FAKE.value)

@@ -79,3 +79,33 @@ __device__ __forceinline__ void barrier_no_fence() {
 }
 
 __host__ __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// Instruction-scheduling patterns for software-pipelined MFMA loops (masks:
+// 0x008 MFMA, 0x100 LDS read, 0x010 vector memory).
+// MFMA slices and LDS reads of one copy group: D reads, each preceded by a
+// share of M MFMAs, then the rest of the MFMAs.
+template <int I, int D, int M>
+__device__ __forceinline__ void group_pattern() {
+  if constexpr (I < D) {
+    constexpr int m = (I + 1) * M / (D + 1) - I * M / (D + 1);
+    if constexpr (m > 0) __builtin_amdgcn_sched_group_barrier(0x008, m, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    group_pattern<I + 1, D, M>();
+  } else {
+    constexpr int m = M - D * M / (D + 1);
+    if constexpr (m > 0) __builtin_amdgcn_sched_group_barrier(0x008, m, 0);
+  }
+}
+
+// Scheduling pattern of one step: group q of LPS issues one copy, then its
+// share of the NRD fragment reads interleaved with its share of the NMF MFMAs.
+template <int Q, int LPS, int NRD, int NMF>
+__device__ __forceinline__ void stage_pattern() {
+  if constexpr (Q < LPS) {
+    constexpr int d = (Q + 1) * NRD / LPS - Q * NRD / LPS;   // reads in this group
+    constexpr int m = (Q + 1) * NMF / LPS - Q * NMF / LPS;   // MFMAs in this group
+    __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);       // one copy
+    group_pattern<0, d, m>();
+    stage_pattern<Q + 1, LPS, NRD, NMF>();
+  }
+}

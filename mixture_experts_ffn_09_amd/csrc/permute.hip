@@ -115,10 +115,16 @@ __global__ __launch_bounds__(256) void permute_kernel(const int32_t* __restrict_
   for (int e = tid; e < N; e += 256) {
     int before = 0, total = 0;
     if (hist) {
-      for (int bb = 0; bb < nblk; ++bb) {
-        const int v = hist[(size_t)bb * N + e];
-        total += v;
-        if (bb < b) before += v;
+      // the loads of 8 blocks' counts are issued together
+      for (int bb0 = 0; bb0 < nblk; bb0 += 8) {
+        int v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = bb0 + u < nblk ? hist[(size_t)(bb0 + u) * N + e] : 0;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          total += v[u];
+          if (bb0 + u < b) before += v[u];
+        }
       }
     } else {
       for (int ww = 0; ww < PB_WAVES; ++ww) total += wh[ww * N + e];

@@ -241,6 +241,136 @@ __global__ __launch_bounds__(256) void router_logits_mfma(const uint16_t* __rest
       }
 }
 
+// Large batches: 128 tokens x 128 experts per workgroup, one wave per SIMD
+// (2 x 2 waves of 64 x 64), both operands moved global -> LDS by buffer
+// loads into a ring of RR_NS stages of 32 K, so several stages are in flight
+// while one is multiplied (the register-prefetch kernel above keeps one).
+// A stage holds 8 activation fragments and 8 expert blocks x 3 weight planes,
+// each 1 KB in MFMA operand order (lane l's 16 bytes at l * 16), read back
+// conflict-free.  Wave 0 copies the activations, waves 1-3 the planes: eight
+// 1 KB copies per wave per stage.  Needs N % 128 == 0, d % 32 == 0 and
+// T * d * 2 < 2^31; rows past T are loaded clamped and not stored.
+constexpr int RR_TM = 128, RR_TN = 128, RR_NS = 5;
+constexpr int RR_STAGE = 32 * 1024;
+constexpr int RR_CPW = 8;  // copies per wave per stage
+
+__global__ __launch_bounds__(256, 1) void router_logits_ring(const uint16_t* __restrict__ x,
+                                                             const uint16_t* __restrict__ planes,
+                                                             float* __restrict__ partial, int T,
+                                                             int d, int N, int NB, int KC) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[RR_NS * RR_STAGE];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int t0 = blockIdx.x * RR_TM, e0 = blockIdx.y * RR_TN, s = blockIdx.z;
+  const int k_begin = s * KC, k_end = min(d, k_begin + KC);
+  const int nst = (k_end - k_begin) / 32;  // >= 1: d and KC are multiples of 32
+  const int ks0 = k_begin / 32;
+
+  const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)x, 0, (int)((size_t)T * d * 2), BUF_DWORD3);
+  const __amdgpu_buffer_rsrc_t pres = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)planes, 0, (int)((size_t)(d / 32) * NB * 3 * 1024), BUF_DWORD3);
+  // this wave's eight copies: byte offset (lane part), LDS slot offset, and
+  // the per-stage advance of the scalar offset
+  uint32_t voff[RR_CPW];
+  int ldst[RR_CPW];
+#pragma unroll
+  for (int i = 0; i < RR_CPW; ++i) {
+    if (wave == 0) {  // activation fragment i: tokens t0 + 16 i + l % 16
+      const int t = min(t0 + 16 * i + (lane & 15), T - 1);
+      voff[i] = (uint32_t)t * (uint32_t)d * 2 + (lane >> 4) * 16;
+      ldst[i] = i * 1024;
+    } else {          // plane fragment c = (wave - 1) * 8 + i: block c / 3, plane c % 3
+      const int c = (wave - 1) * RR_CPW + i;
+      const int gnb = e0 / 16 + c / 3;
+      voff[i] = (uint32_t)((gnb * 3 + c % 3) * 1024 + lane * 16);
+      ldst[i] = 8192 + c * 1024;
+    }
+  }
+  const int sadv = wave == 0 ? 64 : NB * 3 * 1024;  // bytes per 32-K stage
+  const int sbase = wave == 0 ? k_begin * 2 : ks0 * NB * 3 * 1024;
+
+  typedef __attribute__((address_space(3))) void* lds_ptr_t;
+  // copy i of stage j into slot j % RR_NS (stages past the last load the
+  // last one again, into a slot no later stage reads)
+  auto copy_one = [&](int i, int j) {
+    const int jl = min(j, nst - 1);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        wave == 0 ? xres : pres, (lds_ptr_t)(lds + (j % RR_NS) * RR_STAGE + ldst[i]), 16,
+        voff[i], sbase + jl * sadv, 0, 0);
+  };
+  // operand read f of stage j: f < 4 activation fragment wm * 4 + f, else
+  // expert block wn * 4 + (f - 4) / 3 in plane (f - 4) % 3
+  auto read_one = [&](int f, int j, u32x4_t (&a)[4], u32x4_t (&b)[4][3]) {
+    const uint8_t* slot = lds + (j % RR_NS) * RR_STAGE + lane * 16;
+    if (f < 4)
+      a[f] = *reinterpret_cast<const u32x4_t*>(slot + (wm * 4 + f) * 1024);
+    else
+      b[(f - 4) / 3][(f - 4) % 3] = *reinterpret_cast<const u32x4_t*>(
+          slot + 8192 + (wn * 12 + f - 4) * 1024);
+  };
+
+  floatx4_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int n = 0; n < 4; ++n) acc[i][n] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+  u32x4_t ca[4], cb[4][3], na[4], nb[4][3];
+
+#pragma unroll
+  for (int j = 0; j < RR_NS - 1; ++j)
+#pragma unroll
+    for (int i = 0; i < RR_CPW; ++i) copy_one(i, j);
+  wait_vmcnt<(RR_NS - 2) * RR_CPW>();  // stage 0 has landed (this wave's copies)
+  barrier_no_fence();
+#pragma unroll
+  for (int f = 0; f < 16; ++f) read_one(f, 0, ca, cb);
+  // Step j: stage j + 1 has landed for every wave and every wave is past
+  // stage j - 1; stage j's 48 MFMAs run interleaved with the copies of stage
+  // j + RR_NS - 1 and the operand reads of stage j + 1 (program order
+  // alternates the two, since an LDS read may not move past a copy into LDS).
+  auto step = [&](int j, const u32x4_t (&a)[4], const u32x4_t (&b)[4][3], u32x4_t (&ga)[4],
+                  u32x4_t (&gb)[4][3]) {
+    wait_vmcnt<(RR_NS - 3) * RR_CPW>();
+    barrier_no_fence();
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < RR_CPW; ++i) {
+      copy_one(i, j + RR_NS - 1);
+      read_one(2 * i, j + 1, ga, gb);
+      read_one(2 * i + 1, j + 1, ga, gb);
+    }
+#pragma unroll
+    for (int pl = 0; pl < 3; ++pl)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int n = 0; n < 4; ++n) acc[i][n] = mfma16x16x32(a[i], b[n][pl], acc[i][n]);
+    stage_pattern<0, RR_CPW, 16, 48>();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  int j = 0;
+  for (; j + 1 < nst; j += 2) {
+    step(j, ca, cb, na, nb);
+    step(j + 1, na, nb, ca, cb);
+  }
+  if (j < nst) step(j, ca, cb, na, nb);
+  wait_vmcnt<0>();  // the clamped copies of the last stages
+
+  // lane holds rows 4 * (lane / 16) + q of column lane % 16 of each block
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int t = t0 + (wm * 4 + i) * 16 + (lane >> 4) * 4 + q;
+      if (t >= T) continue;
+      float* prow = partial + ((size_t)s * T + t) * N + e0 + wn * 64 + (lane & 15);
+#pragma unroll
+      for (int n = 0; n < 4; ++n) prow[n * 16] = acc[i][n][q];
+    }
+}
+
 template <bool BF16>
 __global__ __launch_bounds__(256) void router_logits_tiled(const void* __restrict__ xv,
                                                            const float* __restrict__ w,
@@ -427,18 +557,28 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
+  // split sums in ascending split order; the loads of 8 splits x NJ columns
+  // are issued together, so the latency is paid once per 8 splits
   float lg[NJ];
 #pragma unroll
-  for (int j = 0; j < NJ; ++j) {
-    const int e = lane + 64 * j;
-    float l = 0.f;
-    if (e < N) {
-#pragma unroll 4
-      for (int sp = 0; sp < S; ++sp) l += partial[((size_t)sp * T + t) * N + e];
-      if (offset) l += offset[e];
-    }
-    lg[j] = l;
+  for (int j = 0; j < NJ; ++j) lg[j] = 0.f;
+  const float* prow = partial + (size_t)t * N + lane;
+  const size_t sstride = (size_t)T * N;
+  for (int sp0 = 0; sp0 < S; sp0 += 8) {
+    float v[8][NJ];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+        v[u][j] = (sp0 + u < S && lane + 64 * j < N) ? prow[(sp0 + u) * sstride + 64 * j] : 0.f;
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) lg[j] += v[u][j];
   }
+#pragma unroll
+  for (int j = 0; j < NJ; ++j)
+    if (offset && lane + 64 * j < N) lg[j] += offset[lane + 64 * j];
   int my_idx;
   float my_w;
   select_topk<NJ>(lg, N, k, sigmoid, bias, lane, gsize, max_groups, gscr[threadIdx.x >> 6],
@@ -451,7 +591,13 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
 
 }  // namespace
 
-// Router kernel choice: N <= 8 -> small_n; bf16 x -> MFMA; else tiled fp32.
+// Router kernel choice: N <= 8 -> small_n; bf16 x -> MFMA (the LDS-ring form
+// for large batches); else tiled fp32.
+static bool router_ring(int T, int N, int d, bool act_bf16) {
+  return act_bf16 && N % RR_TN == 0 && d % 32 == 0 && T >= 1024 &&
+         (long long)T * d * 2 <= 0x7fffffffLL;
+}
+
 static int router_tiles(int T, int N, bool mfma) {
   if (N <= 8) return ceil_div(T, RS_TM);
   if (mfma) return ceil_div(T, RM_TM) * ceil_div(N, RM_TN);
@@ -460,6 +606,16 @@ static int router_tiles(int T, int N, bool mfma) {
 
 int router_splits(int T, int N, int d, bool act_bf16) {
   if (T <= 0) return 1;
+  if (router_ring(T, N, d, act_bf16)) {
+    // one workgroup per CU, at least 256 of K per split
+    const int tiles = ceil_div(T, RR_TM) * (N / RR_TN);
+    int S = 256 / tiles;
+    S = S < 1 ? 1 : S;
+    const int smax = ceil_div(d, 256);
+    S = S > smax ? smax : S;
+    const int KC = ceil_div(ceil_div(d, S), 64) * 64;
+    return ceil_div(d, KC);
+  }
   const int tiles = router_tiles(T, N, act_bf16 && N > 8);
   // enough workgroups to fill the chip, but at least 256 of K per split
   int S = 1024 / tiles;
@@ -515,8 +671,12 @@ hipError_t launch_router_logits(const void* x, bool act_bf16, const float* w_rou
     const size_t total = (size_t)ceil_div(d, 32) * NB * 64;
     router_split_kernel<<<dim3((unsigned)ceil_div((int)total, 256)), 256, 0, st>>>(
         w_router, planes, d, N, NB, total);
-    router_logits_mfma<<<grid, 256, 0, st>>>(static_cast<const uint16_t*>(x), planes, partial,
-                                             T, d, N, NB, KC);
+    if (router_ring(T, N, d, act_bf16))
+      router_logits_ring<<<dim3(ceil_div(T, RR_TM), N / RR_TN, S), 256, 0, st>>>(
+          static_cast<const uint16_t*>(x), planes, partial, T, d, N, NB, KC);
+    else
+      router_logits_mfma<<<grid, 256, 0, st>>>(static_cast<const uint16_t*>(x), planes, partial,
+                                               T, d, N, NB, KC);
   } else {
     dim3 grid(ceil_div(T, RL_TM), ceil_div(N, RL_TN), S);
     router_logits_tiled<false><<<grid, 256, 0, st>>>(x, w_router, partial, T, d, N, KC);

@@ -39,20 +39,35 @@ __global__ __launch_bounds__(256) void router_prob_block_kernel(
   for (int i = 0; i < ST_TPW; ++i) {
     const int t = blockIdx.x * ST_TOK + w * ST_TPW + i;
     if (t >= T) break;  // uniform across the wave
+    // split sums in ascending split order (as the top-k kernel forms them);
+    // the loads of 8 splits x NJ columns are issued together
     float lg[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) lg[j] = 0.f;
+    const float* prow = partial + (size_t)t * N + lane;
+    const size_t sstride = (size_t)T * N;
+    for (int sp0 = 0; sp0 < S; sp0 += 8) {
+      float v[8][NJ];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+          v[u][j] = (sp0 + u < S && lane + 64 * j < N) ? prow[(sp0 + u) * sstride + 64 * j] : 0.f;
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) lg[j] += v[u][j];
+    }
     float mx = -INFINITY;
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       const int e = lane + 64 * j;
-      float l = -INFINITY;
       if (e < N) {
-        l = 0.f;
-#pragma unroll 8
-        for (int sp = 0; sp < S; ++sp) l += partial[((size_t)sp * T + t) * N + e];
-        if (offset) l += offset[e];
+        if (offset) lg[j] += offset[e];
+      } else {
+        lg[j] = -INFINITY;
       }
-      lg[j] = l;
-      mx = fmaxf(mx, l);
+      mx = fmaxf(mx, lg[j]);
     }
     float z[NJ];
     float sum = 0.f;
@@ -93,8 +108,15 @@ __global__ __launch_bounds__(512) void load_stats_finish_kernel(
   const int e = threadIdx.x;
   float t = 0.f;
   if (e < N) {
+    // ascending block order; the loads of 8 blocks are issued together
     float s = 0.f;
-    for (int b = 0; b < nblk; ++b) s += bp[(size_t)b * N + e];
+    for (int b0 = 0; b0 < nblk; b0 += 8) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = b0 + u < nblk ? bp[(size_t)(b0 + u) * N + e] : 0.f;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) s += v[u];
+    }
     const float P = s / (float)T;
     const int c = counts[e];
     const float f = (float)c / (float)((long long)T * k);

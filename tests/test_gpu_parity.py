@@ -43,6 +43,13 @@ SMALL = {
     # 640-row shared expert on 256-row tiles
     "gemm_row_classes": H.small_config(C[3], 114, T=640, d_model=256, d_ff=128, n_experts=32,
                                        zipf_c=1.5),
+    # router logits through the LDS-ring kernel (T >= 1024, N % 128 == 0):
+    # a ragged last token tile and an odd number of 32-K stages; then five
+    # K splits, the last one a single stage
+    "router_ring_T1100_d288": H.small_config(C[3], 115, T=1100, d_model=288, n_experts=128,
+                                             d_ff=128),
+    "router_ring_splits": H.small_config(C[3], 116, T=1024, d_model=1056, n_experts=128,
+                                         d_ff=128),
     # FP8 weights through the GEMM path (routed + shared)
     "gemm_fp8": H.small_config(C[4], 110, T=256, d_model=256, d_ff=256, n_experts=8, top_k=4),
     # decode-sized batches: ragged T, odd N, sigmoid + selection bias + logit

@@ -436,8 +436,47 @@ __global__ __launch_bounds__(256) void router_logits_tiled(const void* __restric
 // Top-k: one wave per token.  Lane l holds experts l, l+64, ...; k rounds of
 // a wave-wide arg-max on (score desc, index asc).
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ bool better(float s1, int i1, float s2, int i2) {
-  return s1 > s2 || (s1 == s2 && i1 < i2);
+// Candidate (score s, index i) as one integer whose order is that of (s desc,
+// i asc): the float's bits made monotone (-0 taken as +0) above the inverted
+// index.  0 is below every candidate and marks "none"; a NaN score gets 0, so
+// it is never selected.
+__device__ __forceinline__ uint64_t order_key(float s, int idx) {
+  if (s != s) return 0;
+  uint32_t u = __float_as_uint(s);
+  if (u == 0x80000000u) u = 0;
+  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((uint64_t)u << 32) | (0xFFFFFFFFu - (uint32_t)idx);
+}
+
+__device__ __forceinline__ int key_index(uint64_t key) {
+  return (int)(0xFFFFFFFFu - (uint32_t)key);
+}
+
+// one DPP step of the wave maximum: each lane takes the larger of its value
+// and the one the DPP control routes to it (lanes with no source keep theirs)
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint64_t dpp_max_step(uint64_t v) {
+  const int lo = (int)(uint32_t)v, hi = (int)(uint32_t)(v >> 32);
+  const uint32_t olo = (uint32_t)__builtin_amdgcn_update_dpp(lo, lo, CTRL, ROWS, 0xf, false);
+  const uint32_t ohi = (uint32_t)__builtin_amdgcn_update_dpp(hi, hi, CTRL, ROWS, 0xf, false);
+  const uint64_t o = ((uint64_t)ohi << 32) | olo;
+  return o > v ? o : v;
+}
+
+// Maximum over the 64 lanes, returned to every lane (as a wave-uniform
+// value): shifts right by 1, 2, 4, 8 within each row of 16 leave the row's
+// maximum in its lane 15; broadcasting lane 15 into the next row and then
+// lane 31 into rows 2 and 3 leaves the wave's maximum in lane 63.  No LDS.
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  v = dpp_max_step<0x111, 0xf>(v);  // row_shr:1
+  v = dpp_max_step<0x112, 0xf>(v);  // row_shr:2
+  v = dpp_max_step<0x114, 0xf>(v);  // row_shr:4
+  v = dpp_max_step<0x118, 0xf>(v);  // row_shr:8
+  v = dpp_max_step<0x142, 0xa>(v);  // row_bcast:15 into rows 1, 3
+  v = dpp_max_step<0x143, 0xc>(v);  // row_bcast:31 into rows 2, 3
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 63);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 63);
+  return ((uint64_t)hi << 32) | lo;
 }
 
 // One wave scores and selects for one token.  Lane l holds the logits of
@@ -477,22 +516,14 @@ __device__ __forceinline__ void select_topk(const float (&lg)[NJ], int N, int k,
     float gm = -INFINITY;
     if (lane < G)
       for (int e = lane * gsize; e < (lane + 1) * gsize; ++e) gm = fmaxf(gm, gscr[e]);
-    bool gl = lane < G;
+    uint64_t gk = lane < G ? order_key(gm, lane) : 0;
     uint64_t allowed = 0;
     for (int r = 0; r < max_groups; ++r) {
-      float bs = gl ? gm : -INFINITY;
-      int bi = gl ? lane : 0x7fffffff;
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) {
-        const float os = __shfl_xor(bs, off);
-        const int oi = __shfl_xor(bi, off);
-        if (better(os, oi, bs, bi)) {
-          bs = os;
-          bi = oi;
-        }
-      }
+      const uint64_t b = wave_max_u64(gk);
+      if (b == 0) break;
+      const int bi = key_index(b);
       allowed |= 1ull << bi;
-      if (lane == bi) gl = false;
+      if (lane == bi) gk = 0;
     }
 #pragma unroll
     for (int j = 0; j < NJ; ++j)
@@ -501,34 +532,29 @@ __device__ __forceinline__ void select_topk(const float (&lg)[NJ], int N, int k,
   float my_logit = 0.f;
   float sel_logit0 = 0.f;
   my_idx = 0;
+  uint64_t key[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) key[j] = live[j] ? order_key(sc[j], lane + 64 * j) : 0;
   for (int r = 0; r < k; ++r) {
-    float bs = -INFINITY;
+    uint64_t b = 0;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) b = key[j] > b ? key[j] : b;
+    b = wave_max_u64(b);
     int bi = 0x7fffffff;
     float bl = 0.f;
+    if (b != 0) {
+      // the winner's logit, from its lane; retire the winner
+      bi = key_index(b);
+      const int bj = bi >> 6;
+      float lsel = lg[0];
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int e = lane + 64 * j;
-      if (live[j] && better(sc[j], e, bs, bi)) {
-        bs = sc[j];
-        bi = e;
-        bl = lg[j];
-      }
+      for (int j = 1; j < NJ; ++j)
+        if (j == bj) lsel = lg[j];
+      bl = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lsel), bi & 63));
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+        if (lane + 64 * j == bi) key[j] = 0;
     }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float os = __shfl_xor(bs, off);
-      const int oi = __shfl_xor(bi, off);
-      const float ol = __shfl_xor(bl, off);
-      if (better(os, oi, bs, bi)) {
-        bs = os;
-        bi = oi;
-        bl = ol;
-      }
-    }
-    // every lane now holds the winner; retire it
-#pragma unroll
-    for (int j = 0; j < NJ; ++j)
-      if (lane + 64 * j == bi) live[j] = false;
     if (r == 0) sel_logit0 = bl;
     if ((r & 63) == lane) {
       my_logit = bl;

@@ -164,6 +164,8 @@ moe_status_t check_weights(const moe_shape_t* s, const moe_weights_t* w, bool ro
                     w->w13_shared_scale, w->w2_shared_scale}))
       return fail(MOE_ERR_INVALID_ARG, "weights and scales must be 16-byte aligned");
   }
+  if (router && misaligned({w->w_router}))
+    return fail(MOE_ERR_INVALID_ARG, "w_router must be 16-byte aligned");
   return MOE_OK;
 }
 
@@ -187,6 +189,16 @@ moe_status_t check_groups(const moe_shape_t* s, const GroupLimit& g) {
 moe_status_t run_router(const moe_shape_t* s, const void* x, const moe_weights_t* w,
                         int32_t* idx, float* gw, float* logits, hipStream_t st,
                         const GroupLimit& g = GroupLimit()) {
+  if (router_fused_small(s->n_tokens, s->n_experts)) {
+    HIP_TRY("router_fused",
+            launch_router_fused_small(x, s->act_dtype == MOE_BF16, w->w_router, w->logit_offset,
+                                      s->route == MOE_ROUTE_SIGMOID_BIAS ? w->select_bias : nullptr,
+                                      s->route == MOE_ROUTE_SIGMOID_BIAS, s->n_tokens, s->d_model,
+                                      s->n_experts, s->top_k,
+                                      g.n_groups ? s->n_experts / g.n_groups : 0, g.max_groups,
+                                      idx, gw, st));
+    return MOE_OK;
+  }
   HIP_TRY("router_logits", launch_router_logits(x, s->act_dtype == MOE_BF16, w->w_router, logits,
                                                 s->n_tokens, s->d_model, s->n_experts, st));
   HIP_TRY("router_topk",

@@ -24,6 +24,12 @@ hipError_t launch_load_stats(const float* partial, int S, const float* offset, i
                              float* bp, float* frac, float* prob, float* aux, float* bias,
                              hipStream_t st);
 // gsize > 0: at most max_groups groups of gsize consecutive experts per token
+// Logits and selection in one launch for T <= 64 tokens and N <= 8 experts.
+bool router_fused_small(int T, int N);
+hipError_t launch_router_fused_small(const void* x, bool act_bf16, const float* w_router,
+                                     const float* offset, const float* select_bias, int sigmoid,
+                                     int T, int d, int N, int k, int gsize, int max_groups,
+                                     int32_t* topk_idx, float* topk_w, hipStream_t st);
 hipError_t launch_router_topk(const float* partial, int S, const float* offset,
                               const float* select_bias, int sigmoid, int T, int N, int k,
                               int gsize, int max_groups, int32_t* topk_idx, float* topk_w,

@@ -615,6 +615,80 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
   }
 }
 
+// Few tokens and experts (T <= 64, N <= 8): logits and selection in one
+// kernel, one workgroup per token.  Each thread dots 8-input chunks of the
+// token against the N weight columns (float32 FMAs), the 256 partial sums are
+// reduced in a fixed order (a butterfly within each wave, then the four wave
+// totals in order), and wave 0 selects and gates as the top-k kernel does.
+// Saves the split-K partial buffer and a second launch at decode sizes.
+template <bool BF16>
+__global__ __launch_bounds__(256) void router_fused_small_kernel(
+    const void* __restrict__ xv, const float* __restrict__ w, const float* __restrict__ offset,
+    const float* __restrict__ bias, int sigmoid, int T, int d, int N, int k, int gsize,
+    int max_groups, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w) {
+  __shared__ float wsum[4][8];
+  __shared__ float gscr[64];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int t = blockIdx.x;
+  // thread tid takes inputs tid, tid + 256, ...: a wave's x loads and its
+  // weight-row loads (N floats each) are contiguous across its lanes
+  // (the loads of 8 inputs are issued together)
+  float acc[8] = {};
+  for (int k0 = tid; k0 < d; k0 += 8 * 256) {
+    float xk[8];
+    u32x4_t w0[8], w1[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int kk = min(k0 + u * 256, d - 1);  // past the end: loaded, weighted 0
+      const float xv_ = BF16 ? bf16_to_f32(static_cast<const uint16_t*>(xv)[(size_t)t * d + kk])
+                             : static_cast<const float*>(xv)[(size_t)t * d + kk];
+      xk[u] = k0 + u * 256 < d ? xv_ : 0.f;
+      const float* wr = w + (size_t)kk * N;
+      if (N == 8) {  // one 32-byte row: two 16-byte loads
+        w0[u] = *reinterpret_cast<const u32x4_t*>(wr);
+        w1[u] = *reinterpret_cast<const u32x4_t*>(wr + 4);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          w0[u][e] = e < N ? __float_as_uint(wr[e]) : 0u;
+          w1[u][e] = e + 4 < N ? __float_as_uint(wr[e + 4]) : 0u;
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[e] = fmaf(xk[u], __uint_as_float(w0[u][e]), acc[e]);
+        acc[e + 4] = fmaf(xk[u], __uint_as_float(w1[u][e]), acc[e + 4]);
+      }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    float v = acc[e];
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) v += __shfl_xor(v, off);
+    acc[e] = v;
+  }
+  if (lane == 0)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) wsum[wv][e] = acc[e];
+  __syncthreads();
+  if (wv != 0) return;
+  float lg[1] = {0.f};
+  if (lane < N) {
+    lg[0] = ((wsum[0][lane] + wsum[1][lane]) + wsum[2][lane]) + wsum[3][lane];
+    if (offset) lg[0] += offset[lane];
+  }
+  int my_idx;
+  float my_w;
+  select_topk<1>(lg, N, k, sigmoid, bias, lane, gsize, max_groups, gscr, my_idx, my_w);
+  if (lane < k) {
+    topk_idx[(size_t)t * k + lane] = my_idx;
+    topk_w[(size_t)t * k + lane] = my_w;
+  }
+}
+
 }  // namespace
 
 // Router kernel choice: N <= 8 -> small_n; bf16 x -> MFMA (the LDS-ring form
@@ -707,6 +781,23 @@ hipError_t launch_router_logits(const void* x, bool act_bf16, const float* w_rou
     dim3 grid(ceil_div(T, RL_TM), ceil_div(N, RL_TN), S);
     router_logits_tiled<false><<<grid, 256, 0, st>>>(x, w_router, partial, T, d, N, KC);
   }
+  return hipGetLastError();
+}
+
+bool router_fused_small(int T, int N) { return T >= 1 && T <= 64 && N <= 8; }
+
+hipError_t launch_router_fused_small(const void* x, bool act_bf16, const float* w_router,
+                                     const float* offset, const float* select_bias, int sigmoid,
+                                     int T, int d, int N, int k, int gsize, int max_groups,
+                                     int32_t* topk_idx, float* topk_w, hipStream_t st) {
+  if (act_bf16)
+    router_fused_small_kernel<true><<<T, 256, 0, st>>>(x, w_router, offset, select_bias, sigmoid,
+                                                       T, d, N, k, gsize, max_groups, topk_idx,
+                                                       topk_w);
+  else
+    router_fused_small_kernel<false><<<T, 256, 0, st>>>(x, w_router, offset, select_bias,
+                                                        sigmoid, T, d, N, k, gsize, max_groups,
+                                                        topk_idx, topk_w);
   return hipGetLastError();
 }
 

@@ -16,11 +16,15 @@ namespace {
 // ---------------------------------------------------------------------------
 // Logits: float32 dot products, split over K into S partial sums
 // partial[s][t][e] (summed in a fixed order by the top-k kernel, so the
-// result does not depend on scheduling).  Two shapes:
+// result does not depend on scheduling).  Shapes:
 //  * N <= 8: one thread per token owning all experts; the W slice is staged
-//    in LDS and read as a broadcast.
-//  * N > 8: 32 tokens x 64 experts per workgroup, each thread 2 x 4,
-//    K staged through LDS 32 at a time.
+//    in LDS and read as a broadcast (router_logits_small_n).  With T <= 64
+//    the layer instead runs logits and selection in one kernel
+//    (router_fused_small_kernel, below the top-k kernel).
+//  * N > 8, bfloat16 x: MFMA on three bfloat16 planes of W
+//    (router_logits_mfma; router_logits_ring for large batches).
+//  * N > 8, float32 x: 32 tokens x 64 experts per workgroup, each thread
+//    2 x 4, K staged through LDS 32 at a time (router_logits_tiled).
 // ---------------------------------------------------------------------------
 constexpr int RL_TM = 32, RL_TN = 64, RL_TK = 32;
 constexpr int RS_TM = 256, RS_KT = 256;

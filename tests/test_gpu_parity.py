@@ -50,6 +50,18 @@ SMALL = {
                                              d_ff=128),
     "router_ring_splits": H.small_config(C[3], 116, T=1024, d_model=1056, n_experts=128,
                                          d_ff=128),
+    # the shape limits: 512 experts (eight per lane in the top-k wave) with
+    # k = 16, and k = 64 (every lane of the wave holds a slot)
+    "wide_router_N512_k16": H.small_config(C[3], 117, T=70, d_model=256, n_experts=512,
+                                           top_k=16, d_ff=128),
+    "many_slots_k64": H.small_config(C[2], 118, T=20, d_model=128, n_experts=100, top_k=64,
+                                     d_ff=64),
+    # the LDS-ring router at the widest N with a multi-block permute; and the
+    # first batch past the fused small-batch router (T = 65, N = 8), which
+    # takes the split-K logits and the separate top-k kernel
+    "ring_N512_k16_T1024": H.small_config(C[3], 119, T=1024, d_model=256, n_experts=512,
+                                          top_k=16, d_ff=128),
+    "router_split_path_T65": H.small_config(C[1], 120, T=65, d_model=512, d_ff=256),
     # FP8 weights through the GEMM path (routed + shared)
     "gemm_fp8": H.small_config(C[4], 110, T=256, d_model=256, d_ff=256, n_experts=8, top_k=4),
     # decode-sized batches: ragged T, odd N, sigmoid + selection bias + logit

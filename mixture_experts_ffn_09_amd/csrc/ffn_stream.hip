@@ -455,10 +455,13 @@ hipError_t launch_stream_d(const StreamParams& sp, int groups, hipStream_t st) {
 // The ring depth must divide the number of K steps; it shrinks as NP or MB
 // grow (down to 2) so that the registers of the ring stay within an
 // occupancy of two or more waves per SIMD.  An MXFP4 step carries four
-// activation fragments, so its ring is half as deep.
+// activation fragments and its LDS chunk holds at most 16, so its ring is at
+// most 4 deep (4 rather than 2 with two blocks per wave: the same two waves
+// per SIMD, and the 4096 x 14336 down pass 57% -> 66% of HBM peak).
 template <int MB, int NP, int FMT, bool GATED>
 hipError_t launch_stream(const StreamParams& sp, int groups, hipStream_t st) {
-  constexpr int DR = (FMT == WF_MXFP4 ? 4 : 8) / (NP * MB);
+  constexpr int DF = 8 / (NP * MB);
+  constexpr int DR = FMT == WF_MXFP4 && DF > 4 ? 4 : DF;
   constexpr int DMAX = DR < 2 ? 2 : DR;
   const int KS = sp.K / (FMT == WF_MXFP4 ? 128 : (FMT == WF_FP8 ? 64 : 32));
   if (DMAX >= 8 && KS % 8 == 0) return launch_stream_d<MB, NP, (DMAX >= 8 ? 8 : 2), FMT, GATED>(sp, groups, st);
@@ -475,12 +478,13 @@ hipError_t launch_stream(const StreamParams& sp, int groups, hipStream_t st) {
 // stream; there a wave takes two blocks (measured: 47% -> 64% of HBM peak
 // on the 7168 x 2048 fp8 down projection; four blocks, with the ring depth
 // halved again, reach only 60%).  MXFP4 steps carry four activation
-// fragments per 1 KB weight block, and two blocks per wave measured faster on
-// both passes (down 34% -> 42% of HBM peak).  Everywhere else one block per
-// wave with the deepest ring measured fastest.
+// fragments per 1 KB weight block; on the down pass two blocks per wave
+// measured faster (34% -> 42% of HBM peak with a ring of 2), on the gate/up
+// pass one block with a ring of 4 (60% -> 68%).  Everywhere else one block
+// per wave with the deepest ring measured fastest.
 int stream_np(int fmt, bool gated, int n_out) {
   const int NB = n_out / 16;
-  int np = ((fmt == WF_FP8 && !gated) || fmt == WF_MXFP4) ? 2 : 1;
+  int np = ((fmt == WF_FP8 || fmt == WF_MXFP4) && !gated) ? 2 : 1;
   while (np > 1 && NB % np) np >>= 1;
   return np;
 }

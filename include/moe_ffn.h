@@ -165,7 +165,9 @@ size_t moe_workspace_bytes(const moe_shape_t* s);
  * router"; [CH19] 19.3.2; [AIS-12] worked example).  x: [T][d] act_dtype.
  * Writes topk_idx [T][k] (descending selection score, exact ties to the
  * lower index) and topk_w [T][k].  Uses w->w_router, w->logit_offset and
- * (sigmoid only) w->select_bias; ws holds the [T][N] float32 logits. */
+ * (sigmoid only) w->select_bias; ws holds the split partial logits (with
+ * T <= 64 and N <= 8 logits and selection run in one kernel and ws is not
+ * touched). */
 moe_status_t moe_router_topk(const moe_shape_t* s, const void* x,
                              const moe_weights_t* w, int32_t* topk_idx,
                              float* topk_w, void* ws, size_t ws_bytes,

@@ -170,8 +170,8 @@ def main():
                          "the HBM byte counters)")
     a = ap.parse_args()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
-              "(the design for sharding is described in the docs)", file=sys.stderr)
+        print("bench.py runs on one GPU only: the library has no multi-GPU path "
+              "(expert- or token-parallel sharding is a design, not code)", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -472,19 +472,18 @@ hipError_t launch_stream(const StreamParams& sp, int groups, hipStream_t st) {
 }
 
 // Weight blocks per wave.  The activation fragments of a K step are loaded
-// once per wave and used for all its blocks.  With fp8 weights a 16-row
-// activation step (bf16) is as large as two weight blocks, which on the down
-// pass (one weight block per step) makes the activation reads the larger
-// stream; there a wave takes two blocks (measured: 47% -> 64% of HBM peak
-// on the 7168 x 2048 fp8 down projection; four blocks, with the ring depth
-// halved again, reach only 60%).  MXFP4 steps carry four activation
-// fragments per 1 KB weight block; on the down pass two blocks per wave
-// measured faster (34% -> 42% of HBM peak with a ring of 2), on the gate/up
-// pass one block with a ring of 4 (60% -> 68%).  Everywhere else one block
-// per wave with the deepest ring measured fastest.
+// once per workgroup into LDS where the K steps allow it (else once per
+// wave) and used for all of a wave's blocks.  MXFP4 steps carry
+// four activation fragments per 1 KB weight block; on its down pass two
+// blocks per wave measured faster (34% -> 42% of HBM peak with a ring of 2),
+// on its gate/up pass one block with a ring of 4 (60% -> 68%).  Everywhere
+// else one block per wave with the deepest ring measured fastest (the fp8
+// 7168 x 2048 down projection once took two blocks, when every wave read its
+// own activation fragments; with the fragments in LDS one block is 2.5%
+// faster on that pass).
 int stream_np(int fmt, bool gated, int n_out) {
   const int NB = n_out / 16;
-  int np = ((fmt == WF_FP8 || fmt == WF_MXFP4) && !gated) ? 2 : 1;
+  int np = (fmt == WF_MXFP4 && !gated) ? 2 : 1;
   while (np > 1 && NB % np) np >>= 1;
   return np;
 }

@@ -23,15 +23,31 @@ __global__ __launch_bounds__(256) void combine_bf16_kernel(const uint16_t* __res
   const int c0 = ((blockIdx.x % chunks) * 256 + threadIdx.x) * 8;
   if (c0 >= d) return;
   float acc[8] = {};
-  for (int i = 0; i < k; ++i) {
-    const int r = inv[(size_t)t * k + i];
-    if (r < 0) continue;
-    const float gi = gw[(size_t)t * k + i];
-    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(y + (size_t)r * d + c0);
+  // slots in ascending order, 8 at a time: the rows and gates of a batch are
+  // loaded together, then added in slot order (a dropped slot, row -1, adds
+  // nothing)
+  for (int i0 = 0; i0 < k; i0 += 8) {
+    int r[8];
+    float g[8];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      acc[2 * j] = fmaf(gi, bf16_to_f32(v[j] & 0xffffu), acc[2 * j]);
-      acc[2 * j + 1] = fmaf(gi, bf16_to_f32(v[j] >> 16), acc[2 * j + 1]);
+    for (int u = 0; u < 8; ++u) {
+      const bool in = i0 + u < k;
+      r[u] = in ? inv[(size_t)t * k + i0 + u] : -1;
+      g[u] = in ? gw[(size_t)t * k + i0 + u] : 0.f;
+    }
+    u32x4_t v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      v[u] = r[u] >= 0 ? *reinterpret_cast<const u32x4_t*>(y + (size_t)r[u] * d + c0)
+                       : u32x4_t{0, 0, 0, 0};
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (r[u] < 0) continue;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        acc[2 * j] = fmaf(g[u], bf16_to_f32(v[u][j] & 0xffffu), acc[2 * j]);
+        acc[2 * j + 1] = fmaf(g[u], bf16_to_f32(v[u][j] >> 16), acc[2 * j + 1]);
+      }
     }
   }
   if (ys) {
@@ -58,10 +74,20 @@ __global__ __launch_bounds__(256) void combine_f32_kernel(const float* __restric
   const int c = (blockIdx.x % chunks) * 256 + threadIdx.x;
   if (c >= d) return;
   float acc = 0.f;
-  for (int i = 0; i < k; ++i) {
-    const int r = inv[(size_t)t * k + i];
-    if (r < 0) continue;
-    acc = fmaf(gw[(size_t)t * k + i], y[(size_t)r * d + c], acc);
+  for (int i0 = 0; i0 < k; i0 += 8) {  // as in the bf16 kernel
+    int r[8];
+    float g[8], v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const bool in = i0 + u < k;
+      r[u] = in ? inv[(size_t)t * k + i0 + u] : -1;
+      g[u] = in ? gw[(size_t)t * k + i0 + u] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = r[u] >= 0 ? y[(size_t)r[u] * d + c] : 0.f;
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (r[u] >= 0) acc = fmaf(g[u], v[u], acc);
   }
   if (ys) acc += ys[(size_t)t * d + c];
   out[(size_t)t * d + c] = acc;

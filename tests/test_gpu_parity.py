@@ -145,7 +145,7 @@ def _sample_tokens(cfg, xo, n_tok, max_experts):
     return sorted(set(chosen))
 
 
-@pytest.mark.parametrize("ci", [1, 2, 3, 4])
+@pytest.mark.parametrize("ci", [1, 2, 3, 4, 5])
 def test_layer_full_size_sampled(ci):
     cfg = C[ci]
     L, x, xd, out, g = _run_gpu(cfg)

@@ -397,15 +397,17 @@ __global__ __launch_bounds__(512, 1) void ffn_gemm_kernel(GemmParams p) {
 // the barrier that follows its last read (2 NPA >= NS + 1).
 
 // One tile: WM x (4 / WM) waves, each MBW x NBW blocks of 16 x 16; NS weight
-// steps and NPA activation pairs in LDS.
+// steps and NPA activation pairs in LDS.  The tile's weight rows are the
+// WN * NBW 16-row blocks from block nb0 on (gate/up: interleaved pairs, nb0
+// even): a whole 256-row weight tile, or a part of one.
 template <bool GATED, int WM, int MBW, int NBW, int NS, int NPA>
 __device__ __forceinline__ void four_wave_tile(const GemmParams& p, uint8_t* lds, int g,
-                                               int row_base, int rows, int m0, int nt) {
+                                               int row_base, int rows, int m0, int nb0) {
   constexpr int WN = 4 / WM;
   constexpr int BM = WM * MBW * 16;
   constexpr int AFR = BM / 16;        // activation fragments per step
-  constexpr int WBL = GM_BN / 16;     // weight blocks per step
-  static_assert(WN * NBW == WBL, "tile width");
+  constexpr int WBL = WN * NBW;       // weight blocks per step
+  static_assert(WBL % 4 == 0 && (!GATED || NBW % 2 == 0), "tile width");
   constexpr int NH = GATED ? 2 : 1;
   constexpr int B_STEP = WBL * 1024;           // one weight step in LDS
   constexpr int A_PAIR = AFR * 2048;           // one activation pair in LDS
@@ -442,10 +444,10 @@ __device__ __forceinline__ void four_wave_tile(const GemmParams& p, uint8_t* lds
     const int jb = wave * B_PER_WAVE + i;
     uint32_t off;
     if (GATED) {
-      const int pb = nt * (WBL / 2) + (jb >> 1);
+      const int pb = nb0 / 2 + (jb >> 1);
       off = (((uint32_t)pb * KT) * 2 + (jb & 1)) * 1024;
     } else {
-      off = ((uint32_t)(nt * WBL + jb) * KT) * 1024;
+      off = ((uint32_t)(nb0 + jb) * KT) * 1024;
     }
     boff[i] = off + lane * 16;
     bdst[i] = jb * 1024;
@@ -575,13 +577,13 @@ __device__ __forceinline__ void four_wave_tile(const GemmParams& p, uint8_t* lds
       if (GATED) {
 #pragma unroll
         for (int q = 0; q < NBW / 2; ++q) {
-          const int col = (nt * (WBL / 2) + wn * (NBW / 2) + q) * 16 + (lane & 15);
+          const int col = (nb0 / 2 + wn * (NBW / 2) + q) * 16 + (lane & 15);
           orow[col] = (uint16_t)f32_to_bf16(silu_f32(acc[i][2 * q][e]) * acc[i][2 * q + 1][e]);
         }
       } else {
 #pragma unroll
         for (int j = 0; j < NBW; ++j) {
-          const int col = (nt * WBL + wn * NBW + j) * 16 + (lane & 15);
+          const int col = (nb0 + wn * NBW + j) * 16 + (lane & 15);
           orow[col] = (uint16_t)f32_to_bf16(acc[i][j][e]);
         }
       }
@@ -589,12 +591,43 @@ __device__ __forceinline__ void four_wave_tile(const GemmParams& p, uint8_t* lds
   }
 }
 
+constexpr int XCD_CUS = 32;  // CUs per XCD
+
+// Work unit of this workgroup for the four-wave kernel: tile L, whole
+// (nsub = 1) or its weight rows cut into nsub parts (part sub).  As in
+// xcd_tile each XCD walks a contiguous eighth of the tiles, one workgroup
+// per CU, in about cnt / XCD_CUS rounds.  When the last round would hold at
+// most half of the XCD's CUs, each of its tiles is cut into 2 (at most 16
+// tiles) or 4 (at most 8) parts of the weight rows, each over the whole K, so
+// that round keeps most CUs busy and takes a fraction of a tile's time (on
+// the mixtral-prefill down pass a last round of 6 tiles on 32 CUs took 18% of
+// the pass).  Each output element is still summed by one workgroup in K
+// order, as in a whole tile.  Returns -1 for no work.  Needs gridDim.x >=
+// 8 * (ceil(total / 8) + XCD_CUS).
+__device__ __forceinline__ int xcd_unit(int total, int& nsub, int& sub) {
+  const int per = (total + NXCD - 1) / NXCD;
+  const int x = blockIdx.x % NXCD, slot = blockIdx.x / NXCD;
+  const int cnt = max(0, min(per, total - x * per));
+  const int tail = cnt % XCD_CUS;
+  const int ns = tail == 0 ? 1 : (tail <= XCD_CUS / 4 ? 4 : (tail <= XCD_CUS / 2 ? 2 : 1));
+  const int whole = ns > 1 ? cnt - tail : cnt;
+  nsub = 1;
+  sub = 0;
+  if (slot < whole) return x * per + slot;
+  const int j = slot - whole;
+  if (ns == 1 || j >= tail * ns) return -1;
+  nsub = ns;
+  sub = j % ns;
+  return x * per + whole + j / ns;
+}
+
 template <bool GATED>
 __global__ __launch_bounds__(256, 1) void ffn_gemm_big_kernel(GemmParams p) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds[FW_LDS];
   const int ngroups = p.g1 - p.g0;
   const int MT = p.tiles[ngroups];
-  const int L = xcd_tile(MT * p.NT);
+  int nsub, sub;
+  const int L = xcd_unit(MT * p.NT, nsub, sub);
   if (L < 0) return;
   // tile-order groups: 4 weight tiles on the gate/up pass, 8 on the down
   // pass, where sharing each activation tile among more weight tiles
@@ -615,12 +648,25 @@ __global__ __launch_bounds__(256, 1) void ffn_gemm_big_kernel(GemmParams p) {
   int row_base, rows;
   group_rows(p, g, row_base, rows);
   const int left = rows - m0;   // rows from this tile on (> 0)
+  const int nb0 = nt * (GM_BN / 16);  // first 16-row weight block of the tile
+  if (nsub > 1) {
+    // a part of a tail tile; shorter tiles (at most 128 rows) stay whole,
+    // in part 0
+    if (left > 128) {
+      if (nsub == 4)
+        four_wave_tile<GATED, 2, 8, 2, 5, 3>(p, lds, g, row_base, rows, m0, nb0 + sub * 4);
+      else
+        four_wave_tile<GATED, 2, 8, 4, 5, 3>(p, lds, g, row_base, rows, m0, nb0 + sub * 8);
+      return;
+    }
+    if (sub != 0) return;
+  }
   if (left > 128)
-    four_wave_tile<GATED, 2, 8, 8, 4, 3>(p, lds, g, row_base, rows, m0, nt);
+    four_wave_tile<GATED, 2, 8, 8, 4, 3>(p, lds, g, row_base, rows, m0, nb0);
   else if (left > 64)
-    four_wave_tile<GATED, 1, 8, 4, 5, 3>(p, lds, g, row_base, rows, m0, nt);
+    four_wave_tile<GATED, 1, 8, 4, 5, 3>(p, lds, g, row_base, rows, m0, nb0);
   else
-    four_wave_tile<GATED, 1, 4, 4, 6, 4>(p, lds, g, row_base, rows, m0, nt);
+    four_wave_tile<GATED, 1, 4, 4, 6, 4>(p, lds, g, row_base, rows, m0, nb0);
 }
 
 template <int BM, bool FP8>
@@ -677,10 +723,12 @@ hipError_t launch_ffn_gemm(const FfnArgs& a, int pass, int g0, int g1, int max_r
     if (a.fp8)
       launch_gemm_kernel<128, true>(gated, nwg, p, st);
     else if (four_wave) {
+      // room for the parts of the last round's tiles (xcd_unit)
+      const unsigned nwg_fw = (unsigned)(nwg + (long long)NXCD * XCD_CUS);
       if (gated)
-        ffn_gemm_big_kernel<true><<<dim3((unsigned)nwg), 256, 0, st>>>(p);
+        ffn_gemm_big_kernel<true><<<dim3(nwg_fw), 256, 0, st>>>(p);
       else
-        ffn_gemm_big_kernel<false><<<dim3((unsigned)nwg), 256, 0, st>>>(p);
+        ffn_gemm_big_kernel<false><<<dim3(nwg_fw), 256, 0, st>>>(p);
     } else
       launch_gemm_kernel<128, false>(gated, nwg, p, st);
     e = hipGetLastError();

@@ -650,16 +650,26 @@ __global__ __launch_bounds__(256, 1) void ffn_gemm_big_kernel(GemmParams p) {
   const int left = rows - m0;   // rows from this tile on (> 0)
   const int nb0 = nt * (GM_BN / 16);  // first 16-row weight block of the tile
   if (nsub > 1) {
-    // a part of a tail tile; shorter tiles (at most 128 rows) stay whole,
-    // in part 0
-    if (left > 128) {
-      if (nsub == 4)
-        four_wave_tile<GATED, 2, 8, 2, 5, 3>(p, lds, g, row_base, rows, m0, nb0 + sub * 4);
+    // a part of a tail tile: 4 parts of 64 weight rows or 2 of 128 (short
+    // tiles stream as many weight bytes as tall ones, so they are cut too)
+    if (nsub == 4) {
+      const int nb = nb0 + sub * 4;
+      if (left > 128)
+        four_wave_tile<GATED, 2, 8, 2, 5, 3>(p, lds, g, row_base, rows, m0, nb);
+      else if (left > 64)
+        four_wave_tile<GATED, 2, 4, 2, 6, 4>(p, lds, g, row_base, rows, m0, nb);
       else
-        four_wave_tile<GATED, 2, 8, 4, 5, 3>(p, lds, g, row_base, rows, m0, nb0 + sub * 8);
-      return;
+        four_wave_tile<GATED, 2, 2, 2, 6, 4>(p, lds, g, row_base, rows, m0, nb);
+    } else {
+      const int nb = nb0 + sub * 8;
+      if (left > 128)
+        four_wave_tile<GATED, 2, 8, 4, 5, 3>(p, lds, g, row_base, rows, m0, nb);
+      else if (left > 64)
+        four_wave_tile<GATED, 1, 8, 2, 6, 4>(p, lds, g, row_base, rows, m0, nb);
+      else
+        four_wave_tile<GATED, 1, 4, 2, 6, 4>(p, lds, g, row_base, rows, m0, nb);
     }
-    if (sub != 0) return;
+    return;
   }
   if (left > 128)
     four_wave_tile<GATED, 2, 8, 8, 4, 3>(p, lds, g, row_base, rows, m0, nb0);

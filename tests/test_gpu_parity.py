@@ -62,9 +62,9 @@ SMALL = {
     "ring_N512_k16_T1024": H.small_config(C[3], 119, T=1024, d_model=256, n_experts=512,
                                           top_k=16, d_ff=128),
     "router_split_path_T65": H.small_config(C[1], 120, T=65, d_model=512, d_ff=256),
-    # a last round of few tiles per XCD: its 256-row tiles are cut into 2 or 4
-    # parts of the weight rows (shorter tiles stay whole); routed only, and
-    # routed + shared in one launch, both passes
+    # a last round of few tiles per XCD: its tiles (256, 128 and 64 rows) are
+    # cut into 2 or 4 parts of the weight rows; routed only, and routed +
+    # shared in one launch, both passes
     "gemm_split_tail": H.small_config(C[2], 121, T=512, d_model=2048, n_experts=4, d_ff=1024),
     "gemm_split_shared": H.small_config(C[3], 122, T=300, d_model=1024, n_experts=4, top_k=2,
                                         d_ff=1024),

@@ -28,8 +28,11 @@
 // linear tile index is remapped to give each XCD a contiguous range, and the
 // range is walked in groups of a few weight tiles x all row tiles (4, or 8
 // on the four-wave kernel's down pass): workgroups that run together on one
-// XCD share their weight and activation slices in that XCD's L2.  Row tiles are counted on the device (a one-workgroup scan
-// of ceil(rows_g / BM)), so no host synchronisation on the counts is needed.
+// XCD share their weight and activation slices in that XCD's L2.  Row tiles
+// are counted on the device (a one-workgroup scan of ceil(rows_g / BM)), so
+// no host synchronisation on the counts is needed.  On the four-wave kernel
+// a short last round of tiles on an XCD runs as parts of the tiles' weight
+// rows (xcd_unit), so that round does not leave most CUs idle.
 
 #include <type_traits>
 

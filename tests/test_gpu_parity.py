@@ -214,8 +214,12 @@ def test_stages_through_abi_match_layer_forward(name):
                    H.TOL["bf16"], "y_shared")
 
 
-def test_deterministic_and_workspace_independent():
-    cfg = SMALL["c5_structure_T64"]
+@pytest.mark.parametrize("name", ["c5_structure_T64", "gemm_split_shared", "ring_N512_k16_T1024"])
+def test_deterministic_and_workspace_independent(name):
+    """Bitwise-equal outputs across calls and whatever the workspace held
+    (streaming path; GEMM with last-round tiles cut into parts; LDS-ring
+    router logits)."""
+    cfg = SMALL[name]
     L, x, xd, out, g = _run_gpu(cfg)
     ws = L.workspace()
     ws.fill_(0xFF)

@@ -1,6 +1,7 @@
-// Grouped expert FFN for bfloat16 activations with bfloat16 or FP8 (OCP
-// E4M3, one float32 scale per 128x128 block) weights: the weight-streaming
-// form, for few rows per expert (decode).
+// Grouped expert FFN for bfloat16 activations with bfloat16, FP8 (OCP E4M3,
+// one float32 scale per 128x128 block) or MXFP4 (E2M1 codes, one E8M0 scale
+// per 32 inputs) weights: the weight-streaming form, for few rows per expert
+// (decode; MXFP4 at every batch size).
 //
 // An expert is a complete SwiGLU FFN with its own three matrices ("Mixture of
 // Experts for LLM Inference", "The MoE change is surprisingly local";
@@ -16,8 +17,11 @@
 // 16*MB rows.  Weights are pre-packed so that one K step of one block is a
 // contiguous 1 KB: each lane's 16-byte load is its v_mfma_f32_16x16x32_bf16
 // B operand (bf16) or two of them (fp8, converted exactly to bf16 in
-// registers), and a wave's loads are fully coalesced.  Activations come from
-// L2 (they are re-read by every wave of the group).
+// registers; MXFP4 words decoded with their scales), and a wave's loads are
+// fully coalesced.  The activation fragments of a chunk of K steps, the same
+// for all of a workgroup's waves, are copied once per workgroup into LDS
+// (double-buffered) where the K steps allow it; otherwise each wave reads
+// them from L2.
 //
 // MFMA 16x16x32 operand mapping used on both sides: lane l holds row (A) /
 // column (B) l % 16 and k = 8 * (l / 16) + j, j < 8; the accumulator lane l

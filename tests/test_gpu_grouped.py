@@ -100,3 +100,47 @@ def test_all_groups_allowed_is_the_plain_router():
     moe.moe_router_topk_grouped(s, xd, L.weights, 8, 8, b[0], b[1], ws)
     torch.cuda.synchronize()
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_grouped_full_size_sampled():
+    """The DeepSeek prefill workload (T = 4096, d = 7168, 256 experts + shared)
+    with 8 groups, at most 4 per token: routing, gates and the permutation on
+    every token, the layer output on sampled tokens."""
+    cfg, G, M = C[3], 8, 4
+    _log(f"[case] grouped full size {cfg.name} T={cfg.T} G={G} M={M}")
+    L = build_device_layer(cfg)
+    x = W.make_x(cfg)
+    xd = x.to("cuda")
+    rb = L.routing_buffers()
+    out = torch.empty_like(xd)
+    moe.moe_layer_forward_grouped(L.shape_for(cfg.T), L.weights, xd, out, G, M, L.workspace(),
+                                  moe.make_routing(**rb))
+    torch.cuda.synchronize()
+    g = {kk: v.cpu().numpy() for kk, v in rb.items()}
+    xo = H.x_f64(cfg, x)
+    w_r, off, bias = H.oracle_router(cfg)
+    logits = O.router_logits(xo, w_r, off)
+    scores = O.selection_scores(logits, cfg.route, bias)
+    _, ties = _check_grouped(scores, g["topk_idx"], cfg.top_k, G, M)
+    gates = O.gate_weights(logits, g["topk_idx"], cfg.route)
+    H.check_gates(g["topk_idx"], g["topk_w"], g["topk_idx"], gates)
+    H.check_permutation(g, g["topk_idx"], cfg.n_experts)
+    # tokens whose experts stay few (keeps the oracle quick), and the last one
+    rng = np.random.default_rng(cfg.index)
+    chosen, used = [], set()
+    for t in rng.permutation(cfg.T):
+        s = set(int(e) for e in g["topk_idx"][t])
+        if len(used | s) <= 64:
+            chosen.append(int(t))
+            used |= s
+        if len(chosen) == 32:
+            break
+    toks = np.array(sorted(set(chosen + [cfg.T - 1])))
+    shared = H.oracle_expert(cfg, cfg.n_experts)
+    ref, _, _, _ = O.moe_forward_with_routing(xo[toks], g["topk_idx"][toks], gates[toks],
+                                              lambda e: H.oracle_expert(cfg, e),
+                                              cfg.n_experts, shared)
+    err = H.assert_close(H.to_np(out)[toks], ref, H.TOL[cfg.w_dtype])
+    _log(f"  ok: near-tie tokens {ties}, {len(toks)} tokens checked, max abs err {err[0]:.3e}")
+    del L
+    torch.cuda.empty_cache()

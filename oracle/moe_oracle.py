@@ -258,7 +258,9 @@ def top_k_select(scores: np.ndarray, k: int) -> np.ndarray:
     """Indices of the k best experts per token, best first.
 
     Ranking is done on float32-rounded scores (the precision the GPU decides
-    in); exact ties go to the lower expert index.  Returns int64 [T][k].
+    in); exact ties go to the lower expert index.  A NaN score ranks below
+    every other score, -inf included (NaN among themselves by index), so k
+    experts are always chosen.  Returns int64 [T][k].
     """
     s32 = np.asarray(scores, dtype=np.float64).astype(np.float32)
     T, N = s32.shape
@@ -288,12 +290,17 @@ def group_limited_top_k(scores: np.ndarray, k: int, n_groups: int,
     gs = N // n_groups
     if k > max_groups * gs:
         raise ValueError("k exceeds the experts of the allowed groups")
-    gscore = s32.reshape(T, n_groups, gs).max(axis=2)
+    # a NaN score ranks below every other one (as in top_k_select): a group's
+    # best score skips NaN and is NaN only when all of its scores are
+    with np.errstate(invalid="ignore"):
+        gscore = np.fmax.reduce(s32.reshape(T, n_groups, gs), axis=2)
     keep_g = np.argsort(-gscore, axis=1, kind="stable")[:, :max_groups]
     allowed = np.zeros((T, n_groups), dtype=bool)
     np.put_along_axis(allowed, keep_g, True, axis=1)
-    masked = np.where(np.repeat(allowed, gs, axis=1), s32, np.float32(-np.inf))
-    order = np.argsort(-masked, axis=1, kind="stable")
+    # experts of the kept groups first, each part by (score desc, NaN last),
+    # exact ties to the lower index (lexsort is stable; its last key is primary)
+    outside = ~np.repeat(allowed, gs, axis=1)
+    order = np.lexsort((-s32, outside), axis=1)
     return order[:, :k].astype(np.int64)
 
 

@@ -528,6 +528,37 @@ def pin_group_limited_selection():
         assert got.tolist() == bf, (G, M)
 
 
+def pin_nan_scores_rank_last():
+    """A NaN selection score ranks below every other score, -inf included
+    (NaN among themselves by index): k experts are always chosen.  Brute
+    force with Python's sort on an explicit key; a group's best score skips
+    NaN (NaN only when the whole group is NaN) and ranks the same way."""
+    nan, inf = float("nan"), float("inf")
+    rows = [[nan, 0.5, -inf, nan, 0.1, nan, 2.0, -1.0],
+            [nan] * 8,
+            [-inf, nan, -inf, nan, -inf, nan, -inf, nan],
+            [nan, nan, 1.0, nan, nan, nan, nan, 3.0]]
+    sc = np.array(rows)
+
+    def key(v, e):
+        return (1, 0.0, e) if v != v else (0, -v, e)
+
+    for k in (1, 3, 6, 8):
+        want = [sorted(range(8), key=lambda e: key(r[e], e))[:k] for r in rows]
+        assert O.top_k_select(sc, k).tolist() == want, k
+    for G, M, k in ((4, 2, 3), (2, 1, 2), (8, 3, 3)):
+        gs = 8 // G
+        want = []
+        for r in rows:
+            def gbest(g):
+                vals = [r[e] for e in range(g * gs, (g + 1) * gs) if r[e] == r[e]]
+                return max(vals) if vals else nan
+            kept = sorted(range(G), key=lambda g: key(gbest(g), g))[:M]
+            allowed = [e for g in kept for e in range(g * gs, (g + 1) * gs)]
+            want.append(sorted(allowed, key=lambda e: key(r[e], e))[:k])
+        assert O.group_limited_top_k(sc, k, G, M).tolist() == want, (G, M)
+
+
 # ---------------------------------------------------------------------------
 # MXFP4 weights
 # ---------------------------------------------------------------------------
@@ -583,7 +614,7 @@ ALL_PINS = [
     pin_experts_touched, pin_router_probabilities, pin_load_statistics_closed_forms,
     pin_load_statistics_brute, pin_bias_controller_rule, pin_bias_controller_balances,
     pin_capacity_limit, pin_capacity_dispatch_brute, pin_capacity_layer,
-    pin_group_limited_selection, pin_e8m0_decoder, pin_e2m1_decoder, pin_mxfp4_dequant,
+    pin_group_limited_selection, pin_nan_scores_rank_last, pin_e8m0_decoder, pin_e2m1_decoder, pin_mxfp4_dequant,
 ]
 
 

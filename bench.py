@@ -1,20 +1,28 @@
 """Benchmark of the MoE FFN layer forward on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config I]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config I] [--only]
 
 A step is one pass of the whole hot path over one batch already resident in
 HBM: router (logits + top-k), permute, expert gate/up + SwiGLU, expert down,
-combine, each through its C-ABI entry point on torch's current stream, with a
-HIP event after each so every stage is timed inside the timed region.  The
-default workload is the Mixtral-8x7B-shaped decode layer (T=16, d=4096, 8
-experts top-2, d_ff=14336, bf16).  Prints one JSON line.
+combine.  The reported workload (default: the Mixtral-8x7B-shaped prefill
+layer, T=8192, d=4096, 8 experts top-2, d_ff=14336, bf16) is timed as K
+single `moe_layer_forward` calls, each between its own pair of HIP events on
+the launch stream, with a 1 GiB scrub write before each step outside the
+events so that L2 and the 256 MB MALL start cold; `ms_per_step` is the
+median, with min and mean beside it.  The same steps through the per-stage
+entry points, with events between the stages, time each kernel for the
+roofline.  Unless --only is given, every other workload is then timed the
+same way and reported under "workloads" in the same JSON line.  Prints one
+JSON line.
 """
 
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -26,6 +34,7 @@ PEAK_BF16_TFLOPS = 2500.0        # dense bf16 MFMA
 PEAK_FP32_VALU_TFLOPS = 78.6     # 256 CU x 64 lanes x 2 flop x 2.4 GHz, no packed math
 METRIC = "MoE-layer tokens/sec at 1 GPU; decode HBM GB/s and prefill TFLOP/s vs roofline"
 STAGES = ["router", "permute", "gate_up", "down", "combine"]
+SCRUB_BYTES = 1 << 30
 
 
 def accounting(cfg, touched: int):
@@ -59,10 +68,7 @@ def accounting(cfg, touched: int):
 
 def roofline_for(cfg, stage: dict, ms: float):
     flops, byts = stage["flops"], stage["bytes"]
-    if cfg.w_dtype == "f32":
-        peak_f = PEAK_FP32_VALU_TFLOPS
-    else:
-        peak_f = PEAK_BF16_TFLOPS
+    peak_f = PEAK_FP32_VALU_TFLOPS if cfg.w_dtype == "f32" else PEAK_BF16_TFLOPS
     ai = flops / max(byts, 1)
     ridge = peak_f * 1e12 / (PEAK_HBM_GBS * 1e9)
     if ai < ridge:
@@ -77,11 +83,11 @@ def roofline_for(cfg, stage: dict, ms: float):
 
 def measured_traffic(workload: str):
     """HBM bytes per launch of the gate/up kernel from the committed rocprofv3
-    counter summary, or None when there is none for this workload or the
-    kernel source has changed since the counters were taken."""
-    import hashlib
-    path = os.path.join(ROOT, "profiles", f"traffic_{workload.replace('-', '_')}_T16.json")
-    if workload != "mixtral-decode" or not os.path.exists(path):
+    counter summary (profiles/traffic_<workload>.json), or None when there is
+    none for this workload or the kernel source has changed since the
+    counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload.replace('-', '_')}.json")
+    if not os.path.exists(path):
         return None
     rec = json.load(open(path))
     src = open(os.path.join(ROOT, rec["source"]), "rb").read()
@@ -117,13 +123,34 @@ def achievable(torch):
     return out
 
 
-def cpu_baseline(cfg, x_cpu, n_tokens: int):
-    """Time the CPU oracle (as it stands) on a bounded sample of the same
-    workload: the first n_tokens tokens, weights decoded from their stored
-    bits inside the timed region."""
-    import numpy as np
+def host_description():
+    """CPU model, cores this process may run on, and the BLAS NumPy uses."""
     from threadpoolctl import threadpool_info
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    blas = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+    return {"cpu_model": model, "affinity_cores": len(os.sched_getaffinity(0)),
+            "blas": (f"{blas[0].get('internal_api')} {blas[0].get('version')}" if blas else "unknown"),
+            "blas_threads": int(max([p.get("num_threads", 1) for p in blas] + [1]))}
 
+
+# tokens of the oracle's timed sample per workload (whole batch when smaller)
+CPU_SAMPLE = {0: 64, 1: 16, 2: 256, 3: 2, 4: 8, 5: 16}
+CPU_SECONDS = 10.0
+
+
+def cpu_baseline(cfg, x_cpu, n_tokens: int):
+    """Time the CPU oracle (as it stands, float64 NumPy) on a bounded sample of
+    the same workload: its first n_tokens tokens, the weights of the experts
+    they use decoded from their stored bits inside the timed region
+    (generation is not timed); the sample is repeated until about 10 s of
+    CPU work have been timed."""
     import oracle.moe_oracle as O
     from mixture_experts_ffn_09_amd import workloads as W
     from tests import _harness as Hh
@@ -138,7 +165,6 @@ def cpu_baseline(cfg, x_cpu, n_tokens: int):
         w = stored[e]
         return tuple(Hh.decode_weight(cfg, w, kk) for kk in ("gate", "up", "down"))
 
-    # repeat the sample until about 10 s of CPU work have been timed
     reps, secs = 0, 0.0
     while reps == 0 or secs < CPU_SECONDS:
         t0 = time.perf_counter()
@@ -147,15 +173,195 @@ def cpu_baseline(cfg, x_cpu, n_tokens: int):
                       expert(cfg.n_experts) if cfg.n_shared else None)
         secs += time.perf_counter() - t0
         reps += 1
-    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    return {"value": round(n_tokens * reps / secs, 3), "unit": "tokens/s", "cores": int(threads),
-            "kind": "oracle",
+    host = host_description()
+    return {"value": round(n_tokens * reps / secs, 3), "unit": "tokens/s",
+            "cores": host["blas_threads"], "kind": "oracle",
             "sample": f"first {n_tokens} of {cfg.T} tokens x {reps} runs, {len(need)} experts "
-                      f"decoded from stored bits, float64 NumPy, {secs:.2f} s"}
+                      f"decoded from stored bits, float64 NumPy, {secs:.2f} s",
+            "host": host}
 
 
-CPU_SAMPLE = {0: 64, 1: 16, 2: 16, 3: 4, 4: 8, 5: 16}
-CPU_SECONDS = 10.0
+def stats_ms(v):
+    return {"median": round(statistics.median(v), 4), "min": round(min(v), 4),
+            "mean": round(sum(v) / len(v), 4)}
+
+
+def run_workload(cfg, steps: int, warmup: int, scrub, next_rows: bool = True):
+    """Build one workload's layer, time it, and return its record (and the
+    host copy of its input)."""
+    import torch
+
+    from mixture_experts_ffn_09_amd import moe, workloads as W
+    from mixture_experts_ffn_09_amd.layer import build_device_layer
+
+    print(f"[bench] building {cfg.name}", file=sys.stderr, flush=True)
+    L = build_device_layer(cfg)
+    x_cpu = W.make_x(cfg)
+    x = x_cpu.to("cuda")
+    T, k, N, d, f = cfg.T, cfg.top_k, cfg.n_experts, cfg.d_model, cfg.d_ff
+    adt = x.dtype
+    s = L.shape_for(T)
+    ws = L.workspace()
+    rb = L.routing_buffers()
+    routing = moe.make_routing(**rb)
+    h = torch.empty(T * k, f, dtype=adt, device="cuda")
+    y = torch.empty(T * k, d, dtype=adt, device="cuda")
+    h_sh = torch.empty(T, f, dtype=adt, device="cuda") if cfg.n_shared else None
+    y_sh = torch.empty(T, d, dtype=adt, device="cuda") if cfg.n_shared else None
+    out = torch.empty_like(x)
+
+    def staged(ev):
+        ev[0].record()
+        moe.moe_router_topk(s, x, L.weights, rb["topk_idx"], rb["topk_w"], ws)
+        ev[1].record()
+        moe.moe_permute(s, rb["topk_idx"], None, routing, ws)
+        ev[2].record()
+        moe.moe_expert_gate_up(s, x, None, rb["perm_token"], rb["offsets"], L.weights, h, h_sh, ws)
+        ev[3].record()
+        moe.moe_expert_down(s, h, h_sh, rb["offsets"], L.weights, y, y_sh, ws)
+        ev[4].record()
+        moe.moe_combine(s, y, y_sh, rb["inv_perm"], rb["topk_w"], out)
+        ev[5].record()
+
+    def forward():
+        moe.moe_layer_forward(s, L.weights, x, out, ws, routing)
+
+    def new_events(n):
+        return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+
+    for _ in range(warmup):
+        forward()
+        staged(new_events(6))
+    torch.cuda.synchronize()
+
+    # Timed region 1 (the reported value): K single-call steps, each between
+    # its own events; the scrub write before each step is outside them.
+    print(f"[bench] {cfg.name}: timing {steps} steps", file=sys.stderr, flush=True)
+    ev1 = [new_events(2) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        scrub.fill_(i & 0xFF)
+        ev1[i][0].record()
+        forward()
+        ev1[i][1].record()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    step_ms = [e[0].elapsed_time(e[1]) for e in ev1]
+
+    # Timed region 2: the same steps through the per-stage entry points with
+    # events between the stages (each stage's kernel time).
+    ev2 = [new_events(6) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        scrub.fill_((i + 1) & 0xFF)
+        staged(ev2[i])
+    torch.cuda.synchronize()
+    stage_all = {name: [ev[j].elapsed_time(ev[j + 1]) for ev in ev2]
+                 for j, name in enumerate(STAGES)}
+    staged_ms = [ev[0].elapsed_time(ev[5]) for ev in ev2]
+
+    nxt = timed_next_rows(cfg, L, x, rb, ws, s, steps) if next_rows else None
+
+    counts = rb["counts"].cpu()
+    touched = int((counts > 0).sum())
+    st, layer = accounting(cfg, touched)
+    stages = {}
+    for name in STAGES:
+        m = stats_ms(stage_all[name])
+        r = roofline_for(cfg, st[name], m["mean"])
+        stages[name] = {"ms": m, "bytes": st[name]["bytes"], "flops": st[name]["flops"],
+                        "bound": r["bound"], "frac": r["frac"], "achieved": r["achieved"],
+                        "unit": r["unit"]}
+    dom = "gate_up"
+    roof = roofline_for(cfg, st[dom], stats_ms(stage_all[dom])["mean"])
+    roof["traffic"] = measured_traffic(cfg.name)
+    roof["kernel"] = "expert gate/up + SwiGLU (moe_expert_gate_up)"
+    ms = stats_ms(step_ms)
+    med = ms["median"]
+    rec = {
+        "workload": cfg.name, "T": T, "ms_per_step": ms, "tokens_per_s": round(T / (med * 1e-3), 2),
+        "wall_ms_per_step_incl_scrub": round(wall_ms, 4),
+        "config": {"workload": cfg.name, "T": T, "d_model": d, "n_experts": N, "top_k": k,
+                   "d_ff": f, "n_shared": cfg.n_shared, "route": cfg.route,
+                   "weights": cfg.w_dtype, "experts_touched": touched,
+                   "max_over_mean_load": round(float(counts.max()) /
+                                               max(1e-9, float(counts.float().mean())), 3)},
+        "roofline": roof,
+        "layer": {"algorithmic_bytes": layer["bytes"], "flops": layer["flops"],
+                  "hbm_GBps": round(layer["bytes"] / (med * 1e-3) / 1e9, 1),
+                  "hbm_frac": round(layer["bytes"] / (med * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                  "TFLOPs": round(layer["flops"] / (med * 1e-3) / 1e12, 2),
+                  "mfma_frac": round(layer["flops"] / (med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                  "staged_ms_per_step": stats_ms(staged_ms)},
+        "stages": stages,
+        "next_rows": nxt,
+    }
+    del L, ws, h, y, h_sh, y_sh, out, x
+    torch.cuda.empty_cache()
+    return rec, x_cpu
+
+
+def timed_next_rows(cfg, L, x, rb, ws, s, steps):
+    """The NEXT-row entry points on the same stream: load statistics plus one
+    selection-bias step, capacity-limited dispatch at capacity factor 1.0,
+    and group-limited selection (8 groups, at most 4 per token)."""
+    import torch
+
+    from mixture_experts_ffn_09_amd import moe
+
+    T, k, N_, d = cfg.T, cfg.top_k, cfg.n_experts, cfg.d_model
+    adt = x.dtype
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(fn):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    st_out = [torch.empty(N_, device="cuda"), torch.empty(N_, device="cuda"),
+              torch.empty(1, device="cuda")]
+    bias_scratch = L.tensors["select_bias"].clone() if cfg.route == "sigmoid" else None
+    ls_ms = timed(lambda: moe.moe_load_stats(s, x, L.weights, rb["counts"], ws, 0.01, 1e-3,
+                                             *st_out, bias_scratch))
+    ls_bytes = T * d * (2 if adt == torch.bfloat16 else 4) + d * N_ * 4 + 4 * N_ * 4
+    ls_gbs = ls_bytes / (ls_ms * 1e-3) / 1e9
+
+    cap = -(-T * k // N_)  # ceil(1.0 * T * k / N)
+    rc = {kk: torch.empty_like(v) for kk, v in rb.items() if kk in
+          ("counts", "offsets", "perm_token", "inv_perm")}
+    rcs = moe.make_routing(**rc)
+    out_c = torch.empty_like(x)
+    cap_ms = timed(lambda: moe.moe_permute_capacity(s, rb["topk_idx"], cap, rcs, ws))
+    kept = int(rc["offsets"][N_].item())
+    cap_layer_ms = timed(lambda: moe.moe_layer_forward_capacity(s, L.weights, x, out_c, cap, ws))
+
+    grouped = None
+    if N_ % 8 == 0 and 4 * (N_ // 8) >= k:
+        gi = torch.empty_like(rb["topk_idx"])
+        gw_ = torch.empty_like(rb["topk_w"])
+        g_router_ms = timed(lambda: moe.moe_router_topk_grouped(s, x, L.weights, 8, 4, gi, gw_, ws))
+        g_layer_ms = timed(lambda: moe.moe_layer_forward_grouped(s, L.weights, x, out_c, 8, 4, ws))
+        grouped = {"n_groups": 8, "max_groups": 4, "router_topk_ms": round(g_router_ms, 4),
+                   "layer_ms": round(g_layer_ms, 4),
+                   "layer_tokens_per_s": round(T / (g_layer_ms * 1e-3), 2),
+                   "what": "moe_router_topk_grouped and moe_layer_forward_grouped"}
+    return {"load_stats": {
+        "ms": round(ls_ms, 4), "bytes": ls_bytes, "bound": "hbm",
+        "achieved": round(ls_gbs, 1), "unit": "GB/s", "frac": round(ls_gbs / PEAK_HBM_GBS, 4),
+        "what": "moe_load_stats: router probabilities, shares, balancing term, bias step"},
+        "capacity_dispatch": {
+            "capacity_factor": 1.0, "capacity": cap, "kept": kept, "assignments": T * k,
+            "permute_capacity_ms": round(cap_ms, 4), "layer_ms": round(cap_layer_ms, 4),
+            "layer_tokens_per_s": round(T / (cap_layer_ms * 1e-3), 2),
+            "what": "moe_permute_capacity and moe_layer_forward_capacity, C = ceil(T*k/N)"},
+        "group_limited": grouped}
 
 
 def main():
@@ -163,7 +369,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=1, help="workload index (1 = Mixtral decode)")
+    ap.add_argument("--config", type=int, default=2, help="reported workload (2 = Mixtral prefill)")
+    ap.add_argument("--only", action="store_true", help="time the reported workload only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB, --steps times (calibrates "
@@ -186,199 +393,49 @@ def main():
         print(json.dumps({"copy_probe_bytes": n, "launches": a.steps}))
         return
 
-    from mixture_experts_ffn_09_amd import moe, workloads as W
-    from mixture_experts_ffn_09_amd.layer import build_device_layer
+    from mixture_experts_ffn_09_amd import workloads as W
 
+    scrub = torch.empty(SCRUB_BYTES, dtype=torch.uint8, device="cuda")
     cfg = W.CONFIGS[a.config]
-    print(f"[bench] building {cfg.name}", file=sys.stderr, flush=True)
-    L = build_device_layer(cfg)
-    x_cpu = W.make_x(cfg)
-    x = x_cpu.to("cuda")
-    T, k, N, d, f = cfg.T, cfg.top_k, cfg.n_experts, cfg.d_model, cfg.d_ff
-    adt = x.dtype
-    s = L.shape_for(T)
-    ws = L.workspace()
-    rb = L.routing_buffers()
-    routing = moe.make_routing(**rb)
-    h = torch.empty(T * k, f, dtype=adt, device="cuda")
-    y = torch.empty(T * k, d, dtype=adt, device="cuda")
-    h_sh = torch.empty(T, f, dtype=adt, device="cuda") if cfg.n_shared else None
-    y_sh = torch.empty(T, d, dtype=adt, device="cuda") if cfg.n_shared else None
-    out = torch.empty_like(x)
-
-    def step(ev=None):
-        if ev is not None:
-            ev[0].record()
-        moe.moe_router_topk(s, x, L.weights, rb["topk_idx"], rb["topk_w"], ws)
-        if ev is not None:
-            ev[1].record()
-        moe.moe_permute(s, rb["topk_idx"], None, routing, ws)
-        if ev is not None:
-            ev[2].record()
-        moe.moe_expert_gate_up(s, x, None, rb["perm_token"], rb["offsets"], L.weights, h, h_sh, ws)
-        if ev is not None:
-            ev[3].record()
-        moe.moe_expert_down(s, h, h_sh, rb["offsets"], L.weights, y, y_sh, ws)
-        if ev is not None:
-            ev[4].record()
-        moe.moe_combine(s, y, y_sh, rb["inv_perm"], rb["topk_w"], out)
-        if ev is not None:
-            ev[5].record()
-
-    def forward():
-        moe.moe_layer_forward(s, L.weights, x, out, ws, routing)
-
-    for _ in range(a.warmup):
-        forward()
-        step()
-    torch.cuda.synchronize()
-
-    # Timed region 1 (the reported value): K steps of the single C-ABI call
-    # that runs the whole layer, nothing else on the stream.
-    print(f"[bench] timing {a.steps} steps", file=sys.stderr, flush=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(a.steps):
-        forward()
-    torch.cuda.synchronize()
-    ms_step = (time.perf_counter() - t0) * 1e3 / a.steps
-
-    # Timed region 2: the same work through the per-stage entry points, with
-    # HIP events recorded on the launch stream between stages; these give
-    # each stage's kernel time (the event records add a few microseconds to
-    # the step, so this region's step time is reported only for reference).
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(a.steps)]
-    torch.cuda.synchronize()
-    t2 = time.perf_counter()
-    for i in range(a.steps):
-        step(events[i])
-    torch.cuda.synchronize()
-    staged_ms = (time.perf_counter() - t2) * 1e3 / a.steps
-    stage_ms = {name: sum(ev[j].elapsed_time(ev[j + 1]) for ev in events) / a.steps
-                for j, name in enumerate(STAGES)}
-
-    # Next-row kernels, timed on the same stream: load statistics of this
-    # batch plus one selection-bias step (on a scratch copy of the bias)
-    N_ = cfg.n_experts
-    st_out = [torch.empty(N_, device="cuda"), torch.empty(N_, device="cuda"),
-              torch.empty(1, device="cuda")]
-    bias_scratch = (L.tensors["select_bias"].clone() if cfg.route == "sigmoid" else None)
-    for _ in range(2):
-        moe.moe_load_stats(s, x, L.weights, rb["counts"], ws, 0.01, 1e-3, *st_out, bias_scratch)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record()
-    for _ in range(a.steps):
-        moe.moe_load_stats(s, x, L.weights, rb["counts"], ws, 0.01, 1e-3, *st_out, bias_scratch)
-    e1.record()
-    torch.cuda.synchronize()
-    ls_ms = e0.elapsed_time(e1) / a.steps
-    ls_bytes = T * d * (2 if adt == torch.bfloat16 else 4) + d * N_ * 4 + 4 * N_ * 4
-    ls_gbs = ls_bytes / (ls_ms * 1e-3) / 1e9
-
-    # Capacity-limited dispatch at capacity factor 1.0: the capped routing on
-    # its own, and the whole layer with it
-    cap = -(-T * k // N_)  # ceil(1.0 * T * k / N)
-    rc = {kk: torch.empty_like(v) for kk, v in rb.items() if kk in
-          ("counts", "offsets", "perm_token", "inv_perm")}
-    rcs = moe.make_routing(**rc)
-    out_c = torch.empty_like(x)
-    for _ in range(2):
-        moe.moe_permute_capacity(s, rb["topk_idx"], cap, rcs, ws)
-        moe.moe_layer_forward_capacity(s, L.weights, x, out_c, cap, ws)
-    torch.cuda.synchronize()
-    e0.record()
-    for _ in range(a.steps):
-        moe.moe_permute_capacity(s, rb["topk_idx"], cap, rcs, ws)
-    e1.record()
-    torch.cuda.synchronize()
-    cap_ms = e0.elapsed_time(e1) / a.steps
-    kept = int(rc["offsets"][N_].item())
-    e0.record()
-    for _ in range(a.steps):
-        moe.moe_layer_forward_capacity(s, L.weights, x, out_c, cap, ws)
-    e1.record()
-    torch.cuda.synchronize()
-    cap_layer_ms = e0.elapsed_time(e1) / a.steps
-
-    # Group-limited selection, DeepSeek-V3 style: 8 groups of N/8 experts,
-    # at most 4 groups per token (when the shape allows it)
-    grouped = None
-    if N_ % 8 == 0 and 4 * (N_ // 8) >= k:
-        gi = torch.empty_like(rb["topk_idx"])
-        gw_ = torch.empty_like(rb["topk_w"])
-        for _ in range(2):
-            moe.moe_router_topk_grouped(s, x, L.weights, 8, 4, gi, gw_, ws)
-        torch.cuda.synchronize()
-        e0.record()
-        for _ in range(a.steps):
-            moe.moe_router_topk_grouped(s, x, L.weights, 8, 4, gi, gw_, ws)
-        e1.record()
-        torch.cuda.synchronize()
-        g_router_ms = e0.elapsed_time(e1) / a.steps
-        e0.record()
-        for _ in range(a.steps):
-            moe.moe_layer_forward_grouped(s, L.weights, x, out_c, 8, 4, ws)
-        e1.record()
-        torch.cuda.synchronize()
-        g_layer_ms = e0.elapsed_time(e1) / a.steps
-        grouped = {"n_groups": 8, "max_groups": 4, "router_topk_ms": round(g_router_ms, 4),
-                   "layer_ms": round(g_layer_ms, 4),
-                   "layer_tokens_per_s": round(T / (g_layer_ms * 1e-3), 2),
-                   "what": "moe_router_topk_grouped and moe_layer_forward_grouped"}
-
-    counts = rb["counts"].cpu()
-    touched = int((counts > 0).sum())
-    st, layer = accounting(cfg, touched)
-    stages = {}
-    for name in STAGES:
-        r = roofline_for(cfg, st[name], stage_ms[name])
-        stages[name] = {"ms": round(stage_ms[name], 4), "bytes": st[name]["bytes"],
-                        "flops": st[name]["flops"], "bound": r["bound"], "frac": r["frac"],
-                        "achieved": r["achieved"], "unit": r["unit"]}
-    dom = "gate_up"
-    roof = roofline_for(cfg, st[dom], stage_ms[dom])
-    roof["traffic"] = measured_traffic(cfg.name)
-    roof["kernel"] = "expert gate/up + SwiGLU (moe_expert_gate_up)"
+    main_rec, x_cpu = run_workload(cfg, a.steps, a.warmup, scrub)
+    others = {}
+    if not a.only:
+        for c in W.CONFIGS:
+            if c.index == a.config:
+                continue
+            r, _ = run_workload(c, a.steps, a.warmup, scrub)
+            others[c.name] = r
     ach = achievable(torch)
-    ach_peak = ach["hbm_copy_GBps"] if roof["bound"] == "hbm" else ach["mfma_bf16_TFLOPs"]
+    roof = main_rec["roofline"]
     if roof["bound"] in ("hbm", "mfma"):
+        ach_peak = ach["hbm_copy_GBps"] if roof["bound"] == "hbm" else ach["mfma_bf16_TFLOPs"]
         ach["dominant_kernel_frac_of_achievable"] = round(roof["achieved"] / ach_peak, 4)
-    layer_gbs = layer["bytes"] / (ms_step * 1e-3) / 1e9
-    layer_tflops = layer["flops"] / (ms_step * 1e-3) / 1e12
+    del scrub
+    torch.cuda.empty_cache()
 
+    med = main_rec["ms_per_step"]["median"]
     rec = {
-        "metric": METRIC, "value": round(T / (ms_step * 1e-3), 2), "unit": "tokens/s",
-        "n_gpus": 1, "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms_step, 4),
+        "metric": METRIC, "value": main_rec["tokens_per_s"], "unit": "tokens/s",
+        "n_gpus": 1, "steps": a.steps, "warmup": a.warmup, "ms_per_step": med,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": {"f32": "f32", "bf16": "bf16", "fp8": "fp8-e4m3 weights, bf16 activations",
                   "mxfp4": "mxfp4 (e2m1 + e8m0) weights, bf16 activations"}[cfg.w_dtype],
         "data": "synthetic (seeded random weights and inputs)",
-        "config": {"workload": cfg.name, "T": T, "d_model": d, "n_experts": N, "top_k": k,
-                   "d_ff": f, "n_shared": cfg.n_shared, "route": cfg.route,
-                   "weights": cfg.w_dtype, "experts_touched": touched,
-                   "max_over_mean_load": round(float(counts.max()) / max(1e-9, float(counts.float().mean())), 3)},
+        "config": main_rec["config"],
         "roofline": roof,
+        "timing": {"ms_per_step": main_rec["ms_per_step"],
+                   "wall_ms_per_step_incl_scrub": main_rec["wall_ms_per_step_incl_scrub"],
+                   "protocol": "per step: 1 GiB scrub write, then HIP events around one "
+                               "moe_layer_forward call; value = T / median"},
         "achievable": ach,
-        "layer": {"algorithmic_bytes": layer["bytes"], "flops": layer["flops"],
-                  "hbm_GBps": round(layer_gbs, 1), "hbm_frac": round(layer_gbs / PEAK_HBM_GBS, 4),
-                  "TFLOPs": round(layer_tflops, 2),
-                  "staged_ms_per_step": round(staged_ms, 4)},
-        "stages": stages,
-        "next_rows": {"load_stats": {
-            "ms": round(ls_ms, 4), "bytes": ls_bytes, "bound": "hbm",
-            "achieved": round(ls_gbs, 1), "unit": "GB/s", "frac": round(ls_gbs / PEAK_HBM_GBS, 4),
-            "what": "moe_load_stats: router probabilities, shares, balancing term, bias step"},
-            "capacity_dispatch": {
-                "capacity_factor": 1.0, "capacity": cap, "kept": kept, "assignments": T * k,
-                "permute_capacity_ms": round(cap_ms, 4), "layer_ms": round(cap_layer_ms, 4),
-                "layer_tokens_per_s": round(T / (cap_layer_ms * 1e-3), 2),
-                "what": "moe_permute_capacity and moe_layer_forward_capacity, C = ceil(T*k/N)"},
-            "group_limited": grouped},
+        "layer": main_rec["layer"],
+        "stages": main_rec["stages"],
+        "next_rows": main_rec["next_rows"],
+        "workloads": others,
     }
     if not a.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
-        rec["cpu_baseline"] = cpu_baseline(cfg, x_cpu, min(T, CPU_SAMPLE.get(a.config, 8)))
+        rec["cpu_baseline"] = cpu_baseline(cfg, x_cpu, min(cfg.T, CPU_SAMPLE.get(a.config, 8)))
     print(json.dumps(rec), flush=True)
 
 

@@ -164,7 +164,10 @@ size_t moe_workspace_bytes(const moe_shape_t* s);
 /* a1+a2: router logits, selection and gates ([MoE-LLM] "Opening the
  * router"; [CH19] 19.3.2; [AIS-12] worked example).  x: [T][d] act_dtype.
  * Writes topk_idx [T][k] (descending selection score, exact ties to the
- * lower index) and topk_w [T][k].  Uses w->w_router, w->logit_offset and
+ * lower index) and topk_w [T][k].  A NaN selection score (from NaN inputs,
+ * weights or offsets) ranks below every other score, -inf included, NaN
+ * among themselves by index: every id is in [0, N) and k distinct experts
+ * are chosen; a token that has to take a NaN-scored expert gets NaN gates.  Uses w->w_router, w->logit_offset and
  * (sigmoid only) w->select_bias; ws holds the split partial logits (with
  * T <= 64 and N <= 8 logits and selection run in one kernel and ws is not
  * touched). */

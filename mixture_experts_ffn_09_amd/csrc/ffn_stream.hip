@@ -67,9 +67,10 @@ __device__ __forceinline__ void fp8_block_to_bf16(const u32x4_t& q, u32x4_t& lo,
 // Weight formats of the streaming kernel
 constexpr int WF_BF16 = 0, WF_FP8 = 1, WF_MXFP4 = 2;
 
-// E8M0 scale byte -> float 2^(e - 127) (e = 0 is the subnormal 2^-127)
+// E8M0 scale byte -> float 2^(e - 127) (e = 0 is the subnormal 2^-127);
+// e = 255 is the format's NaN
 __device__ __forceinline__ float e8m0_to_f32(uint32_t e) {
-  return __uint_as_float(e ? (e << 23) : 0x00400000u);
+  return __uint_as_float(e == 255u ? 0x7fc00000u : (e ? (e << 23) : 0x00400000u));
 }
 
 // 8 E2M1 codes (one 32-bit word, element 2i in the low nibble of byte i) ->
@@ -391,10 +392,12 @@ __device__ __forceinline__ void stream_body(const StreamParams& p, int nb0, int 
 
 // HOT: a routed group with more than 16 rows takes passes of 32 rows (MB =
 // 2, half the ring depth) and one with more than 32 rows passes of 64 (MB =
-// 4, a quarter of it), so the registers stay within the 16-row form's,
-// instead of streaming its weights once per 16 rows: with skewed routing a
-// few hot experts hold many of the rows (on the skewed fp8 decode workload
-// this cut the gate/up time by 12%).
+// 4, a quarter of it, but 2 at most and never more than D), so the registers
+// stay within the 16-row form's, instead of streaming its weights once per 16
+// rows: with skewed routing a few hot experts hold many of the rows (on the
+// skewed fp8 decode workload this cut the gate/up time by 12%).  Each ring
+// depth used here divides D, and D divides the K steps, so the K loop never
+// runs past the last step.
 template <int MB, int NP, int D, int FMT, bool GATED, bool HOT, bool LDSA>
 __global__ __launch_bounds__(256) void ffn_stream_kernel(StreamParams p) {
   // activation chunks: two buffers of up to 8 KB (bf16) or 16 KB (FP8, MXFP4)
@@ -422,7 +425,7 @@ __global__ __launch_bounds__(256) void ffn_stream_kernel(StreamParams p) {
   }
   if (rows <= m_first) return;
   if (HOT && !shared && rows > 32)
-    stream_body<4, NP, (D >= 8 ? D / 4 : 2), FMT, GATED, false, LDSA && HOT>(
+    stream_body<4, NP, (D >= 8 ? D / 4 : (D >= 2 ? 2 : 1)), FMT, GATED, false, LDSA && HOT>(
         p, nb0, g, shared, row_base, rows, m_first, alds, store);
   else if (HOT && !shared && rows > 16)
     stream_body<2, NP, (D >= 4 ? D / 2 : D), FMT, GATED, false, LDSA && HOT>(

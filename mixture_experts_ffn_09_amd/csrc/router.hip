@@ -442,10 +442,12 @@ __global__ __launch_bounds__(256) void router_logits_tiled(const void* __restric
 // ---------------------------------------------------------------------------
 // Candidate (score s, index i) as one integer whose order is that of (s desc,
 // i asc): the float's bits made monotone (-0 taken as +0) above the inverted
-// index.  0 is below every candidate and marks "none"; a NaN score gets 0, so
-// it is never selected.
+// index.  0 is below every candidate and marks "none".  A NaN score ranks
+// below every other score, -inf included (its upper half is 0, below the
+// monotone bits of -inf), and among NaN scores the lower index wins, so k
+// experts are always chosen and every id lies in [0, N).
 __device__ __forceinline__ uint64_t order_key(float s, int idx) {
-  if (s != s) return 0;
+  if (s != s) return 0xFFFFFFFFull - (uint32_t)idx;
   uint32_t u = __float_as_uint(s);
   if (u == 0x80000000u) u = 0;
   u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
@@ -517,9 +519,13 @@ __device__ __forceinline__ void select_topk(const float (&lg)[NJ], int N, int k,
     for (int j = 0; j < NJ; ++j)
       if (live[j]) gscr[lane + 64 * j] = sc[j];
     __builtin_amdgcn_wave_barrier();
+    // the group's best score: fmaxf skips NaN, so the maximum is NaN only
+    // when every score of the group is NaN (and then ranks lowest)
     float gm = -INFINITY;
-    if (lane < G)
-      for (int e = lane * gsize; e < (lane + 1) * gsize; ++e) gm = fmaxf(gm, gscr[e]);
+    if (lane < G) {
+      gm = gscr[lane * gsize];
+      for (int e = lane * gsize + 1; e < (lane + 1) * gsize; ++e) gm = fmaxf(gm, gscr[e]);
+    }
     uint64_t gk = lane < G ? order_key(gm, lane) : 0;
     uint64_t allowed = 0;
     for (int r = 0; r < max_groups; ++r) {

@@ -10,6 +10,8 @@ choice only selects which of them to compare against.
 from __future__ import annotations
 
 import itertools
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import replace
 from functools import lru_cache
 
@@ -144,3 +146,56 @@ def to_np(t: torch.Tensor) -> np.ndarray:
     if t.dtype == torch.bfloat16:
         return O.bf16_bits_to_f64(bits16(t))
     return t.numpy()
+
+
+def host_threads() -> int:
+    """Worker threads for host-side test work (the GPU machine's CPU share is 16
+    whatever os.cpu_count() shows)."""
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+class ExpertPrefetch:
+    """Expert weights for the oracle, generated and decoded from their stored
+    bits in a thread pool a bounded window ahead of the order in which the
+    oracle will ask for them (ascending expert id, the order of
+    ``O.moe_forward_with_routing``).  Call it with e to get (w_gate, w_up,
+    w_down) as float64; each expert is produced once and then dropped."""
+
+    def __init__(self, cfg: W.MoEConfig, order, threads: int | None = None,
+                 window: int | None = None):
+        self.cfg = cfg
+        self.order = [int(e) for e in order]
+        self.threads = threads or host_threads()
+        self.window = window or 2 * self.threads
+        self.pool = ThreadPoolExecutor(self.threads)
+        self.futs = {}
+        self.nxt = 0
+        self.pos = 0
+        self._fill()
+
+    def _fill(self):
+        while self.nxt < len(self.order) and self.nxt < self.pos + self.window:
+            e = self.order[self.nxt]
+            self.futs[e] = self.pool.submit(oracle_expert, self.cfg, e)
+            self.nxt += 1
+
+    def __call__(self, e: int):
+        assert self.pos < len(self.order) and e == self.order[self.pos], (e, self.pos)
+        w = self.futs.pop(e).result()
+        self.pos += 1
+        self._fill()
+        if self.pos == len(self.order):
+            self.pool.shutdown(wait=False)
+        return w
+
+
+def oracle_layer(cfg: W.MoEConfig, xo: np.ndarray, idx: np.ndarray, gates: np.ndarray):
+    """The oracle's layer output for a given routing on every token,
+    streaming the experts (generated and decoded in parallel, computed in
+    ascending order by ``O.moe_forward_with_routing``).  Returns (out,
+    Permutation, y_perm, y_shared)."""
+    counts = np.bincount(np.asarray(idx).reshape(-1), minlength=cfg.n_experts)
+    order = [e for e in range(cfg.n_experts) if counts[e] > 0]
+    shared = oracle_expert(cfg, cfg.n_experts) if cfg.n_shared else None
+    src = ExpertPrefetch(cfg, order)
+    return O.moe_forward_with_routing(xo, idx, gates, src, cfg.n_experts, shared)

@@ -1,7 +1,7 @@
 """GPU parity: the HIP path through the C ABI against the CPU oracle.
 
-Small cases run the oracle on every token; full-size cases check routing and
-the permutation on every token and the layer output on sampled tokens.
+Every case, the full-size workloads included, compares every token's output
+(and, at full size, every expert row) with the oracle.
 """
 
 from __future__ import annotations
@@ -85,6 +85,12 @@ SMALL = {
                                            w_dtype="mxfp4"),
     "mxfp4_many_rows": H.small_config(C[2], 152, T=300, d_model=256, d_ff=256, n_experts=4,
                                       w_dtype="mxfp4"),
+    # odd K-step counts (3 on gate/up, 5 on down: a ring depth of 1) with a
+    # hot expert of more than 32 rows in a 16-row launch (its 64-row passes)
+    "stream_odd_ksteps_hot": H.small_config(C[1], 123, T=64, d_model=96, d_ff=160,
+                                            zipf_c=3.0),
+    # float32 activations with more than 8 experts: the tiled fp32 router
+    "router_tiled_f32_N16": H.small_config(C[0], 124, T=100, n_experts=16, top_k=4),
 }
 
 
@@ -93,7 +99,7 @@ def _log(msg):
     sys.stdout.flush()
 
 
-def _run_gpu(cfg, sample_tokens=None):
+def _run_gpu(cfg):
     _log(f"[case] {cfg.name} idx={cfg.index} T={cfg.T} d={cfg.d_model} N={cfg.n_experts} "
          f"k={cfg.top_k} d_ff={cfg.d_ff} w={cfg.w_dtype}")
     L = build_device_layer(cfg)
@@ -106,7 +112,7 @@ def _run_gpu(cfg, sample_tokens=None):
     return L, x, xd, out, g
 
 
-def _check_case(cfg, x, out, g, sample=None):
+def _check_case(cfg, x, out, g):
     xo = H.x_f64(cfg, x)
     w_r, off, bias = H.oracle_router(cfg)
     R = O.route_tokens(xo, w_r, cfg.top_k, cfg.route, off, bias)
@@ -114,12 +120,11 @@ def _check_case(cfg, x, out, g, sample=None):
     ref_g = O.gate_weights(R.logits, ref_idx, cfg.route)
     H.check_gates(g["topk_idx"], g["topk_w"], ref_idx, ref_g)
     H.check_permutation(g, ref_idx, cfg.n_experts)
-    toks = np.arange(cfg.T) if sample is None else np.asarray(sample)
     shared = H.oracle_expert(cfg, cfg.n_experts) if cfg.n_shared else None
-    ref, _, _, _ = O.moe_forward_with_routing(xo[toks], ref_idx[toks], ref_g[toks],
+    ref, _, _, _ = O.moe_forward_with_routing(xo, ref_idx, ref_g,
                                               lambda e: H.oracle_expert(cfg, e),
                                               cfg.n_experts, shared)
-    got = H.to_np(out)[toks]
+    got = H.to_np(out)
     err = H.assert_close(got, ref, H.TOL[cfg.w_dtype])
     if cfg.w_dtype == "f32":
         H.assert_close(got, ref, H.TOL_F32_INTERNAL, "out (f32 internal bar)")
@@ -134,32 +139,56 @@ def test_layer_small(name):
     _check_case(cfg, x, out, g)
 
 
-def _sample_tokens(cfg, xo, n_tok, max_experts):
-    """Tokens whose union of experts stays small (keeps the oracle quick)."""
-    w_r, off, bias = H.oracle_router(cfg)
-    R = O.route_tokens(xo, w_r, cfg.top_k, cfg.route, off, bias)
-    rng = np.random.default_rng(cfg.index)
-    chosen, used = [], set()
-    for t in rng.permutation(cfg.T):
-        s = set(int(e) for e in R.idx[t])
-        if len(used | s) <= max_experts:
-            chosen.append(int(t))
-            used |= s
-        if len(chosen) == n_tok:
-            break
-    chosen.append(cfg.T - 1)  # always include the ragged end
-    return sorted(set(chosen))
+def _worst(got, ref, tol):
+    """Largest |got - ref| / (tol (1 + |ref|)) (1.0 = at the bar)."""
+    return float((np.abs(got - ref) / (tol * (1.0 + np.abs(ref)))).max())
 
 
 @pytest.mark.parametrize("ci", [1, 2, 3, 4, 5])
-def test_layer_full_size_sampled(ci):
+def test_layer_full_size(ci):
+    """Each full-size workload on every token: routing, gates and the
+    permutation against the oracle, the layer output of every token, and the
+    expert rows y_perm / y_shared of a staged run (router, permute, grouped
+    FFN, combine through their own entry points) row by row.  The oracle
+    streams the experts (generated and decoded in parallel)."""
     cfg = C[ci]
     L, x, xd, out, g = _run_gpu(cfg)
-    xo = H.x_f64(cfg, x)
-    sample = None if cfg.T <= 16 else _sample_tokens(cfg, xo, 48, 24)
-    _check_case(cfg, x, out, g, sample)
-    del L
+    s, ws = L.shape_for(cfg.T), L.workspace()
+    rb = L.routing_buffers()
+    moe.moe_router_topk(s, xd, L.weights, rb["topk_idx"], rb["topk_w"], ws)
+    moe.moe_permute(s, rb["topk_idx"], None, moe.make_routing(**rb), ws)
+    y = torch.empty(cfg.T * cfg.top_k, cfg.d_model, dtype=xd.dtype, device="cuda")
+    ys = torch.empty(cfg.T, cfg.d_model, dtype=xd.dtype, device="cuda") if cfg.n_shared else None
+    moe.moe_grouped_ffn(s, xd, None, rb["perm_token"], rb["offsets"], L.weights, y, ys, ws)
+    out2 = torch.empty_like(xd)
+    moe.moe_combine(s, y, ys, rb["inv_perm"], rb["topk_w"], out2)
+    torch.cuda.synchronize()
+    for key, v in g.items():
+        assert np.array_equal(v, rb[key].cpu().numpy()), key
+    assert torch.equal(out2.view(torch.int16), out.view(torch.int16))
+    got_out, got_y = H.to_np(out), H.to_np(y)
+    got_ys = H.to_np(ys) if ys is not None else None
+    del L, ws, y, ys, out2, rb
     torch.cuda.empty_cache()
+
+    xo = H.x_f64(cfg, x)
+    w_r, off, bias = H.oracle_router(cfg)
+    R = O.route_tokens(xo, w_r, cfg.top_k, cfg.route, off, bias)
+    ref_idx, ties = H.resolve_routing(R, g["topk_idx"], cfg.top_k)
+    ref_g = O.gate_weights(R.logits, ref_idx, cfg.route)
+    H.check_gates(g["topk_idx"], g["topk_w"], ref_idx, ref_g)
+    H.check_permutation(g, ref_idx, cfg.n_experts)
+    _log(f"  routing ok on all {cfg.T} tokens (near-ties {len(ties)}); oracle layer ...")
+    ref, P, yref, ysref = H.oracle_layer(cfg, xo, ref_idx, ref_g)
+    tol = H.TOL[cfg.w_dtype]
+    err = H.assert_close(got_out, ref, tol)
+    H.assert_close(got_y, yref, tol, "y_perm")
+    worst = {"out": _worst(got_out, ref, tol), "y_perm": _worst(got_y, yref, tol)}
+    if cfg.n_shared:
+        H.assert_close(got_ys, ysref, tol, "y_shared")
+        worst["y_shared"] = _worst(got_ys, ysref, tol)
+    _log(f"  ok: {cfg.T} tokens, {cfg.T * cfg.top_k} expert rows; max abs err {err[0]:.3e}; "
+         "worst err / bound " + ", ".join(f"{k} {v:.3f}" for k, v in worst.items()))
 
 
 @pytest.mark.parametrize("name", ["c4_structure_T37", "decode_sigmoid_T16"])
@@ -286,3 +315,51 @@ def test_permute_direct_against_sorted(T, N, k):
     for row, (e, t, i) in enumerate(keys):
         want_inv[t, i] = row
     assert np.array_equal(g["inv_perm"], want_inv)
+
+
+def test_eight_wave_gemm_past_32bit_offsets():
+    """A batch whose H buffer (T k d_ff bf16) passes 2^31 bytes takes the
+    eight-wave GEMM (128-row tiles, 64-bit operand addresses) instead of the
+    four-wave one; every token against the oracle."""
+    cfg = H.small_config(C[2], 160, T=70000, d_model=256, n_experts=16, top_k=8, d_ff=2048)
+    assert cfg.T * cfg.top_k * cfg.d_ff * 2 > 0x7FFFFFFF
+    L, x, xd, out, g = _run_gpu(cfg)
+    del L
+    torch.cuda.empty_cache()
+    _check_case(cfg, x, out, g)
+
+
+@pytest.mark.parametrize("T,N,k,nan_experts,bf16_x", [(20, 8, 2, (1, 4), True),
+                                                      (20, 8, 7, (1, 4), True),
+                                                      (100, 16, 4, (0, 5, 6), True),
+                                                      (100, 16, 15, (0, 5, 6), False)])
+def test_nan_scores_rank_last(T, N, k, nan_experts, bf16_x):
+    """Experts whose logit offset is NaN rank below every other expert (lower
+    index first among them), on the fused small-batch router and on the
+    separate top-k kernel: ids equal the oracle's and stay in [0, N); gates
+    equal the oracle's, NaN exactly where a NaN expert had to be taken."""
+    base = C[1] if bf16_x else C[0]
+    cfg = H.small_config(base, 161, T=T, d_model=128, n_experts=N, top_k=k, d_ff=64)
+    _log(f"[case] nan scores T={T} N={N} k={k} nan={nan_experts} bf16_x={bf16_x}")
+    L = build_device_layer(cfg)
+    off = torch.zeros(N)
+    off[list(nan_experts)] = float("nan")
+    t = dict(L.tensors)
+    t["logit_offset"] = off.cuda()
+    w = moe.make_weights(**t)
+    x = W.make_x(cfg)
+    idx = torch.empty(T, k, dtype=torch.int32, device="cuda")
+    gw = torch.empty(T, k, dtype=torch.float32, device="cuda")
+    moe.moe_router_topk(L.shape_for(T), x.cuda(), w, idx, gw, L.workspace())
+    torch.cuda.synchronize()
+    gi, gg = idx.cpu().numpy(), gw.cpu().numpy()
+    w_r, _, bias = H.oracle_router(cfg)
+    R = O.route_tokens(H.x_f64(cfg, x), w_r, k, cfg.route, off.double().numpy(), bias)
+    assert ((gi >= 0) & (gi < N)).all()
+    ref_idx, _ = H.resolve_routing(R, gi, k)
+    assert np.array_equal(gi, ref_idx)
+    ref_g = O.gate_weights(R.logits, ref_idx, cfg.route)
+    assert np.array_equal(np.isnan(gg), np.isnan(ref_g))
+    ok = ~np.isnan(ref_g)
+    assert np.all(np.abs(gg[ok] - ref_g[ok]) <= 1e-5)
+    assert np.isnan(ref_g).any() == (k > N - len(nan_experts))

@@ -302,6 +302,25 @@ moe_status_t moe_layer_forward_grouped(const moe_shape_t* s, const moe_weights_t
                                        int32_t max_groups, moe_routing_t* routing_out,
                                        void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* Bytes of the static device scratch behind moe_layer_forward_noalloc. */
+#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/* moe_layer_forward for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same kernels and results, with the scratch space taken
+ * from a static device array of MOE_NOALLOC_SCRATCH_BYTES (64 MiB) per GPU
+ * instead of a caller workspace.  No allocation of any kind.  The shape's
+ * moe_workspace_bytes() must not exceed that size (decode batches do: the
+ * Mixtral 8x7B shape up to about 900 tokens, the DeepSeek-V3 shape up to 256
+ * tokens), else MOE_ERR_UNSUPPORTED before any HIP call.  The array's device
+ * address is looked up on the first call on each device (the caller's
+ * current device).  All calls on one GPU share its array: calls that
+ * overlap in time on one GPU (several streams or host threads) race and
+ * must be serialised by the caller. */
+moe_status_t moe_layer_forward_noalloc(const moe_shape_t* s, const moe_weights_t* w,
+                                       const void* x, void* out,
+                                       moe_routing_t* routing_out, hipStream_t stream);
+
 /* Static description of a status code. */
 const char* moe_status_string(moe_status_t st);
 

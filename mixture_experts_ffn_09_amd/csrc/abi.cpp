@@ -11,6 +11,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "kernels.h"
 
@@ -272,6 +273,42 @@ moe_status_t run_ffn(const moe_shape_t* s, const void* x, const void* x_rows,
 
 }  // namespace
 
+// Scratch of moe_layer_forward_noalloc: a file-scope device array (each GPU
+// the library runs on holds its own copy until the process ends), in place
+// of a caller workspace.  Host code never passes the array's name to a
+// kernel or a copy (on the host it is only a stand-in for the symbol): it
+// uses the device address that hipGetSymbolAddress returns, looked up once
+// per device with that device current.  Every call on a GPU shares that
+// GPU's array; no kernel needs it cleared (each piece is written before it
+// is read within a call), and calls that overlap on one GPU race.
+__device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device.
+moe_status_t static_scratch(void** out) {
+  int dev = -1;
+  HIP_TRY("hipGetDevice", hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(MOE_ERR_UNSUPPORTED, "device %d: the static scratch covers devices 0..%d", dev,
+                kMaxDevices - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    HIP_TRY("hipGetSymbolAddress(scratch)", hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    if (!p) return fail(MOE_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* moe_status_string(moe_status_t st) {
@@ -522,10 +559,10 @@ moe_status_t moe_load_stats(const moe_shape_t* s, const void* x, const moe_weigh
   return MOE_OK;
 }
 
-static moe_status_t layer_forward(const moe_shape_t* s, const moe_weights_t* w, const void* x,
-                                  void* out, moe_routing_t* r, int32_t capacity,
-                                  const GroupLimit& g, void* ws, size_t ws_bytes,
-                                  hipStream_t stream) {
+// Arguments of the whole-layer calls other than the workspace (checked on
+// the host before any HIP call).
+static moe_status_t check_layer_args(const moe_shape_t* s, const moe_weights_t* w, const void* x,
+                                     void* out, const GroupLimit& g) {
   moe_status_t st = check_shape(s);
   if (st != MOE_OK) return st;
   if ((st = check_groups(s, g)) != MOE_OK) return st;
@@ -533,7 +570,15 @@ static moe_status_t layer_forward(const moe_shape_t* s, const moe_weights_t* w, 
   if ((st = check_weights(s, w, true, true)) != MOE_OK) return st;
   if (!x || !out) return fail(MOE_ERR_INVALID_ARG, "x / out is NULL");
   if (x == out) return fail(MOE_ERR_INVALID_ARG, "x and out must not overlap");
-  if ((st = check_aligned({x, out})) != MOE_OK) return st;
+  return check_aligned({x, out});
+}
+
+static moe_status_t layer_forward(const moe_shape_t* s, const moe_weights_t* w, const void* x,
+                                  void* out, moe_routing_t* r, int32_t capacity,
+                                  const GroupLimit& g, void* ws, size_t ws_bytes,
+                                  hipStream_t stream) {
+  moe_status_t st = check_layer_args(s, w, x, out, g);
+  if (st != MOE_OK || s->n_tokens == 0) return st;
   if ((st = check_ws(s, ws, ws_bytes)) != MOE_OK) return st;
   const WsLayout L = ws_layout(s);
   char* b = static_cast<char*>(ws);
@@ -595,6 +640,22 @@ moe_status_t moe_layer_forward_capacity(const moe_shape_t* s, const moe_weights_
                                         hipStream_t stream) {
   if (capacity < 0) return fail(MOE_ERR_INVALID_ARG, "capacity is negative");
   return layer_forward(s, w, x, out, r, capacity, GroupLimit(), ws, ws_bytes, stream);
+}
+
+moe_status_t moe_layer_forward_noalloc(const moe_shape_t* s, const moe_weights_t* w,
+                                       const void* x, void* out, moe_routing_t* r,
+                                       hipStream_t stream) {
+  moe_status_t st = check_layer_args(s, w, x, out, GroupLimit());
+  if (st != MOE_OK || s->n_tokens == 0) return st;
+  const size_t need = ws_layout(s).total;
+  if (need > MOE_NOALLOC_SCRATCH_BYTES)
+    return fail(MOE_ERR_UNSUPPORTED,
+                "this shape needs %zu bytes of scratch; moe_layer_forward_noalloc holds %zu "
+                "(use moe_layer_forward with a workspace)",
+                need, (size_t)MOE_NOALLOC_SCRATCH_BYTES);
+  void* p = nullptr;
+  if ((st = static_scratch(&p)) != MOE_OK) return st;
+  return layer_forward(s, w, x, out, r, -1, GroupLimit(), p, MOE_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 }  // extern "C"

@@ -21,6 +21,9 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE_TOO_SMALL, M
 MOE_F32, MOE_BF16, MOE_FP8_E4M3, MOE_MXFP4 = range(4)
 MOE_ROUTE_SOFTMAX_TOPK, MOE_ROUTE_SIGMOID_BIAS = range(2)
 
+# bytes of the static device scratch of moe_layer_forward_noalloc (moe_ffn.h)
+MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
+
 DTYPE_CODES = {"f32": MOE_F32, "bf16": MOE_BF16, "fp8": MOE_FP8_E4M3, "mxfp4": MOE_MXFP4}
 ROUTE_CODES = {"softmax": MOE_ROUTE_SOFTMAX_TOPK, "sigmoid": MOE_ROUTE_SIGMOID_BIAS}
 
@@ -28,7 +31,8 @@ EXPORTS = ["moe_packed_weight_bytes", "moe_pack_weights", "moe_workspace_bytes",
            "moe_router_topk", "moe_permute", "moe_grouped_ffn", "moe_expert_gate_up",
            "moe_expert_down", "moe_combine", "moe_layer_forward", "moe_load_stats",
            "moe_permute_capacity", "moe_layer_forward_capacity", "moe_router_topk_grouped",
-           "moe_layer_forward_grouped", "moe_status_string", "moe_last_error"]
+           "moe_layer_forward_grouped", "moe_layer_forward_noalloc", "moe_status_string",
+           "moe_last_error"]
 
 
 class MoEError(RuntimeError):
@@ -88,10 +92,13 @@ def lib() -> C.CDLL:
                                               P, C.c_size_t, P]
         L.moe_layer_forward_grouped.argtypes = [S, C.POINTER(Weights), P, P, C.c_int32, C.c_int32,
                                                 C.POINTER(Routing), P, C.c_size_t, P]
+        L.moe_layer_forward_noalloc.argtypes = [S, C.POINTER(Weights), P, P, C.POINTER(Routing),
+                                                P]
         for f in ("moe_pack_weights", "moe_router_topk", "moe_permute", "moe_grouped_ffn",
                   "moe_expert_gate_up", "moe_expert_down", "moe_combine", "moe_layer_forward",
                   "moe_load_stats", "moe_permute_capacity", "moe_layer_forward_capacity",
-                  "moe_router_topk_grouped", "moe_layer_forward_grouped"):
+                  "moe_router_topk_grouped", "moe_layer_forward_grouped",
+                  "moe_layer_forward_noalloc"):
             getattr(L, f).restype = C.c_int
         L.moe_status_string.argtypes = [C.c_int]
         L.moe_status_string.restype = C.c_char_p
@@ -257,3 +264,10 @@ def moe_layer_forward_grouped(shape: Shape, weights: Weights, x: torch.Tensor, o
                                            C.c_int32(n_groups), C.c_int32(max_groups),
                                            C.byref(routing) if routing is not None else None,
                                            _ptr(ws), ws.numel() * ws.element_size(), _stream()))
+
+
+def moe_layer_forward_noalloc(shape: Shape, weights: Weights, x: torch.Tensor, out: torch.Tensor,
+                              routing: Optional[Routing] = None):
+    _check(lib().moe_layer_forward_noalloc(C.byref(shape), C.byref(weights), _ptr(x), _ptr(out),
+                                           C.byref(routing) if routing is not None else None,
+                                           _stream()))

@@ -68,6 +68,15 @@ SMALL = {
     "gemm_split_tail": H.small_config(C[2], 121, T=512, d_model=2048, n_experts=4, d_ff=1024),
     "gemm_split_shared": H.small_config(C[3], 122, T=300, d_model=1024, n_experts=4, top_k=2,
                                         d_ff=1024),
+    # groups of 257..512 rows (two row tiles each, the second 64, 128 or 256
+    # rows tall): whole tiles, and last rounds cut into 2 or 4 parts, on both
+    # passes
+    "gemm_tall_parts": H.small_config(C[2], 125, T=1500, d_model=512, d_ff=1024, n_experts=8,
+                                      zipf_c=0.3),
+    "gemm_tall_whole": H.small_config(C[2], 128, T=1500, d_model=2048, d_ff=2048, n_experts=8,
+                                      zipf_c=0.3),
+    "gemm_tall_mixed": H.small_config(C[2], 129, T=1500, d_model=1280, d_ff=1536, n_experts=8,
+                                      zipf_c=0.3),
     # FP8 weights through the GEMM path (routed + shared)
     "gemm_fp8": H.small_config(C[4], 110, T=256, d_model=256, d_ff=256, n_experts=8, top_k=4),
     # decode-sized batches: ragged T, odd N, sigmoid + selection bias + logit

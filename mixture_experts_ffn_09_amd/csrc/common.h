@@ -38,7 +38,22 @@ __device__ __forceinline__ float sigmoid_f32(float z) {
   return z >= 0.0f ? p : e * p;
 }
 
-__device__ __forceinline__ float silu_f32(float z) { return z * sigmoid_f32(z); }
+// silu(z) = z / (1 + e^-z) with the hardware exponential and reciprocal
+// (about 1 ulp each; the result is rounded to bfloat16 or used in float32
+// with a tolerance far above that).  z -> -inf: e^-z overflows to inf and
+// the product is -0; z -> +inf: z.
+__device__ __forceinline__ float silu_f32(float z) {
+  return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
+}
+
+// Two floats -> two bfloat16 in one dword (lo in the low half), rounded to
+// nearest even by the hardware conversion.
+__device__ __forceinline__ uint32_t pack_bf16x2_rne(float lo, float hi) {
+  typedef float f2_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 b2_t __attribute__((ext_vector_type(2)));
+  const f2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, b2_t));
+}
 
 // Two OCP E4M3 codes (the low or high 16 bits of `w`) -> two bf16 in one
 // dword.  E4M3 values are exact in bf16, so the conversion is exact.

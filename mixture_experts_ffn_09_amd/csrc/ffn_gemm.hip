@@ -570,27 +570,57 @@ __device__ __forceinline__ void four_wave_tile(const GemmParams& p, uint8_t* lds
   }
   wait_vmcnt<0>();  // the clamped copies of the last steps
 
+  // Epilogue through LDS.  A lane holds 4 rows of one column of each 16 x 16
+  // block; neighbouring lanes hold neighbouring columns.  Lanes 2c and 2c+1
+  // swap two values (one DPP move each), so that each holds two rows of the
+  // column pair (2c, 2c+1), packs each pair into one dword (hardware RNE
+  // conversion) and writes it to the wave's staging rows in LDS; then every
+  // lane reads 16 contiguous bytes of a row back and the wave stores whole
+  // rows with 16-byte stores (a 128-byte line per 8 or 16 lanes) instead of
+  // one 2-byte store per value.
+  constexpr int WC = GATED ? NBW * 8 : NBW * 16;  // output columns of a wave
+  constexpr int WR = MBW * 16;                    // output rows of a wave
+  constexpr int RS = WC * 2 + 16;                 // staging row stride (bytes)
+  static_assert(4 * WR * RS <= FW_LDS, "epilogue staging");
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's last ring reads
+  barrier_no_fence();                  // no wave reads the rings any more
+  uint8_t* const stg = lds + wave * (WR * RS);
+  const bool odd = lane & 1;
 #pragma unroll
   for (int i = 0; i < MBW; ++i) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int r = m0 + (wm * MBW + i) * 16 + (lane >> 4) * 4 + e;
-      if (r >= rows) continue;
-      uint16_t* orow = out + (size_t)(row_base + r) * p.n_out;
-      if (GATED) {
+    for (int q = 0; q < (GATED ? NBW / 2 : NBW); ++q) {
+      float v[4];
 #pragma unroll
-        for (int q = 0; q < NBW / 2; ++q) {
-          const int col = (nb0 / 2 + wn * (NBW / 2) + q) * 16 + (lane & 15);
-          orow[col] = (uint16_t)f32_to_bf16(silu_f32(acc[i][2 * q][e]) * acc[i][2 * q + 1][e]);
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < NBW; ++j) {
-          const int col = (nb0 + wn * NBW + j) * 16 + (lane & 15);
-          orow[col] = (uint16_t)f32_to_bf16(acc[i][j][e]);
-        }
-      }
+      for (int e = 0; e < 4; ++e)
+        v[e] = GATED ? silu_f32(acc[i][2 * q][e]) * acc[i][2 * q + 1][e] : acc[i][q][e];
+      // even lanes keep rows 0, 2 and take the neighbour's; odd lanes rows 1, 3
+      const float s0 = odd ? v[0] : v[1], s1 = odd ? v[2] : v[3];
+      const float r0 = __int_as_float(
+          __builtin_amdgcn_update_dpp(0, __float_as_int(s0), 0xB1, 0xf, 0xf, false));
+      const float r1 = __int_as_float(
+          __builtin_amdgcn_update_dpp(0, __float_as_int(s1), 0xB1, 0xf, 0xf, false));
+      const uint32_t w0 = odd ? pack_bf16x2_rne(r0, v[1]) : pack_bf16x2_rne(v[0], r0);
+      const uint32_t w1 = odd ? pack_bf16x2_rne(r1, v[3]) : pack_bf16x2_rne(v[2], r1);
+      const int row = i * 16 + (lane >> 4) * 4 + (odd ? 1 : 0);
+      const int col = q * 16 + (lane & 14);
+      *reinterpret_cast<uint32_t*>(stg + row * RS + col * 2) = w0;
+      *reinterpret_cast<uint32_t*>(stg + (row + 2) * RS + col * 2) = w1;
     }
+  }
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // the wave's staging writes are done
+  __builtin_amdgcn_wave_barrier();
+  constexpr int LPR = WC * 2 / 16;     // lanes per output row
+  constexpr int RPI = 64 / LPR;        // rows per read
+  const int col0 = GATED ? (nb0 / 2 + wn * (NBW / 2)) * 16 : (nb0 + wn * NBW) * 16;
+#pragma unroll
+  for (int it = 0; it < WR / RPI; ++it) {
+    const int rr = it * RPI + lane / LPR;
+    const int c8 = (lane % LPR) * 8;
+    const u32x4_t val = *reinterpret_cast<const u32x4_t*>(stg + rr * RS + c8 * 2);
+    const int r = m0 + wm * WR + rr;
+    if (r < rows)
+      *reinterpret_cast<u32x4_t*>(out + (size_t)(row_base + r) * p.n_out + col0 + c8) = val;
   }
 }
 

@@ -342,6 +342,12 @@ def timed_next_rows(cfg, L, x, rb, ws, s, steps):
                                              *st_out, bias_scratch))
     ls_bytes = T * d * (2 if adt == torch.bfloat16 else 4) + d * N_ * 4 + 4 * N_ * 4
     ls_gbs = ls_bytes / (ls_ms * 1e-3) / 1e9
+    # the same statistics as part of the forward (no second pass over the
+    # router logits): extra time over the plain forward
+    out_s = torch.empty_like(x)
+    fwd_ms = timed(lambda: moe.moe_layer_forward(s, L.weights, x, out_s, ws))
+    fwd_stats_ms = timed(lambda: moe.moe_layer_forward_stats(s, L.weights, x, out_s, ws, None,
+                                                             0.01, 1e-3, *st_out, bias_scratch))
 
     cap = -(-T * k // N_)  # ceil(1.0 * T * k / N)
     rc = {kk: torch.empty_like(v) for kk, v in rb.items() if kk in
@@ -365,7 +371,11 @@ def timed_next_rows(cfg, L, x, rb, ws, s, steps):
     return {"load_stats": {
         "ms": round(ls_ms, 4), "bytes": ls_bytes, "bound": "hbm",
         "achieved": round(ls_gbs, 1), "unit": "GB/s", "frac": round(ls_gbs / PEAK_HBM_GBS, 4),
-        "what": "moe_load_stats: router probabilities, shares, balancing term, bias step"},
+        "what": "moe_load_stats: router probabilities, shares, balancing term, bias step",
+        "in_forward": {"layer_ms": round(fwd_ms, 4), "layer_with_stats_ms": round(fwd_stats_ms, 4),
+                       "extra_ms": round(fwd_stats_ms - fwd_ms, 4),
+                       "what": "moe_layer_forward_stats against moe_layer_forward, "
+                               "back to back without scrub"}},
         "capacity_dispatch": {
             "capacity_factor": 1.0, "capacity": cap, "kept": kept, "assignments": T * k,
             "permute_capacity_ms": round(cap_ms, 4), "layer_ms": round(cap_layer_ms, 4),

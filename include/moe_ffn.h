@@ -286,6 +286,23 @@ moe_status_t moe_layer_forward(const moe_shape_t* s, const moe_weights_t* w,
                                moe_routing_t* routing_out, void* ws,
                                size_t ws_bytes, hipStream_t stream);
 
+/* moe_layer_forward followed by the load statistics of the batch it routed
+ * and one selection-bias step, as moe_load_stats computes them (the same
+ * kernels, so the same bits), without recomputing the router logits: the
+ * statistics read the logit partials the router left in the workspace and
+ * the counts of this call's permute (the logits are recomputed only where
+ * logits and selection ran in one kernel: T <= 64 and N <= 8).  The
+ * selection uses w->select_bias as it was before the call; `bias` (may be
+ * that same buffer) receives the step afterwards, for the next batch.
+ * Outputs and errors as moe_layer_forward and moe_load_stats ([CH19] 19.3.3,
+ * 19.3.4; [MoE-LLM] "Classic fix: auxiliary loss", "DeepSeek-style bias
+ * controller"; [AIS-12] "How are experts kept evenly busy?"). */
+moe_status_t moe_layer_forward_stats(const moe_shape_t* s, const moe_weights_t* w,
+                                     const void* x, void* out, moe_routing_t* routing_out,
+                                     float alpha, float step, float* frac, float* prob,
+                                     float* aux, float* bias, void* ws, size_t ws_bytes,
+                                     hipStream_t stream);
+
 /* moe_layer_forward with capacity-limited dispatch (see
  * moe_permute_capacity): experts run only on their kept rows and dropped
  * branches contribute nothing.  routing_out, when given, receives the

@@ -529,6 +529,29 @@ moe_status_t moe_combine(const moe_shape_t* s, const void* y_perm, const void* y
   return MOE_OK;
 }
 
+static moe_status_t check_stats_args(const moe_shape_t* s, float alpha, float step,
+                                     const float* bias) {
+  if (!(alpha == alpha) || !(step == step)) return fail(MOE_ERR_INVALID_ARG, "alpha / step is NaN");
+  if (bias && s->route != MOE_ROUTE_SIGMOID_BIAS)
+    return fail(MOE_ERR_INVALID_ARG, "the selection bias belongs to the sigmoid router");
+  return MOE_OK;
+}
+
+// The statistics kernels on router logit partials already in the workspace.
+static moe_status_t run_stats(const moe_shape_t* s, const moe_weights_t* w, const float* logits,
+                              const int32_t* counts, float alpha, float step, float* frac,
+                              float* prob, float* aux, float* bias, float* bp,
+                              hipStream_t stream) {
+  HIP_TRY("load_stats",
+          launch_load_stats(logits,
+                            router_splits(s->n_tokens, s->n_experts, s->d_model,
+                                          s->act_dtype == MOE_BF16),
+                            w->logit_offset, s->route == MOE_ROUTE_SIGMOID_BIAS, s->n_tokens,
+                            s->n_experts, s->top_k, counts, alpha, step, bp, frac, prob, aux, bias,
+                            stream));
+  return MOE_OK;
+}
+
 moe_status_t moe_load_stats(const moe_shape_t* s, const void* x, const moe_weights_t* w,
                             const int32_t* counts, float alpha, float step, float* frac,
                             float* prob, float* aux, float* bias, void* ws, size_t ws_bytes,
@@ -539,24 +562,15 @@ moe_status_t moe_load_stats(const moe_shape_t* s, const void* x, const moe_weigh
   if ((st = check_weights(s, w, true, false)) != MOE_OK) return st;
   if (!x || !counts) return fail(MOE_ERR_INVALID_ARG, "x / counts is NULL");
   if ((st = check_aligned({x})) != MOE_OK) return st;
-  if (!(alpha == alpha) || !(step == step)) return fail(MOE_ERR_INVALID_ARG, "alpha / step is NaN");
-  if (bias && s->route != MOE_ROUTE_SIGMOID_BIAS)
-    return fail(MOE_ERR_INVALID_ARG, "the selection bias belongs to the sigmoid router");
+  if ((st = check_stats_args(s, alpha, step, bias)) != MOE_OK) return st;
   if ((st = check_ws(s, ws, ws_bytes)) != MOE_OK) return st;
   const WsLayout L = ws_layout(s);
   char* b = static_cast<char*>(ws);
   float* logits = reinterpret_cast<float*>(b + L.logits);
   HIP_TRY("router_logits", launch_router_logits(x, s->act_dtype == MOE_BF16, w->w_router, logits,
                                                 s->n_tokens, s->d_model, s->n_experts, stream));
-  HIP_TRY("load_stats",
-          launch_load_stats(logits,
-                            router_splits(s->n_tokens, s->n_experts, s->d_model,
-                                          s->act_dtype == MOE_BF16),
-                            w->logit_offset, s->route == MOE_ROUTE_SIGMOID_BIAS, s->n_tokens,
-                            s->n_experts, s->top_k, counts, alpha, step,
-                            reinterpret_cast<float*>(b + L.stats), frac, prob, aux, bias,
-                            stream));
-  return MOE_OK;
+  return run_stats(s, w, logits, counts, alpha, step, frac, prob, aux, bias,
+                   reinterpret_cast<float*>(b + L.stats), stream);
 }
 
 // Arguments of the whole-layer calls other than the workspace (checked on
@@ -640,6 +654,30 @@ moe_status_t moe_layer_forward_capacity(const moe_shape_t* s, const moe_weights_
                                         hipStream_t stream) {
   if (capacity < 0) return fail(MOE_ERR_INVALID_ARG, "capacity is negative");
   return layer_forward(s, w, x, out, r, capacity, GroupLimit(), ws, ws_bytes, stream);
+}
+
+moe_status_t moe_layer_forward_stats(const moe_shape_t* s, const moe_weights_t* w, const void* x,
+                                     void* out, moe_routing_t* r, float alpha, float step,
+                                     float* frac, float* prob, float* aux, float* bias, void* ws,
+                                     size_t ws_bytes, hipStream_t stream) {
+  moe_status_t st = check_layer_args(s, w, x, out, GroupLimit());
+  if (st != MOE_OK || s->n_tokens == 0) return st;
+  if ((st = check_stats_args(s, alpha, step, bias)) != MOE_OK) return st;
+  if ((st = check_ws(s, ws, ws_bytes)) != MOE_OK) return st;
+  if ((st = layer_forward(s, w, x, out, r, -1, GroupLimit(), ws, ws_bytes, stream)) != MOE_OK)
+    return st;
+  const WsLayout L = ws_layout(s);
+  char* b = static_cast<char*>(ws);
+  float* logits = reinterpret_cast<float*>(b + L.logits);
+  // the router left its logit partials in the workspace, except where logits
+  // and selection ran in one kernel (a few tokens, N <= 8)
+  if (router_fused_small(s->n_tokens, s->n_experts))
+    HIP_TRY("router_logits", launch_router_logits(x, s->act_dtype == MOE_BF16, w->w_router,
+                                                  logits, s->n_tokens, s->d_model, s->n_experts,
+                                                  stream));
+  const int32_t* counts = (r && r->counts) ? r->counts : reinterpret_cast<int32_t*>(b + L.counts);
+  return run_stats(s, w, logits, counts, alpha, step, frac, prob, aux, bias,
+                   reinterpret_cast<float*>(b + L.stats), stream);
 }
 
 moe_status_t moe_layer_forward_noalloc(const moe_shape_t* s, const moe_weights_t* w,

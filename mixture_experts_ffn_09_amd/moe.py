@@ -31,7 +31,8 @@ EXPORTS = ["moe_packed_weight_bytes", "moe_pack_weights", "moe_workspace_bytes",
            "moe_router_topk", "moe_permute", "moe_grouped_ffn", "moe_expert_gate_up",
            "moe_expert_down", "moe_combine", "moe_layer_forward", "moe_load_stats",
            "moe_permute_capacity", "moe_layer_forward_capacity", "moe_router_topk_grouped",
-           "moe_layer_forward_grouped", "moe_layer_forward_noalloc", "moe_status_string",
+           "moe_layer_forward_grouped", "moe_layer_forward_noalloc", "moe_layer_forward_stats",
+           "moe_status_string",
            "moe_last_error"]
 
 
@@ -94,11 +95,13 @@ def lib() -> C.CDLL:
                                                 C.POINTER(Routing), P, C.c_size_t, P]
         L.moe_layer_forward_noalloc.argtypes = [S, C.POINTER(Weights), P, P, C.POINTER(Routing),
                                                 P]
+        L.moe_layer_forward_stats.argtypes = [S, C.POINTER(Weights), P, P, C.POINTER(Routing),
+                                              C.c_float, C.c_float, P, P, P, P, P, C.c_size_t, P]
         for f in ("moe_pack_weights", "moe_router_topk", "moe_permute", "moe_grouped_ffn",
                   "moe_expert_gate_up", "moe_expert_down", "moe_combine", "moe_layer_forward",
                   "moe_load_stats", "moe_permute_capacity", "moe_layer_forward_capacity",
                   "moe_router_topk_grouped", "moe_layer_forward_grouped",
-                  "moe_layer_forward_noalloc"):
+                  "moe_layer_forward_noalloc", "moe_layer_forward_stats"):
             getattr(L, f).restype = C.c_int
         L.moe_status_string.argtypes = [C.c_int]
         L.moe_status_string.restype = C.c_char_p
@@ -271,3 +274,17 @@ def moe_layer_forward_noalloc(shape: Shape, weights: Weights, x: torch.Tensor, o
     _check(lib().moe_layer_forward_noalloc(C.byref(shape), C.byref(weights), _ptr(x), _ptr(out),
                                            C.byref(routing) if routing is not None else None,
                                            _stream()))
+
+
+def moe_layer_forward_stats(shape: Shape, weights: Weights, x: torch.Tensor, out: torch.Tensor,
+                            ws: torch.Tensor, routing: Optional[Routing] = None,
+                            alpha: float = 0.01, step: float = 1e-3,
+                            frac: Optional[torch.Tensor] = None,
+                            prob: Optional[torch.Tensor] = None,
+                            aux: Optional[torch.Tensor] = None,
+                            bias: Optional[torch.Tensor] = None):
+    _check(lib().moe_layer_forward_stats(C.byref(shape), C.byref(weights), _ptr(x), _ptr(out),
+                                         C.byref(routing) if routing is not None else None,
+                                         C.c_float(alpha), C.c_float(step), _ptr(frac),
+                                         _ptr(prob), _ptr(aux), _ptr(bias), _ptr(ws),
+                                         ws.numel() * ws.element_size(), _stream()))

@@ -4,6 +4,8 @@ declares, and rejects bad arguments on the host before any HIP call."""
 import ctypes as C
 import os
 import re
+import subprocess
+import sys
 
 import pytest
 
@@ -303,3 +305,24 @@ def test_grouped_argument_checks():
     assert call(64, 1) == moe.MOE_ERR_INVALID_ARG     # 4 experts per group < top_k = 8
     assert _status("moe_layer_forward_grouped", C.byref(s), C.byref(w), FAKE, C.c_void_p(0x2000),
                    7, 2, None, FAKE, ws, None) == moe.MOE_ERR_INVALID_ARG
+
+
+def test_validation_layer_under_host_sanitizers():
+    """The host code of the C ABI (argument checks, workspace sizing and
+    carving in abi.cpp) built with AddressSanitizer and
+    UndefinedBehaviorSanitizer runs every other test of this file without a
+    report (a report aborts the run)."""
+    if os.environ.get("MOE_FFN_LIB"):
+        pytest.skip("already running against another build of the library")
+    from mixture_experts_ffn_09_amd import build as B
+    lib = B.build_host_sanitized()
+    syms = subprocess.run(["nm", "-D", lib], capture_output=True, text=True).stdout
+    assert "__asan_report_load" in syms and "__ubsan_handle" in syms, "not instrumented"
+    env = dict(os.environ, LD_PRELOAD=B.asan_runtime(), MOE_FFN_LIB=lib,
+               ASAN_OPTIONS="detect_leaks=0:halt_on_error=1",
+               UBSAN_OPTIONS="halt_on_error=1:print_stacktrace=1")
+    r = subprocess.run([sys.executable, "-m", "pytest", os.path.abspath(__file__), "-q", "-x",
+                        "-p", "no:cacheprovider", "-k", "not host_sanitizers"],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    assert r.returncode == 0, r.stdout[-3000:] + r.stderr[-3000:]
+    assert " passed" in r.stdout and "failed" not in r.stdout

@@ -135,3 +135,61 @@ def test_bias_step_at_exact_mean_and_determinism():
                           np.array([b0[0], b0[1] - d, b0[2] + d, b0[3]], dtype=np.float32))
     for k in s1:
         assert torch.equal(s1[k], s2[k]), k
+
+
+FUSED = {
+    # logits and selection in one kernel (T <= 64, N <= 8): logits recomputed
+    "fused_router_T16": C[1],
+    # the split-K small-N router (T > 64, N <= 8), the MFMA router (N > 8)
+    # and the LDS-ring router (T >= 1024, N % 128 == 0): partials reused
+    "small_n_T65": H.small_config(C[1], 180, T=65, d_model=512, d_ff=256),
+    "mfma_router_T37": H.small_config(C[3], 181, T=37, d_model=256, d_ff=128),
+    "ring_router_T1024": H.small_config(C[4], 182, T=1024, d_model=256, n_experts=256, d_ff=128,
+                                        w_dtype="bf16"),
+}
+
+
+@pytest.mark.parametrize("name", list(FUSED))
+def test_layer_forward_stats_equals_forward_then_load_stats(name):
+    """moe_layer_forward_stats gives the bits of moe_layer_forward followed by
+    moe_load_stats on the same batch: output, routing, f, P, the balancing
+    term and the bias step (in place on the bias the router selected with)."""
+    from mixture_experts_ffn_09_amd.layer import build_device_layer
+    cfg = FUSED[name]
+    _log(f"[case] forward+stats {name} T={cfg.T} N={cfg.n_experts} k={cfg.top_k}")
+    L = build_device_layer(cfg)
+    x = W.make_x(cfg).to("cuda")
+    s, N = L.shape_for(cfg.T), cfg.n_experts
+    sig = cfg.route == "sigmoid"
+
+    def outs():
+        return {"frac": torch.full((N,), float("nan"), device="cuda"),
+                "prob": torch.full((N,), float("nan"), device="cuda"),
+                "aux": torch.full((1,), float("nan"), device="cuda")}
+
+    # reference: the forward, then the separate statistics call
+    ra, sa = L.routing_buffers(), outs()
+    ba = L.tensors["select_bias"].clone() if sig else None
+    out_a = torch.empty_like(x)
+    ws = L.workspace()
+    moe.moe_layer_forward(s, L.weights, x, out_a, ws, moe.make_routing(**ra))
+    moe.moe_load_stats(s, x, L.weights, ra["counts"], ws, ALPHA, STEP, sa["frac"], sa["prob"],
+                       sa["aux"], ba)
+    # one call, the bias updated in the buffer the router reads
+    rb, sb = L.routing_buffers(), outs()
+    b0 = L.tensors["select_bias"].clone() if sig else None
+    out_b = torch.empty_like(x)
+    ws.fill_(0xFF)
+    moe.moe_layer_forward_stats(s, L.weights, x, out_b, ws, moe.make_routing(**rb), ALPHA, STEP,
+                                sb["frac"], sb["prob"], sb["aux"],
+                                L.tensors["select_bias"] if sig else None)
+    torch.cuda.synchronize()
+    assert torch.equal(out_a.view(torch.int16), out_b.view(torch.int16))
+    for k in ra:
+        assert torch.equal(ra[k], rb[k]), k
+    for k in sa:
+        assert torch.equal(sa[k], sb[k]), k
+    if sig:
+        assert torch.equal(ba, L.tensors["select_bias"])
+        assert not torch.equal(b0, ba)
+    _log(f"  ok: aux {float(sb['aux'][0]):.6g}")

@@ -620,7 +620,8 @@ __device__ __forceinline__ void four_wave_tile(const GemmParams& p, uint8_t* lds
     const u32x4_t val = *reinterpret_cast<const u32x4_t*>(stg + rr * RS + c8 * 2);
     const int r = m0 + wm * WR + rr;
     if (r < rows)
-      *reinterpret_cast<u32x4_t*>(out + (size_t)(row_base + r) * p.n_out + col0 + c8) = val;
+      __builtin_nontemporal_store(
+          val, reinterpret_cast<u32x4_t*>(out + (size_t)(row_base + r) * p.n_out + col0 + c8));
   }
 }
 

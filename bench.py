@@ -142,7 +142,7 @@ def host_description():
 
 
 # tokens of the oracle's timed sample per workload (whole batch when smaller)
-CPU_SAMPLE = {0: 64, 1: 16, 2: 256, 3: 2, 4: 8, 5: 16}
+CPU_SAMPLE = {0: 64, 1: 16, 2: 256, 3: 2, 4: 8, 5: 16, 6: 256}
 CPU_SECONDS = 10.0
 
 

@@ -64,6 +64,25 @@ __device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// E8M0 scale byte -> float 2^(e - 127) (e = 0 is the subnormal 2^-127);
+// e = 255 is the format's NaN
+__device__ __forceinline__ float e8m0_to_f32(uint32_t e) {
+  return __uint_as_float(e == 255u ? 0x7fc00000u : (e ? (e << 23) : 0x00400000u));
+}
+
+// 8 E2M1 codes (one 32-bit word, element 2i in the low nibble of byte i) ->
+// 8 bf16 = one MFMA operand, each times 2^(e - 127) (exact: an E2M1 value
+// times a power of two is a bf16 value)
+__device__ __forceinline__ u32x4_t fp4_word_to_bf16(uint32_t q, uint32_t e) {
+  const float sc = e8m0_to_f32(e);
+  u32x4_t r;
+  r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, sc, 0));
+  r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, sc, 1));
+  r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, sc, 2));
+  r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, sc, 3));
+  return r;
+}
+
 __device__ __forceinline__ floatx4_t mfma16x16x32(const u32x4_t& a, const u32x4_t& b,
                                                   floatx4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),

@@ -60,6 +60,8 @@ struct GemmParams {
   const uint8_t* w_sh;        // packed shared weights
   const float* s;             // FP8 block scales (routed)
   const float* s_sh;          // FP8 block scales (shared)
+  const uint8_t* s4;          // MXFP4 E8M0 scales, packed (routed)
+  const uint8_t* s4_sh;       // MXFP4 E8M0 scales, packed (shared)
   uint16_t* out;
   uint16_t* out_sh;
 };
@@ -399,11 +401,27 @@ __global__ __launch_bounds__(512, 1) void ffn_gemm_kernel(GemmParams p) {
 // step kt + 1 are read during step kt.  A pair buffer is rewritten only after
 // the barrier that follows its last read (2 NPA >= NS + 1).
 
+// MXFP4 weights (FP4): the packed 1 KB blocks hold 16 weight rows x 128
+// inputs (four 32-K steps; lane l's 16 bytes are four words of 8 E2M1 codes,
+// word s the B operand of step s), so the weight ring holds NQ "quads" of
+// four steps each, WBL blocks per quad, plus each block's E8M0 scales of the
+// quad (16 rows x 4 bytes, one byte per 32 inputs, in a 256-byte slot).  Copy step j carries,
+// besides its activation half-pair, one weight block and its scale bytes of
+// quad j / 4 + 1 per wave (block (4 (j % 4) + wave) % WBL, so the four
+// waves and four steps cover all WBL blocks); so every step still issues the
+// same number of copies, quad 0 comes in copy steps -4 .. -1 of the prologue,
+// and quad q is read during steps 4 q - 1 .. 4 q + 2.  A quad buffer is
+// rewritten only after the barrier that follows its last read
+// (4 NQ >= NS + 6).  The operand reads of a step are one code word and one
+// scale byte per block; they are decoded exactly to bf16 (a power of two
+// times an E2M1 value) at the end of the step before, in the shadow of the
+// step's last MFMAs.
+//
 // One tile: WM x (4 / WM) waves, each MBW x NBW blocks of 16 x 16; NS weight
-// steps and NPA activation pairs in LDS.  The tile's weight rows are the
-// WN * NBW 16-row blocks from block nb0 on (gate/up: interleaved pairs, nb0
-// even): a whole 256-row weight tile, or a part of one.
-template <bool GATED, int WM, int MBW, int NBW, int NS, int NPA>
+// steps (bf16) and NPA activation pairs in LDS.  The tile's weight rows are
+// the WN * NBW 16-row blocks from block nb0 on (gate/up: interleaved pairs,
+// nb0 even): a whole 256-row weight tile, or a part of one.
+template <bool GATED, int WM, int MBW, int NBW, int NS, int NPA, bool FP4 = false>
 __device__ __forceinline__ void four_wave_tile(const GemmParams& p, uint8_t* lds, int g,
                                                int row_base, int rows, int m0, int nb0) {
   constexpr int WN = 4 / WM;
@@ -411,16 +429,22 @@ __device__ __forceinline__ void four_wave_tile(const GemmParams& p, uint8_t* lds
   constexpr int AFR = BM / 16;        // activation fragments per step
   constexpr int WBL = WN * NBW;       // weight blocks per step
   static_assert(WBL % 4 == 0 && (!GATED || NBW % 2 == 0), "tile width");
+  static_assert(AFR % 4 == 0, "activation fragments are copied four waves at a time");
   constexpr int NH = GATED ? 2 : 1;
-  constexpr int B_STEP = WBL * 1024;           // one weight step in LDS
+  constexpr int NQ = 3;                        // FP4: quad buffers
+  constexpr int B_STEP = WBL * 1024;           // one weight step (FP4: quad) in LDS
+  constexpr int B_BUFS = FP4 ? NQ : NS;
+  constexpr int S_QUAD = WBL * 256;            // FP4: scales of one quad (64 of 256 bytes used)
+  constexpr int S_RING = FP4 ? NQ * S_QUAD : 0;
   constexpr int A_PAIR = AFR * 2048;           // one activation pair in LDS
-  constexpr int B_PER_WAVE = WBL / 4;          // weight copies per wave per step
+  constexpr int B_PER_WAVE = FP4 ? 2 : WBL / 4;  // weight (FP4: block + scale) copies
   constexpr int A_HALF = AFR / 4;              // activation copies per wave per step
   constexpr int LPS = B_PER_WAVE + A_HALF;     // copies per wave per step
-  constexpr int NRD = MBW + NBW;               // fragment reads per wave per step
+  constexpr int NRD = MBW + (FP4 ? 2 : 1) * NBW;  // operand reads per wave per step
   constexpr int NMF = MBW * NBW;               // MFMAs per wave per step
-  static_assert(NS * B_STEP + NPA * A_PAIR <= FW_LDS, "LDS");
+  static_assert(B_BUFS * B_STEP + S_RING + NPA * A_PAIR <= FW_LDS, "LDS");
   static_assert(NS >= 3 && 2 * NPA >= NS + 1 && (NS - 2) * LPS < 64, "ring");
+  static_assert(!FP4 || 4 * NQ >= NS + 6, "quad ring");
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -428,10 +452,13 @@ __device__ __forceinline__ void four_wave_tile(const GemmParams& p, uint8_t* lds
   const bool shared = g >= p.N;
   uint16_t* out = shared ? p.out_sh : p.out;
   uint8_t* const bring = lds;
-  uint8_t* const aring = lds + NS * B_STEP;
+  uint8_t* const sring = lds + B_BUFS * B_STEP;
+  uint8_t* const aring = sring + S_RING;
 
   const int KT = p.K / 32;
-  const size_t wbytes = (size_t)NH * p.n_out * p.K * 2;
+  const int KQ4 = p.K / 128;                   // FP4: quads (packed K steps)
+  const int KQ = (KT + 15) / 16;               // FP4: 256-byte scale chunks per row block
+  const size_t wbytes = FP4 ? (size_t)NH * p.n_out * p.K / 2 : (size_t)NH * p.n_out * p.K * 2;
   const uint8_t* W = shared ? p.w_sh : p.w + (size_t)g * wbytes;
   const size_t wstep = (size_t)NH * 1024;
 
@@ -440,20 +467,45 @@ __device__ __forceinline__ void four_wave_tile(const GemmParams& p, uint8_t* lds
   // past a resource's size return zero.
   const __amdgpu_buffer_rsrc_t wres =
       __builtin_amdgcn_make_buffer_rsrc((void*)W, 0, (int)(uint32_t)wbytes, BUF_DWORD3);
-  uint32_t boff[B_PER_WAVE];
-  int bdst[B_PER_WAVE];
-#pragma unroll
-  for (int i = 0; i < B_PER_WAVE; ++i) {
-    const int jb = wave * B_PER_WAVE + i;
-    uint32_t off;
+  // weight block jb of the tile: its 16-row block and gate/up half
+  auto block_rh = [&](int jb, int& rb, int& h) {
     if (GATED) {
-      const int pb = nb0 / 2 + (jb >> 1);
-      off = (((uint32_t)pb * KT) * 2 + (jb & 1)) * 1024;
+      rb = nb0 / 2 + (jb >> 1);
+      h = jb & 1;
     } else {
-      off = ((uint32_t)(nb0 + jb) * KT) * 1024;
+      rb = nb0 + jb;
+      h = 0;
     }
-    boff[i] = off + lane * 16;
+  };
+  // bf16: block jb = wave * B_PER_WAVE + i; FP4: the block of sub-step i
+  constexpr int NBO = FP4 ? 4 : B_PER_WAVE;
+  uint32_t boff[NBO];
+  int bdst[NBO];
+#pragma unroll
+  for (int i = 0; i < NBO; ++i) {
+    const int jb = FP4 ? (4 * i + wave) % WBL : wave * B_PER_WAVE + i;
+    int rb, h;
+    block_rh(jb, rb, h);
+    const uint32_t ksteps = FP4 ? (uint32_t)KQ4 : (uint32_t)KT;
+    boff[i] = (((uint32_t)rb * ksteps) * NH + h) * 1024 + lane * 16;
     bdst[i] = jb * 1024;
+  }
+  // FP4 scales: chunk (row block, 4 quads, gate/up) of 16 rows x 16 bytes;
+  // lane i < 16 copies row i's 4 bytes of a quad
+  const uint8_t* S4 = nullptr;
+  uint32_t sbytes = 0;
+  if (FP4) {
+    sbytes = (uint32_t)((size_t)NH * p.n_out * KQ * 16);
+    S4 = shared ? p.s4_sh : p.s4 + (size_t)g * sbytes;
+  }
+  const __amdgpu_buffer_rsrc_t sres =
+      __builtin_amdgcn_make_buffer_rsrc((void*)S4, 0, (int)sbytes, BUF_DWORD3);
+  uint32_t soff[FP4 ? 4 : 1];
+#pragma unroll
+  for (int i = 0; i < (FP4 ? 4 : 0); ++i) {
+    int rb, h;
+    block_rh((4 * i + wave) % WBL, rb, h);
+    soff[i] = (((uint32_t)rb * KQ) * NH + h) * 256 + (lane & 15) * 16;
   }
   const uint16_t* abase = shared ? p.a_sh : p.a;
   const uint32_t abytes = (uint32_t)((size_t)(shared ? rows : (p.perm ? p.T : row_base + rows)) * p.K * 2);
@@ -490,9 +542,25 @@ __device__ __forceinline__ void four_wave_tile(const GemmParams& p, uint8_t* lds
 
   typedef __attribute__((address_space(3))) void* lds_ptr_t;
   // copy number q of step j (weights first, then half (j + 1) % 2 of the
-  // activation pair (j + 1) / 2; j = -1 has only the latter)
+  // activation pair (j + 1) / 2; j = -1 has only the latter in bf16)
   auto copy_one = [&](int q, int j) {
-    if (q < B_PER_WAVE) {
+    if (FP4 && q < B_PER_WAVE) {
+      // block (4 (j % 4) + wave) % WBL of quad j / 4 + 1 (source clamped to
+      // the last quad; the buffer index is not)
+      const int qd = (j >> 2) + 1, sub = j & 3;
+      const int qc = min(qd, KQ4 - 1);
+      if (q == 0) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            wres, (lds_ptr_t)(bring + (qd % NQ) * B_STEP + bdst[sub]), 16, boff[sub],
+            qc * (int)wstep, 0, 0);
+      } else {
+        // every lane copies 4 bytes to slot offset 4 * lane: lanes 16..63 repeat
+        // rows 0..15 into the unused 192 bytes of the block's 256-byte slot
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            sres, (lds_ptr_t)(sring + (qd % NQ) * S_QUAD + (bdst[sub] >> 2)), 4, soff[sub],
+            ((qc >> 2) * NH) * 256 + (qc & 3) * 4, 0, 0);
+      }
+    } else if (q < B_PER_WAVE) {
       const int kl = min(j, KT - 1);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           wres, (lds_ptr_t)(bring + (j % NS) * B_STEP + bdst[q]), 16, boff[q],
@@ -513,15 +581,32 @@ __device__ __forceinline__ void four_wave_tile(const GemmParams& p, uint8_t* lds
 #pragma unroll
     for (int j = 0; j < NBW; ++j) acc[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
   u32x4_t ca[MBW], cb[NBW], na[MBW], nb[NBW];
+  uint32_t rc[FP4 ? NBW : 1], rs[FP4 ? NBW : 1];  // FP4: code words and scale bytes
   // fragment f of step kt: f < MBW are activation blocks, the rest weight blocks
-  // (odd: the parity of kt, known where it is called)
+  // (FP4: NBW code words, then NBW scale bytes) (odd: the parity of kt, known
+  // where it is called)
   auto read_one = [&](u32x4_t (&fa)[MBW], u32x4_t (&fb)[NBW], int f, int kt, bool odd) {
-    if (f < MBW)
+    if (f < MBW) {
       fa[f] = *reinterpret_cast<const u32x4_t*>(aring + ((kt >> 1) % NPA) * A_PAIR +
                                                 (wm * MBW + f) * 2048 + (odd ? a_rd1 : a_rd0));
-    else
+    } else if (FP4) {
+      const int qd = kt >> 2, sub = kt & 3;
+      const int j = (f - MBW) % NBW;
+      if (f < MBW + NBW)
+        rc[FP4 ? j : 0] = *reinterpret_cast<const uint32_t*>(
+            bring + (qd % NQ) * B_STEP + (wn * NBW + j) * 1024 + lane * 16 + sub * 4);
+      else
+        rs[FP4 ? j : 0] = *(sring + (qd % NQ) * S_QUAD + (wn * NBW + j) * 256 + (lane & 15) * 4 +
+                            sub);
+    } else {
       fb[f - MBW] = *reinterpret_cast<const u32x4_t*>(
           bring + (kt % NS) * B_STEP + ((wn * NBW + f - MBW) * 64 + lane) * 16);
+    }
+  };
+  // FP4: the weight operands of the step just read
+  auto decode = [&](u32x4_t (&fb)[NBW]) {
+#pragma unroll
+    for (int j = 0; j < (FP4 ? NBW : 0); ++j) fb[j] = fp4_word_to_bf16(rc[FP4 ? j : 0], rs[FP4 ? j : 0]);
   };
   // Step kt (PAR = kt & 1): wait until the copies of step kt+1 have landed for
   // every wave, then run step kt's MFMAs with two streams interleaved: the
@@ -550,11 +635,25 @@ __device__ __forceinline__ void four_wave_tile(const GemmParams& p, uint8_t* lds
       for (int j = 0; j < NBW; ++j) acc[i][j] = mfma16x16x32(fa[i], fb[j], acc[i][j]);
     stage_pattern<0, LPS, NRD, NMF>();
     __builtin_amdgcn_sched_barrier(0);
+    if (FP4) {
+      decode(gb);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
 
   // K/32 is even (and at least 4) for every accepted shape
+  if (FP4) {
+    // quad 0: weight blocks and scales of copy steps -4 .. -1
 #pragma unroll
-  for (int q = B_PER_WAVE; q < LPS; ++q) copy_one(q, -1);
+    for (int j = -4; j < -1; ++j)
+#pragma unroll
+      for (int q = 0; q < B_PER_WAVE; ++q) copy_one(q, j);
+#pragma unroll
+    for (int q = 0; q < LPS; ++q) copy_one(q, -1);
+  } else {
+#pragma unroll
+    for (int q = B_PER_WAVE; q < LPS; ++q) copy_one(q, -1);
+  }
 #pragma unroll
   for (int j = 0; j < NS - 1; ++j)
 #pragma unroll
@@ -563,6 +662,7 @@ __device__ __forceinline__ void four_wave_tile(const GemmParams& p, uint8_t* lds
   barrier_no_fence();
 #pragma unroll
   for (int f = 0; f < NRD; ++f) read_one(ca, cb, f, 0, false);
+  if (FP4) decode(cb);
 
   for (int kt = 0; kt < KT; kt += 2) {
     stage(std::integral_constant<int, 0>{}, ca, cb, na, nb, kt);
@@ -655,7 +755,7 @@ __device__ __forceinline__ int xcd_unit(int total, int& nsub, int& sub) {
   return x * per + whole + j / ns;
 }
 
-template <bool GATED>
+template <bool GATED, bool FP4>
 __global__ __launch_bounds__(256, 1) void ffn_gemm_big_kernel(GemmParams p) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds[FW_LDS];
   const int ngroups = p.g1 - p.g0;
@@ -689,28 +789,28 @@ __global__ __launch_bounds__(256, 1) void ffn_gemm_big_kernel(GemmParams p) {
     if (nsub == 4) {
       const int nb = nb0 + sub * 4;
       if (left > 128)
-        four_wave_tile<GATED, 2, 8, 2, 5, 3>(p, lds, g, row_base, rows, m0, nb);
+        four_wave_tile<GATED, 2, 8, 2, 5, 3, FP4>(p, lds, g, row_base, rows, m0, nb);
       else if (left > 64)
-        four_wave_tile<GATED, 2, 4, 2, 6, 4>(p, lds, g, row_base, rows, m0, nb);
+        four_wave_tile<GATED, 2, 4, 2, 6, 4, FP4>(p, lds, g, row_base, rows, m0, nb);
       else
-        four_wave_tile<GATED, 2, 2, 2, 6, 4>(p, lds, g, row_base, rows, m0, nb);
+        four_wave_tile<GATED, 2, 2, 2, 6, 4, FP4>(p, lds, g, row_base, rows, m0, nb);
     } else {
       const int nb = nb0 + sub * 8;
       if (left > 128)
-        four_wave_tile<GATED, 2, 8, 4, 5, 3>(p, lds, g, row_base, rows, m0, nb);
+        four_wave_tile<GATED, 2, 8, 4, 5, 3, FP4>(p, lds, g, row_base, rows, m0, nb);
       else if (left > 64)
-        four_wave_tile<GATED, 1, 8, 2, 6, 4>(p, lds, g, row_base, rows, m0, nb);
+        four_wave_tile<GATED, 1, 8, 2, 6, 4, FP4>(p, lds, g, row_base, rows, m0, nb);
       else
-        four_wave_tile<GATED, 1, 4, 2, 6, 4>(p, lds, g, row_base, rows, m0, nb);
+        four_wave_tile<GATED, 1, 4, 2, 6, 4, FP4>(p, lds, g, row_base, rows, m0, nb);
     }
     return;
   }
   if (left > 128)
-    four_wave_tile<GATED, 2, 8, 8, 4, 3>(p, lds, g, row_base, rows, m0, nb0);
+    four_wave_tile<GATED, 2, 8, 8, 4, 3, FP4>(p, lds, g, row_base, rows, m0, nb0);
   else if (left > 64)
-    four_wave_tile<GATED, 1, 8, 4, 5, 3>(p, lds, g, row_base, rows, m0, nb0);
+    four_wave_tile<GATED, 1, 8, 4, 5, 3, FP4>(p, lds, g, row_base, rows, m0, nb0);
   else
-    four_wave_tile<GATED, 1, 4, 4, 6, 4>(p, lds, g, row_base, rows, m0, nb0);
+    four_wave_tile<GATED, 1, 4, 4, 6, 4, FP4>(p, lds, g, row_base, rows, m0, nb0);
 }
 
 template <int BM, bool FP8>
@@ -725,15 +825,22 @@ void launch_gemm_kernel(bool gated, long long nwg, const GemmParams& p, hipStrea
 
 bool gemm_shape_ok(int d, int d_ff) { return d % 256 == 0 && d_ff % 128 == 0; }
 
+// The four-wave kernel addresses operands through 32-bit buffer offsets.
+bool gemm_four_wave_ok(const FfnArgs& a) {
+  const long long lim = 0x7fffffffLL;
+  return !a.fp8 && (long long)a.T * a.d * 2 <= lim && (long long)a.T * a.k * a.d_ff * 2 <= lim &&
+         4LL * a.d * a.d_ff <= lim;
+}
+
 hipError_t launch_ffn_gemm(const FfnArgs& a, int pass, int g0, int g1, int max_rows,
                            int32_t* sched, hipStream_t st) {
   if (g1 <= g0) return hipSuccess;
-  // bf16 weights take the four-wave kernel (tiles of 64..256 rows), which
-  // addresses operands through 32-bit buffer offsets; FP8 weights, or shapes
-  // past those offsets, take the eight-wave kernel with 128-row tiles
-  const long long lim = 0x7fffffffLL;
-  const bool four_wave = !a.fp8 && (long long)a.T * a.d * 2 <= lim &&
-                         (long long)a.T * a.k * a.d_ff * 2 <= lim && 4LL * a.d * a.d_ff <= lim;
+  // bf16 and MXFP4 weights take the four-wave kernel (tiles of 64..256 rows);
+  // FP8 weights, or bf16 shapes past 32-bit operand offsets, take the
+  // eight-wave kernel with 128-row tiles (MXFP4 there is the caller's error:
+  // it runs through the streaming kernel instead)
+  const bool four_wave = gemm_four_wave_ok(a);
+  if (a.mxfp4 && !four_wave) return hipErrorInvalidValue;
   const int bm = four_wave ? 256 : 128;
   for (int ps = 1; ps <= 2; ++ps) {
     if (!(pass & ps)) continue;
@@ -753,8 +860,13 @@ hipError_t launch_ffn_gemm(const FfnArgs& a, int pass, int g0, int g1, int max_r
     p.NT = gated ? (2 * a.d_ff) / GM_BN : a.d / GM_BN;
     p.w = static_cast<const uint8_t*>(gated ? a.w13 : a.w2);
     p.w_sh = static_cast<const uint8_t*>(gated ? a.w13_sh : a.w2_sh);
-    p.s = static_cast<const float*>(gated ? a.s13 : a.s2);
-    p.s_sh = static_cast<const float*>(gated ? a.s13_sh : a.s2_sh);
+    if (a.mxfp4) {
+      p.s4 = static_cast<const uint8_t*>(gated ? a.s13 : a.s2);
+      p.s4_sh = static_cast<const uint8_t*>(gated ? a.s13_sh : a.s2_sh);
+    } else {
+      p.s = static_cast<const float*>(gated ? a.s13 : a.s2);
+      p.s_sh = static_cast<const float*>(gated ? a.s13_sh : a.s2_sh);
+    }
     p.out = gated ? a.H : a.Y;
     p.out_sh = gated ? a.H_sh : a.Y_sh;
     tile_schedule_kernel<<<1, 1024, 0, st>>>(p, bm, const_cast<int32_t*>(p.tiles));
@@ -769,10 +881,16 @@ hipError_t launch_ffn_gemm(const FfnArgs& a, int pass, int g0, int g1, int max_r
     else if (four_wave) {
       // room for the parts of the last round's tiles (xcd_unit)
       const unsigned nwg_fw = (unsigned)(nwg + (long long)NXCD * XCD_CUS);
-      if (gated)
-        ffn_gemm_big_kernel<true><<<dim3(nwg_fw), 256, 0, st>>>(p);
-      else
-        ffn_gemm_big_kernel<false><<<dim3(nwg_fw), 256, 0, st>>>(p);
+      if (a.mxfp4) {
+        if (gated)
+          ffn_gemm_big_kernel<true, true><<<dim3(nwg_fw), 256, 0, st>>>(p);
+        else
+          ffn_gemm_big_kernel<false, true><<<dim3(nwg_fw), 256, 0, st>>>(p);
+      } else if (gated) {
+        ffn_gemm_big_kernel<true, false><<<dim3(nwg_fw), 256, 0, st>>>(p);
+      } else {
+        ffn_gemm_big_kernel<false, false><<<dim3(nwg_fw), 256, 0, st>>>(p);
+      }
     } else
       launch_gemm_kernel<128, false>(gated, nwg, p, st);
     e = hipGetLastError();

@@ -1,7 +1,7 @@
 // Grouped expert FFN for bfloat16 activations with bfloat16, FP8 (OCP E4M3,
 // one float32 scale per 128x128 block) or MXFP4 (E2M1 codes, one E8M0 scale
 // per 32 inputs) weights: the weight-streaming form, for few rows per expert
-// (decode; MXFP4 at every batch size).
+// (decode).
 //
 // An expert is a complete SwiGLU FFN with its own three matrices ("Mixture of
 // Experts for LLM Inference", "The MoE change is surprisingly local";
@@ -66,24 +66,6 @@ __device__ __forceinline__ void fp8_block_to_bf16(const u32x4_t& q, u32x4_t& lo,
 
 // Weight formats of the streaming kernel
 constexpr int WF_BF16 = 0, WF_FP8 = 1, WF_MXFP4 = 2;
-
-// E8M0 scale byte -> float 2^(e - 127) (e = 0 is the subnormal 2^-127);
-// e = 255 is the format's NaN
-__device__ __forceinline__ float e8m0_to_f32(uint32_t e) {
-  return __uint_as_float(e == 255u ? 0x7fc00000u : (e ? (e << 23) : 0x00400000u));
-}
-
-// 8 E2M1 codes (one 32-bit word, element 2i in the low nibble of byte i) ->
-// 8 bf16 = one MFMA operand, each times 2^(e - 127)
-__device__ __forceinline__ u32x4_t fp4_word_to_bf16(uint32_t q, uint32_t e) {
-  const float sc = e8m0_to_f32(e);
-  u32x4_t r;
-  r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, sc, 0));
-  r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, sc, 1));
-  r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, sc, 2));
-  r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, sc, 3));
-  return r;
-}
 
 // GATED: pass 1 (gate+up, SwiGLU) else pass 2 (down).  One wave owns NP
 // consecutive 16-row output blocks and walks K with a ring of D K-steps of
@@ -579,9 +561,9 @@ hipError_t launch_ffn_stream(const FfnArgs& a, int pass, int g0, int g1, int row
 }
 
 hipError_t launch_ffn_lowp(const FfnArgs& a, int pass, hipStream_t st) {
-  // MXFP4 weights run through the streaming kernel at every size (the
-  // tiled GEMM has no E2M1 operand path)
-  const bool gemm_ok = gemm_shape_ok(a.d, a.d_ff) && !a.mxfp4;
+  // MXFP4 weights take the tiled GEMM only in its four-wave form (the one
+  // with an E2M1 operand path)
+  const bool gemm_ok = gemm_shape_ok(a.d, a.d_ff) && (!a.mxfp4 || gemm_four_wave_ok(a));
   const int avg = (int)(((long long)a.T * a.k + a.N - 1) / a.N);  // rows per routed expert
   const bool routed_gemm = gemm_ok && avg >= 64;
   // the shared expert joins a routed streaming launch up to a few hundred

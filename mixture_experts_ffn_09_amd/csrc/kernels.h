@@ -89,6 +89,8 @@ hipError_t launch_ffn_stream(const FfnArgs& a, int pass, int g0, int g1, int row
 // Tiled GEMM over groups [g0, g1) with row tile bm; max_rows bounds the total
 // rows of those groups.
 bool gemm_shape_ok(int d, int d_ff);
+// the four-wave GEMM (bf16 and MXFP4 weights) fits this call's sizes
+bool gemm_four_wave_ok(const FfnArgs& a);
 hipError_t launch_ffn_gemm(const FfnArgs& a, int pass, int g0, int g1, int max_rows,
                            int32_t* sched, hipStream_t st);
 

@@ -20,6 +20,8 @@ expert):
                        1 shared expert
   4 dsv3-decode-fp8    T=256  d=7168 N=256 k=8 d_ff=2048  fp8 weights, sigmoid
                        + bias, 1 shared expert, Zipf-skewed router offsets
+  5, 6 the Mixtral decode and prefill shapes with MXFP4 expert weights (E2M1
+                       codes, one E8M0 scale per 32 inputs)
 
 Distributions: x ~ N(0, 1); router W ~ N(0, 1/d) in float32; W_gate, W_up ~
 N(0, 1/d) and W_down ~ N(0, 1/d_ff) (fan-in scaling); selection bias ~
@@ -74,8 +76,10 @@ CONFIGS = [
     MoEConfig(2, "mixtral-prefill", 8192, 4096, 8, 2, 14336, "softmax", 0, "bf16", "bf16", False),
     MoEConfig(3, "dsv3-prefill", 4096, 7168, 256, 8, 2048, "sigmoid", 1, "bf16", "bf16", True),
     MoEConfig(4, "dsv3-decode-fp8", 256, 7168, 256, 8, 2048, "sigmoid", 1, "bf16", "fp8", True, 0.25),
-    # the Mixtral decode shape with its experts in MXFP4
+    # the Mixtral decode and prefill shapes with their experts in MXFP4
     MoEConfig(5, "mixtral-decode-mxfp4", 16, 4096, 8, 2, 14336, "softmax", 0, "bf16", "mxfp4",
+              False),
+    MoEConfig(6, "mixtral-prefill-mxfp4", 8192, 4096, 8, 2, 14336, "softmax", 0, "bf16", "mxfp4",
               False),
 ]
 
@@ -113,7 +117,8 @@ def quantize_fp8_block(w: torch.Tensor):
 
 
 MX_BLOCK = 32
-_FP4_GRID = torch.tensor([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+# midpoints between consecutive E2M1 magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6
+_FP4_MID = torch.tensor([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
 
 
 def quantize_mxfp4(w: torch.Tensor):
@@ -129,10 +134,10 @@ def quantize_mxfp4(w: torch.Tensor):
     ex = torch.where(amax > 0, torch.floor(torch.log2(amax)) - 2, torch.full_like(amax, -127.0))
     ex = ex.clamp(-127, 127)
     v = (b / torch.exp2(ex)[..., None]).clamp(-6.0, 6.0)
-    diff = (v.abs()[..., None] - _FP4_GRID).abs()
-    best = diff == diff.min(dim=-1, keepdim=True).values
-    pref = best.to(torch.int32) * (2 - torch.arange(8) % 2)  # ties: even code
-    mag = pref.argmax(dim=-1).to(torch.uint8)
+    a = v.abs()
+    mag = torch.bucketize(a, _FP4_MID)  # midpoints below |v| (a tie counts as above)
+    tie = (mag < 7) & (a == _FP4_MID[mag.clamp(max=6)]) & (mag % 2 == 1)
+    mag = (mag + tie.to(mag.dtype)).to(torch.uint8)  # a tie goes to the even code
     codes = (mag | torch.where(v < 0, 8, 0).to(torch.uint8)).reshape(R, C)
     packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).contiguous()
     return packed, (ex + 127).to(torch.uint8).contiguous()

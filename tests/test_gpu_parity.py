@@ -94,6 +94,19 @@ SMALL = {
                                            w_dtype="mxfp4"),
     "mxfp4_many_rows": H.small_config(C[2], 152, T=300, d_model=256, d_ff=256, n_experts=4,
                                       w_dtype="mxfp4"),
+    # MXFP4 weights through the four-wave GEMM (E2M1 codes and E8M0 scales
+    # in LDS, decoded to bf16 on the way to the MFMAs): 256-row tiles with a
+    # ragged last tile and last rounds cut into 2 or 4 parts; routed + shared
+    # in one launch with the sigmoid router; whole tiles on the gate/up pass;
+    # K = 768 and 384 (the last 512-input scale chunk partly used)
+    "mxfp4_gemm_routed": H.small_config(C[6], 190, T=1200, d_model=512, d_ff=1024,
+                                        n_experts=4),
+    "mxfp4_gemm_shared": H.small_config(C[3], 191, T=800, d_model=512, d_ff=512, n_experts=16,
+                                        top_k=2, w_dtype="mxfp4"),
+    "mxfp4_gemm_parts": H.small_config(C[6], 192, T=512, d_model=2048, n_experts=4, d_ff=1024),
+    "mxfp4_gemm_whole": H.small_config(C[6], 194, T=2048, d_model=1024, d_ff=2048,
+                                       n_experts=4),
+    "mxfp4_gemm_k768": H.small_config(C[6], 193, T=600, d_model=768, d_ff=384, n_experts=4),
     # odd K-step counts (3 on gate/up, 5 on down: a ring depth of 1) with a
     # hot expert of more than 32 rows in a 16-row launch (its 64-row passes)
     "stream_odd_ksteps_hot": H.small_config(C[1], 123, T=64, d_model=96, d_ff=160,
@@ -153,7 +166,7 @@ def _worst(got, ref, tol):
     return float((np.abs(got - ref) / (tol * (1.0 + np.abs(ref)))).max())
 
 
-@pytest.mark.parametrize("ci", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("ci", [1, 2, 3, 4, 5, 6])
 def test_layer_full_size(ci):
     """Each full-size workload on every token: routing, gates and the
     permutation against the oracle, the layer output of every token, and the

@@ -131,6 +131,18 @@ __device__ __forceinline__ void group_pattern() {
   }
 }
 
+// NB groups of V VALU instructions (an operand decode), each followed by its
+// share of M MFMAs.
+template <int Q, int NB, int V, int M>
+__device__ __forceinline__ void decode_pattern() {
+  if constexpr (Q < NB) {
+    constexpr int m = (Q + 1) * M / NB - Q * M / NB;
+    __builtin_amdgcn_sched_group_barrier(0x002, V, 0);
+    if constexpr (m > 0) __builtin_amdgcn_sched_group_barrier(0x008, m, 0);
+    decode_pattern<Q + 1, NB, V, M>();
+  }
+}
+
 // Scheduling pattern of one step: group q of LPS issues one copy, then its
 // share of the NRD fragment reads interleaved with its share of the NMF MFMAs.
 template <int Q, int LPS, int NRD, int NMF>

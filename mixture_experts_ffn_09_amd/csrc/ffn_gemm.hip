@@ -633,11 +633,23 @@ __device__ __forceinline__ void four_wave_tile(const GemmParams& p, uint8_t* lds
     for (int i = 0; i < MBW; ++i)
 #pragma unroll
       for (int j = 0; j < NBW; ++j) acc[i][j] = mfma16x16x32(fa[i], fb[j], acc[i][j]);
-    stage_pattern<0, LPS, NRD, NMF>();
-    __builtin_amdgcn_sched_barrier(0);
-    if (FP4) {
+    if constexpr (FP4 && GATED) {
+      // copies and operand reads between the first half of the MFMAs, the
+      // decode of the next step's weight operands (4 conversions and the
+      // scale per block) between the second half
       decode(gb);
+      stage_pattern<0, LPS, NRD, NMF / 2>();
+      decode_pattern<0, NBW, 8, NMF - NMF / 2>();
       __builtin_amdgcn_sched_barrier(0);
+    } else {
+      stage_pattern<0, LPS, NRD, NMF>();
+      __builtin_amdgcn_sched_barrier(0);
+      if (FP4) {
+        // the down pass decodes after the MFMAs (interleaving them would
+        // spill registers there)
+        decode(gb);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   };
 

@@ -149,8 +149,8 @@ def to_np(t: torch.Tensor) -> np.ndarray:
 
 
 def host_threads() -> int:
-    """Worker threads for host-side test work (the GPU machine's CPU share is 16
-    whatever os.cpu_count() shows)."""
+    """Worker threads for host-side test work: the affinity set, at most 16
+    (the host share of one GPU, whatever os.cpu_count() shows)."""
     return max(1, min(16, len(os.sched_getaffinity(0))))
 
 

@@ -23,8 +23,8 @@ namespace {
 
 __global__ __launch_bounds__(256) void pack_kernel(const uint8_t* __restrict__ a,
                                                    const uint8_t* __restrict__ b,
-                                                   uint8_t* __restrict__ dst, int n_mats,
-                                                   int rows, int cols, int esize, int nh,
+                                                   uint8_t* __restrict__ dst, int rows,
+                                                   int cols, int esize, int nh,
                                                    size_t total_chunks) {
   const size_t c = (size_t)blockIdx.x * 256 + threadIdx.x;
   if (c >= total_chunks) return;
@@ -133,7 +133,7 @@ hipError_t launch_pack(const void* src_a, const void* src_b, void* dst, int n_ma
   const size_t grid = (chunks + 255) / 256;
   pack_kernel<<<dim3((unsigned)grid), 256, 0, st>>>(static_cast<const uint8_t*>(src_a),
                                                     static_cast<const uint8_t*>(src_b),
-                                                    static_cast<uint8_t*>(dst), n_mats, rows,
-                                                    cols, esize, nh, chunks);
+                                                    static_cast<uint8_t*>(dst), rows, cols,
+                                                    esize, nh, chunks);
   return hipGetLastError();
 }

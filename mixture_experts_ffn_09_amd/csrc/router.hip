@@ -634,7 +634,7 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float* __restric
 template <bool BF16>
 __global__ __launch_bounds__(256) void router_fused_small_kernel(
     const void* __restrict__ xv, const float* __restrict__ w, const float* __restrict__ offset,
-    const float* __restrict__ bias, int sigmoid, int T, int d, int N, int k, int gsize,
+    const float* __restrict__ bias, int sigmoid, int d, int N, int k, int gsize,
     int max_groups, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w) {
   __shared__ float wsum[4][8];
   __shared__ float gscr[64];
@@ -802,11 +802,11 @@ hipError_t launch_router_fused_small(const void* x, bool act_bf16, const float* 
                                      int32_t* topk_idx, float* topk_w, hipStream_t st) {
   if (act_bf16)
     router_fused_small_kernel<true><<<T, 256, 0, st>>>(x, w_router, offset, select_bias, sigmoid,
-                                                       T, d, N, k, gsize, max_groups, topk_idx,
+                                                       d, N, k, gsize, max_groups, topk_idx,
                                                        topk_w);
   else
     router_fused_small_kernel<false><<<T, 256, 0, st>>>(x, w_router, offset, select_bias,
-                                                        sigmoid, T, d, N, k, gsize, max_groups,
+                                                        sigmoid, d, N, k, gsize, max_groups,
                                                         topk_idx, topk_w);
   return hipGetLastError();
 }

@@ -13,7 +13,6 @@ import itertools
 import os
 from concurrent.futures import ThreadPoolExecutor
 from dataclasses import replace
-from functools import lru_cache
 
 import numpy as np
 import torch

@@ -1,0 +1,116 @@
+"""bench.py's host logic without a GPU: the algorithmic byte and flop
+accounting behind every roofline figure, the roofline classification, the
+guard on the committed traffic counters, and the one-GPU refusal."""
+
+import hashlib
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+import bench
+from mixture_experts_ffn_09_amd import moe, workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _shape(cfg):
+    return moe.make_shape(cfg.T, cfg.d_model, cfg.n_experts, cfg.top_k, cfg.d_ff, cfg.n_shared,
+                          cfg.route, cfg.act_dtype, cfg.w_dtype)
+
+
+@pytest.mark.parametrize("i", range(len(W.CONFIGS)))
+def test_weight_bytes_are_what_the_library_stores(i):
+    """The weight part of each expert pass's algorithmic bytes equals the
+    bytes the library packs per expert (moe_packed_weight_bytes), times the
+    touched experts plus the shared one; scales included."""
+    if not os.path.exists(moe.LIB_PATH):
+        pytest.fail("libmoe_ffn.so is not built (python -m mixture_experts_ffn_09_amd.build)")
+    cfg = W.CONFIGS[i]
+    s = _shape(cfg)
+    touched = min(cfg.n_experts, 5)
+    st, layer = bench.accounting(cfg, touched)
+    mats = touched + cfg.n_shared
+    w13, w2 = moe.moe_packed_weight_bytes(s, 0, 1), moe.moe_packed_weight_bytes(s, 1, 1)
+    assert w13 > 0 and w2 > 0
+    if cfg.w_dtype == "mxfp4":
+        s13, s2 = moe.moe_packed_weight_bytes(s, 2, 1), moe.moe_packed_weight_bytes(s, 3, 1)
+    elif cfg.w_dtype == "fp8":  # one float32 per 128 x 128 block, as the layer uploads them
+        s13 = 2 * (cfg.d_ff // 128) * (cfg.d_model // 128) * 4
+        s2 = (cfg.d_model // 128) * (cfg.d_ff // 128) * 4
+    else:
+        s13 = s2 = 0
+    ab = 4 if cfg.act_dtype == "f32" else 2
+    rows = cfg.T * cfg.top_k + cfg.n_shared * cfg.T
+    acts_gu = rows * cfg.d_model * ab + rows * cfg.d_ff * ab   # X in, H out
+    acts_dn = rows * cfg.d_ff * ab + rows * cfg.d_model * ab   # H in, Y out
+    assert st["gate_up"]["bytes"] - acts_gu == mats * (w13 + s13)
+    assert st["down"]["bytes"] - acts_dn == mats * (w2 + s2)
+    # the layer reads every weight byte once and x / writes out once
+    assert layer["bytes"] == (mats * (w13 + s13 + w2 + s2) + cfg.d_model * cfg.n_experts * 4
+                              + 2 * cfg.T * cfg.d_model * ab)
+
+
+@pytest.mark.parametrize("i", range(len(W.CONFIGS)))
+def test_flop_counts(i):
+    """Gate/up multiplies by two d x d_ff matrices, down by one: twice the
+    flops; the layer total is the sum of the stages."""
+    cfg = W.CONFIGS[i]
+    st, layer = bench.accounting(cfg, cfg.n_experts)
+    assert st["gate_up"]["flops"] == 2 * st["down"]["flops"]
+    rows = cfg.T * cfg.top_k + cfg.n_shared * cfg.T
+    assert st["down"]["flops"] == 2 * rows * cfg.d_ff * cfg.d_model
+    assert layer["flops"] == sum(v["flops"] for v in st.values())
+
+
+def test_roofline_picks_the_bound():
+    dec, pre, f32 = W.CONFIGS[1], W.CONFIGS[2], W.CONFIGS[0]
+    st_d, _ = bench.accounting(dec, dec.n_experts)
+    st_p, _ = bench.accounting(pre, pre.n_experts)
+    r = bench.roofline_for(dec, st_d["gate_up"], 0.3)
+    assert r["bound"] == "hbm" and r["unit"] == "GB/s" and r["peak"] == bench.PEAK_HBM_GBS
+    assert r["achieved"] == pytest.approx(st_d["gate_up"]["bytes"] / 0.3e-3 / 1e9, abs=0.05)
+    assert r["frac"] == pytest.approx(r["achieved"] / r["peak"], abs=1e-4)
+    r = bench.roofline_for(pre, st_p["gate_up"], 3.0)
+    assert r["bound"] == "mfma" and r["unit"] == "TFLOP/s" and r["peak"] == bench.PEAK_BF16_TFLOPS
+    assert r["achieved"] == pytest.approx(st_p["gate_up"]["flops"] / 3.0e-3 / 1e12, abs=0.05)
+    # float32 weights: plain ALU arithmetic above the ridge
+    r = bench.roofline_for(f32, {"flops": 10 ** 12, "bytes": 10 ** 6}, 1.0)
+    assert r["bound"] == "alu" and r["peak"] == bench.PEAK_FP32_VALU_TFLOPS
+
+
+def test_traffic_only_while_the_profiled_source_is_unchanged(tmp_path, monkeypatch):
+    src = tmp_path / "kernel.hip"
+    src.write_text("// kernel v1\n")
+    (tmp_path / "profiles").mkdir()
+    rec = {"traffic_bytes_per_launch": 12345, "source": "kernel.hip",
+           "source_sha256": hashlib.sha256(src.read_bytes()).hexdigest()}
+    (tmp_path / "profiles" / "traffic_some_workload.json").write_text(json.dumps(rec))
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    assert bench.measured_traffic("some-workload") == 12345
+    assert bench.measured_traffic("other-workload") is None
+    src.write_text("// kernel v2\n")
+    assert bench.measured_traffic("some-workload") is None
+
+
+def test_committed_traffic_files_name_existing_sources():
+    d = os.path.join(ROOT, "profiles")
+    files = [f for f in os.listdir(d) if f.startswith("traffic_") and f.endswith(".json")]
+    assert files
+    names = {c.name.replace("-", "_") for c in W.CONFIGS}
+    for f in files:
+        rec = json.load(open(os.path.join(d, f)))
+        assert f[len("traffic_"):-len(".json")] in names
+        assert os.path.exists(os.path.join(ROOT, rec["source"]))
+        assert rec["traffic_bytes_per_launch"] == rec["fetched_bytes"] + rec["written_bytes"]
+
+
+@pytest.mark.parametrize("args,env", [(["--gpus", "2"], {}), ([], {"WORLD_SIZE": "4"})])
+def test_more_than_one_gpu_is_refused(args, env):
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *args],
+                       env={**os.environ, **env}, capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU only" in r.stderr
+    assert r.stdout == ""

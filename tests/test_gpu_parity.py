@@ -107,6 +107,10 @@ SMALL = {
     "mxfp4_gemm_whole": H.small_config(C[6], 194, T=2048, d_model=1024, d_ff=2048,
                                        n_experts=4),
     "mxfp4_gemm_k768": H.small_config(C[6], 193, T=600, d_model=768, d_ff=384, n_experts=4),
+    # skewed routing: MXFP4 groups of every row class, full-height tiles
+    # (1 x 4 waves of 256 x 64) cut short by a group's end, on both passes
+    "mxfp4_gemm_skew": H.small_config(C[6], 195, T=1500, d_model=512, d_ff=1024, n_experts=8,
+                                      zipf_c=0.3),
     # odd K-step counts (3 on gate/up, 5 on down: a ring depth of 1) with a
     # hot expert of more than 32 rows in a 16-row launch (its 64-row passes)
     "stream_odd_ksteps_hot": H.small_config(C[1], 123, T=64, d_model=96, d_ff=160,

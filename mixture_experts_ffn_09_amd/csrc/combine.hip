@@ -35,10 +35,12 @@ __global__ __launch_bounds__(256) void combine_bf16_kernel(const uint16_t* __res
       r[u] = in ? inv[(size_t)t * k + i0 + u] : -1;
       g[u] = in ? gw[(size_t)t * k + i0 + u] : 0.f;
     }
+    // expert output rows are read once: non-temporal loads
     u32x4_t v[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u)
-      v[u] = r[u] >= 0 ? *reinterpret_cast<const u32x4_t*>(y + (size_t)r[u] * d + c0)
+      v[u] = r[u] >= 0 ? __builtin_nontemporal_load(
+                             reinterpret_cast<const u32x4_t*>(y + (size_t)r[u] * d + c0))
                        : u32x4_t{0, 0, 0, 0};
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
@@ -51,7 +53,8 @@ __global__ __launch_bounds__(256) void combine_bf16_kernel(const uint16_t* __res
     }
   }
   if (ys) {
-    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(ys + (size_t)t * d + c0);
+    const u32x4_t v =
+        __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(ys + (size_t)t * d + c0));
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       acc[2 * j] += bf16_to_f32(v[j] & 0xffffu);

@@ -17,11 +17,15 @@ namespace {
 // Logits: float32 dot products, split over K into S partial sums
 // partial[s][t][e] (summed in a fixed order by the top-k kernel, so the
 // result does not depend on scheduling).  Shapes:
-//  * N <= 8: one thread per token owning all experts; the W slice is staged
-//    in LDS and read as a broadcast (router_logits_small_n).  With T <= 64
+//  * N <= 8 (float32 x, or bfloat16 x below 1024 tokens): one thread per
+//    token owning all experts; the W slice is staged in LDS and read as a
+//    broadcast (router_logits_small_n).  With T <= 64
 //    the layer instead runs logits and selection in one kernel
 //    (router_fused_small_kernel, below the top-k kernel).
-//  * N > 8, bfloat16 x: MFMA on three bfloat16 planes of W
+//  * N > 8, or N <= 8 from 1024 tokens, bfloat16 x: MFMA on three bfloat16
+//    planes of W (at large batches the one-token-per-lane form reads 64 rows
+//    per load instruction, and the copy path, not the arithmetic, set its
+//    time: 45 us for the 8192 x 4096 mixtral-prefill batch)
 //    (router_logits_mfma; router_logits_ring for large batches).
 //  * N > 8, float32 x: 32 tokens x 64 experts per workgroup, each thread
 //    2 x 4, K staged through LDS 32 at a time (router_logits_tiled).
@@ -701,16 +705,19 @@ __global__ __launch_bounds__(256) void router_fused_small_kernel(
 
 }  // namespace
 
-// Router kernel choice: N <= 8 -> small_n; bf16 x -> MFMA (the LDS-ring form
-// for large batches); else tiled fp32.
+// Router kernel choice: bf16 x with N > 8 or T >= 1024 -> MFMA (the LDS-ring
+// form for large batches with N % 128 == 0); else N <= 8 -> small_n; else
+// tiled fp32.
+static bool router_mfma(int T, int N, bool act_bf16) { return act_bf16 && (N > 8 || T >= 1024); }
+
 static bool router_ring(int T, int N, int d, bool act_bf16) {
   return act_bf16 && N % RR_TN == 0 && d % 32 == 0 && T >= 1024 &&
          (long long)T * d * 2 <= 0x7fffffffLL;
 }
 
 static int router_tiles(int T, int N, bool mfma) {
-  if (N <= 8) return ceil_div(T, RS_TM);
   if (mfma) return ceil_div(T, RM_TM) * ceil_div(N, RM_TN);
+  if (N <= 8) return ceil_div(T, RS_TM);
   return ceil_div(T, RL_TM) * ceil_div(N, RL_TN);
 }
 
@@ -726,7 +733,7 @@ int router_splits(int T, int N, int d, bool act_bf16) {
     const int KC = ceil_div(ceil_div(d, S), 64) * 64;
     return ceil_div(d, KC);
   }
-  const int tiles = router_tiles(T, N, act_bf16 && N > 8);
+  const int tiles = router_tiles(T, N, router_mfma(T, N, act_bf16));
   // enough workgroups to fill the chip, but at least 256 of K per split
   int S = 1024 / tiles;
   S = S < 1 ? 1 : S;
@@ -745,7 +752,7 @@ static size_t align256_sz(size_t v) { return (v + 255) / 256 * 256; }
 
 size_t router_scratch_bytes(int T, int N, int d, bool act_bf16) {
   const size_t logits = (size_t)router_splits(T, N, d, act_bf16) * T * N * 4;
-  return N > 8 && act_bf16 ? align256_sz(logits) + router_plane_bytes(N, d) : logits;
+  return router_mfma(T, N, act_bf16) ? align256_sz(logits) + router_plane_bytes(N, d) : logits;
 }
 
 static int router_chunk(int T, int N, int d, bool act_bf16) {
@@ -757,7 +764,7 @@ hipError_t launch_router_logits(const void* x, bool act_bf16, const float* w_rou
                                 float* partial, int T, int d, int N, hipStream_t st) {
   const int S = router_splits(T, N, d, act_bf16);
   const int KC = router_chunk(T, N, d, act_bf16);
-  if (N <= 8) {
+  if (!router_mfma(T, N, act_bf16) && N <= 8) {
     // few tokens: spread each token's K over lanes of the workgroup
     if (T <= 16) {
       dim3 grid(ceil_div(T, 16), 1, S);

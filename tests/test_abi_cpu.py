@@ -164,10 +164,10 @@ def _router_splits(T, N, d, bf16=True):
     """Number of K-splits of the router logits (restated from the library's
     sizing rule: ~1024 workgroups, at least 256 of K per split)."""
     cdiv = lambda a, b: -(-a // b)
-    if N <= 8:
-        tiles = cdiv(T, 256)
-    elif bf16:
+    if bf16 and (N > 8 or T >= 1024):   # the MFMA form: 64 x 64 tiles
         tiles = cdiv(T, 64) * cdiv(N, 64)
+    elif N <= 8:
+        tiles = cdiv(T, 256)
     else:
         tiles = cdiv(T, 32) * cdiv(N, 64)
     S = max(1, 1024 // tiles)
@@ -183,8 +183,10 @@ def test_workspace_size_formula(T, N, k, d, f, sh):
               route="sigmoid" if sh else "softmax")
     a = lambda v: (v + 255) // 256 * 256
     S = _router_splits(T, N, d)
-    # router scratch: partial logits, then (N > 8, bf16 x) the three weight planes
-    planes = a(S * T * N * 4) + (-(-d // 32)) * (-(-N // 16)) * 3 * 1024 if N > 8 else S * T * N * 4
+    # router scratch: partial logits, then (bf16 x, N > 8 or T >= 1024) the
+    # three weight planes
+    mfma = N > 8 or T >= 1024
+    planes = a(S * T * N * 4) + (-(-d // 32)) * (-(-N // 16)) * 3 * 1024 if mfma else S * T * N * 4
     want = (a(planes) + 2 * a(T * k * 4) + a(N * 4) + a((N + 1) * 4) + 2 * a(T * k * 4)
             + a(-(-T // 256) * N * 4) + a(-(-T // 16) * N * 4)
             + a(N * 4) + a((N + 1) * 4) + 2 * a(T * k * 4) + a(2048 * 4) + a(T * k * f * 2)

@@ -376,12 +376,13 @@ __device__ __forceinline__ void stream_body(const StreamParams& p, int nb0, int 
   }
 }
 
-// HOT: a routed group with more than 16 rows takes passes of 32 rows (MB =
-// 2, half the ring depth) and one with more than 32 rows passes of 64 (MB =
-// 4, a quarter of it, but 2 at most and never more than D), so the registers
-// stay within the 16-row form's, instead of streaming its weights once per 16
-// rows: with skewed routing a few hot experts hold many of the rows (on the
-// skewed fp8 decode workload this cut the gate/up time by 12%).  Each ring
+// HOT: a routed group (or a slice of the shared expert) with more than 16
+// rows takes passes of 32 rows (MB = 2, half the ring depth) and one with
+// more than 32 rows passes of 64 (MB = 4, a quarter of it, but 2 at most and
+// never more than D), so the registers stay within the 16-row form's,
+// instead of streaming its weights once per 16 rows: with skewed routing a
+// few hot experts hold many of the rows (on the skewed fp8 decode workload
+// this cut the gate/up time by 12%).  Each ring
 // depth used here divides D, and D divides the K steps, so the K loop never
 // runs past the last step.
 template <int MB, int NP, int D, int FMT, bool GATED, bool HOT, bool LDSA>
@@ -410,10 +411,12 @@ __global__ __launch_bounds__(256) void ffn_stream_kernel(StreamParams p) {
     rows = min(p.T, m_first + p.sh_rows);
   }
   if (rows <= m_first) return;
-  if (HOT && !shared && rows > 32)
+  // rows of this grid row: a routed group, or one slice of the shared expert
+  const int nrows = rows - m_first;
+  if (HOT && nrows > 32)
     stream_body<4, NP, (D >= 8 ? D / 4 : (D >= 2 ? 2 : 1)), FMT, GATED, false, LDSA && HOT>(
         p, nb0, g, shared, row_base, rows, m_first, alds, store);
-  else if (HOT && !shared && rows > 16)
+  else if (HOT && nrows > 16)
     stream_body<2, NP, (D >= 4 ? D / 2 : D), FMT, GATED, false, LDSA && HOT>(
         p, nb0, g, shared, row_base, rows, m_first, alds, store);
   else if (FMT == WF_MXFP4 && p.K % 512 == 0 &&
@@ -510,9 +513,12 @@ hipError_t launch_ffn_stream(const FfnArgs& a, int pass, int g0, int g1, int row
 
   const bool with_shared = g1 > a.N;
   const int n_routed = (g1 > a.N ? a.N : g1) - g0;
-  // the shared expert's rows are cut into slices of one pass each, run
-  // side by side (their repeated weight reads meet in L2 / MALL)
-  const int sh_rows = 16 * mb;
+  // the shared expert's rows are cut into slices of one pass each, run side
+  // by side; where the 64-row passes exist (16-row launches, not MXFP4)
+  // each slice is 64 rows, so the shared weights are streamed once per 64
+  // tokens rather than per 16 (dsv3-decode-fp8: 4 slices instead of 16)
+  const bool hot = mb == 1 && fmt != WF_MXFP4;
+  const int sh_rows = hot ? 64 : 16 * mb;
   const int sh_slices = with_shared ? ceil_div(a.T, sh_rows) : 0;
   StreamParams up{};
   up.a = a.x_rows;

@@ -590,21 +590,17 @@ __device__ __forceinline__ void four_wave_tile(const GemmParams& p, uint8_t* lds
   // where it is called)
   // The ring slots are uniform values passed through readfirstlane: opaque to
   // loop strength reduction, which would otherwise keep one address register
-  // per fragment and correct each of them every step; so a read is a lane
-  // base plus the slot plus a constant that the instruction carries.
-  // (the bf16 down pass keeps the plain arithmetic: with opaque slots it runs
-  // out of registers)
-  constexpr bool OPAQUE = FP4 || GATED;
+  // per fragment and correct each of them every step (on the MXFP4 gate/up
+  // pass 54 of its 138 vector instructions per two steps); so a read is a
+  // lane base plus the slot plus a constant that the instruction carries.
+  // The bf16 down pass keeps the plain arithmetic for its weight reads: with
+  // those opaque too it runs out of registers.
+  constexpr bool OPAQUE_B = FP4 || GATED;
   auto read_one = [&](u32x4_t (&fa)[MBW], u32x4_t (&fb)[NBW], int f, int kt, bool odd) {
     if (f < MBW) {
-      if constexpr (OPAQUE) {
-        const int slot = __builtin_amdgcn_readfirstlane(((kt >> 1) % NPA) * A_PAIR);
-        fa[f] = *reinterpret_cast<const u32x4_t*>(aring + slot + (odd ? a_rd1 : a_rd0) +
-                                                  (wm * MBW + f) * 2048);
-      } else {
-        fa[f] = *reinterpret_cast<const u32x4_t*>(aring + ((kt >> 1) % NPA) * A_PAIR +
-                                                  (wm * MBW + f) * 2048 + (odd ? a_rd1 : a_rd0));
-      }
+      const int slot = __builtin_amdgcn_readfirstlane(((kt >> 1) % NPA) * A_PAIR);
+      fa[f] = *reinterpret_cast<const u32x4_t*>(aring + slot + (odd ? a_rd1 : a_rd0) +
+                                                (wm * MBW + f) * 2048);
     } else if (FP4) {
       const int qd = kt >> 2, sub = kt & 3;
       const int j = (f - MBW) % NBW;
@@ -616,7 +612,7 @@ __device__ __forceinline__ void four_wave_tile(const GemmParams& p, uint8_t* lds
         const int slot = __builtin_amdgcn_readfirstlane((qd % NQ) * S_QUAD + sub);
         rs[FP4 ? j : 0] = *(sring + slot + (lane & 15) * 4 + (wn * NBW + j) * 256);
       }
-    } else if constexpr (OPAQUE) {
+    } else if constexpr (OPAQUE_B) {
       const int slot = __builtin_amdgcn_readfirstlane((kt % NS) * B_STEP);
       fb[f - MBW] = *reinterpret_cast<const u32x4_t*>(bring + slot + lane * 16 +
                                                       (wn * NBW + f - MBW) * 1024);

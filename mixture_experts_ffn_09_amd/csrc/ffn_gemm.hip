@@ -699,6 +699,19 @@ __device__ __forceinline__ void four_wave_tile(const GemmParams& p, uint8_t* lds
     stage(std::integral_constant<int, 1>{}, na, nb, ca, cb, kt + 1);
   }
   wait_vmcnt<0>();  // the clamped copies of the last steps
+  // Pin every accumulator to its AGPRs at the end of the loop (an empty asm
+  // statement, no instruction).  Without it the register allocator gives the
+  // down pass's MFMAs of the smaller tiles destinations other than their
+  // accumulator inputs and copies the accumulators back at every loop latch
+  // (three moves per MFMA on the 128-row down tile), apparently to suit the
+  // epilogue's read order.  The 256-accumulator tile needs no pin (and with
+  // one it spills a register).
+  if constexpr (MBW * NBW < 64) {
+#pragma unroll
+    for (int i = 0; i < MBW; ++i)
+#pragma unroll
+      for (int j = 0; j < NBW; ++j) asm volatile("" : "+a"(acc[i][j]));
+  }
 
   // Epilogue through LDS.  A lane holds 4 rows of one column of each 16 x 16
   // block; neighbouring lanes hold neighbouring columns.  Lanes 2c and 2c+1

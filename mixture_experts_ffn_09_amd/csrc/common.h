@@ -64,17 +64,17 @@ __device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-// E8M0 scale byte -> float 2^(e - 127) (e = 0 is the subnormal 2^-127);
-// e = 255 is the format's NaN
-__device__ __forceinline__ float e8m0_to_f32(uint32_t e) {
-  return __uint_as_float(e == 255u ? 0x7fc00000u : (e ? (e << 23) : 0x00400000u));
-}
-
 // 8 E2M1 codes (one 32-bit word, element 2i in the low nibble of byte i) ->
 // 8 bf16 = one MFMA operand, each times 2^(e - 127) (exact: an E2M1 value
-// times a power of two is a bf16 value)
+// times a power of two is a bf16 value; e = 0 scales by 2^-127, e = 255 is
+// the E8M0 NaN).  The conversion takes the exponent field of its float scale
+// operand as an E8M0 exponent, so the byte shifted into that field is the
+// scale as it stands: for every one of the 256 codes and all 16 E2M1 values
+// this decodes bit for bit like the float 2^(e - 127) (the subnormal 2^-127
+// for e = 0, a NaN for e = 255) on gfx950, without the selects those two
+// codes would otherwise need.
 __device__ __forceinline__ u32x4_t fp4_word_to_bf16(uint32_t q, uint32_t e) {
-  const float sc = e8m0_to_f32(e);
+  const float sc = __uint_as_float(e << 23);
   u32x4_t r;
   r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, sc, 0));
   r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, sc, 1));

@@ -653,11 +653,11 @@ __device__ __forceinline__ void four_wave_tile(const GemmParams& p, uint8_t* lds
       for (int j = 0; j < NBW; ++j) acc[i][j] = mfma16x16x32(fa[i], fb[j], acc[i][j]);
     if constexpr (FP4 && GATED) {
       // copies and operand reads between the first half of the MFMAs, the
-      // decode of the next step's weight operands (4 conversions and the
-      // scale per block) between the second half
+      // decode of the next step's weight operands (5 vector instructions per
+      // block: 4 conversions and the scale shift) between the second half
       decode(gb);
       stage_pattern<0, LPS, NRD, NMF / 2>();
-      decode_pattern<0, NBW, 8, NMF - NMF / 2>();
+      decode_pattern<0, NBW, 5, NMF - NMF / 2>();
       __builtin_amdgcn_sched_barrier(0);
     } else {
       stage_pattern<0, LPS, NRD, NMF>();

@@ -6,7 +6,7 @@ pack them with the library's pack entry point, own the workspace, and call
 from __future__ import annotations
 
 from dataclasses import dataclass, field
-from typing import Dict, Optional
+from typing import Callable, Dict, Optional
 
 import torch
 
@@ -53,8 +53,12 @@ def _act_torch(cfg: MoEConfig):
     return torch.float32 if cfg.act_dtype == "f32" else torch.bfloat16
 
 
-def build_device_layer(cfg: MoEConfig, threads: int = 16) -> DeviceLayer:
-    """Generate cfg's weights expert by expert, upload and pack them."""
+def build_device_layer(cfg: MoEConfig, threads: int = 16,
+                       edit: Optional[Callable[[int, dict], dict]] = None) -> DeviceLayer:
+    """Generate cfg's weights expert by expert, upload and pack them.
+
+    ``edit(e, weights)``, when given, may change expert e's generated
+    weights (storage format, the keys of ``make_expert``) before upload."""
     shape = moe.make_shape(cfg.T, cfg.d_model, cfg.n_experts, cfg.top_k, cfg.d_ff, cfg.n_shared,
                            cfg.route, cfg.act_dtype, cfg.w_dtype)
     dev = "cuda"
@@ -94,6 +98,8 @@ def build_device_layer(cfg: MoEConfig, threads: int = 16) -> DeviceLayer:
             t["w2_shared_scale"] = torch.empty(sr2, dtype=sdt, device=dev)
 
     def upload(e, w):
+        if edit is not None:
+            w = edit(e, w)
         shared = e == N
         g = w["gate"].to(dev, non_blocking=False)
         u = w["up"].to(dev)

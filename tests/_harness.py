@@ -49,8 +49,10 @@ def decode_weight(cfg: W.MoEConfig, w: dict, key: str) -> np.ndarray:
     return O.dequant_fp8_block(bits8(w[key]), w[key + "_scale"].numpy())
 
 
-def oracle_expert(cfg: W.MoEConfig, e: int):
+def oracle_expert(cfg: W.MoEConfig, e: int, edit=None):
     w = W.make_expert(cfg, e)
+    if edit is not None:
+        w = edit(e, w)
     return tuple(decode_weight(cfg, w, k) for k in ("gate", "up", "down"))
 
 

@@ -389,3 +389,61 @@ def test_nan_scores_rank_last(T, N, k, nan_experts, bf16_x):
     ok = ~np.isnan(ref_g)
     assert np.all(np.abs(gg[ok] - ref_g[ok]) <= 1e-5)
     assert np.isnan(ref_g).any() == (k > N - len(nan_experts))
+
+
+def _plant_scale_codes(cfg, seed):
+    """An ``edit`` for the expert weights: in every expert, some 32-element
+    blocks of each matrix get the E8M0 scale codes 0, 1 and 2 (2^-127,
+    2^-126, 2^-125: the first a denormal float32), and each routed expert's
+    down matrix gets code 255 (NaN) in one block of one row."""
+    def edit(e, w):
+        w = dict(w)
+        rng = np.random.default_rng(seed * 1000 + e)
+        for key in ("gate", "up", "down"):
+            s = w[key + "_scale"].clone()
+            R, B = s.shape
+            for code in (0, 1, 2):
+                for _ in range(3):
+                    s[int(rng.integers(R)), int(rng.integers(B))] = code
+            if key == "down" and e < cfg.n_experts:
+                s[(7 * e + 3) % R, int(rng.integers(B))] = 255
+            w[key + "_scale"] = s
+        return w
+    return edit
+
+
+@pytest.mark.parametrize("name,cfg", [
+    ("stream", H.small_config(C[1], 170, T=16, d_model=512, d_ff=1024, w_dtype="mxfp4")),
+    ("stream_shared", H.small_config(C[3], 171, T=40, d_model=256, d_ff=256, w_dtype="mxfp4")),
+    ("gemm", H.small_config(C[6], 172, T=1200, d_model=512, d_ff=1024)),
+])
+def test_mxfp4_extreme_scale_codes(name, cfg):
+    """MXFP4 weights whose E8M0 scales take the extreme codes: 0..2 decode
+    to 2^-127..2^-125 and 255 to NaN.  The layer's output is NaN exactly
+    where the oracle's is (the down rows carrying a NaN scale, for the tokens
+    routed to that expert) and equals it everywhere else."""
+    assert cfg.w_dtype == "mxfp4"
+    edit = _plant_scale_codes(cfg, cfg.index)
+    _log(f"[case] mxfp4 scale codes {name} T={cfg.T} d={cfg.d_model} N={cfg.n_experts} "
+         f"k={cfg.top_k} d_ff={cfg.d_ff}")
+    L = build_device_layer(cfg, edit=edit)
+    x = W.make_x(cfg)
+    rb = L.routing_buffers()
+    out = L.forward(x.to("cuda"), routing=rb)
+    torch.cuda.synchronize()
+    g = {k: v.cpu().numpy() for k, v in rb.items()}
+    xo = H.x_f64(cfg, x)
+    w_r, off, bias = H.oracle_router(cfg)
+    R = O.route_tokens(xo, w_r, cfg.top_k, cfg.route, off, bias)
+    ref_idx, _ = H.resolve_routing(R, g["topk_idx"], cfg.top_k)
+    ref_g = O.gate_weights(R.logits, ref_idx, cfg.route)
+    shared = H.oracle_expert(cfg, cfg.n_experts, edit) if cfg.n_shared else None
+    ref, _, _, _ = O.moe_forward_with_routing(xo, ref_idx, ref_g,
+                                              lambda e: H.oracle_expert(cfg, e, edit),
+                                              cfg.n_experts, shared)
+    got = H.to_np(out)
+    nan = np.isnan(ref)
+    assert nan.any() and not nan.all()
+    assert np.array_equal(np.isnan(got), nan)
+    err = H.assert_close(got[~nan], ref[~nan], H.TOL[cfg.w_dtype])
+    _log(f"  ok: {int(nan.sum())} NaN outputs where the oracle's are, max abs err {err[0]:.3e}")

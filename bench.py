@@ -85,15 +85,17 @@ def roofline_for(cfg, stage: dict, ms: float):
 def measured_traffic(workload: str):
     """HBM bytes per launch of the gate/up kernel from the committed rocprofv3
     counter summary (profiles/traffic_<workload>.json), or None when there is
-    none for this workload or the kernel source has changed since the
-    counters were taken."""
+    none for this workload or any source the kernel is built from (its file
+    and the headers it includes) has changed since the counters were taken."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload.replace('-', '_')}.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    src = open(os.path.join(ROOT, rec["source"]), "rb").read()
-    if hashlib.sha256(src).hexdigest() != rec["source_sha256"]:
+    if not rec.get("sources"):
         return None
+    for src, digest in rec["sources"].items():
+        if hashlib.sha256(open(os.path.join(ROOT, src), "rb").read()).hexdigest() != digest:
+            return None
     return rec["traffic_bytes_per_launch"]
 
 

@@ -81,16 +81,21 @@ def test_roofline_picks_the_bound():
     assert r["bound"] == "alu" and r["peak"] == bench.PEAK_FP32_VALU_TFLOPS
 
 
-def test_traffic_only_while_the_profiled_source_is_unchanged(tmp_path, monkeypatch):
-    src = tmp_path / "kernel.hip"
+def test_traffic_only_while_the_profiled_sources_are_unchanged(tmp_path, monkeypatch):
+    src, hdr = tmp_path / "kernel.hip", tmp_path / "common.h"
     src.write_text("// kernel v1\n")
+    hdr.write_text("// header v1\n")
     (tmp_path / "profiles").mkdir()
-    rec = {"traffic_bytes_per_launch": 12345, "source": "kernel.hip",
-           "source_sha256": hashlib.sha256(src.read_bytes()).hexdigest()}
+    rec = {"traffic_bytes_per_launch": 12345,
+           "sources": {f.name: hashlib.sha256(f.read_bytes()).hexdigest() for f in (src, hdr)}}
     (tmp_path / "profiles" / "traffic_some_workload.json").write_text(json.dumps(rec))
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     assert bench.measured_traffic("some-workload") == 12345
     assert bench.measured_traffic("other-workload") is None
+    hdr.write_text("// header v2\n")
+    assert bench.measured_traffic("some-workload") is None
+    hdr.write_text("// header v1\n")
+    assert bench.measured_traffic("some-workload") == 12345
     src.write_text("// kernel v2\n")
     assert bench.measured_traffic("some-workload") is None
 
@@ -103,7 +108,10 @@ def test_committed_traffic_files_name_existing_sources():
     for f in files:
         rec = json.load(open(os.path.join(d, f)))
         assert f[len("traffic_"):-len(".json")] in names
-        assert os.path.exists(os.path.join(ROOT, rec["source"]))
+        assert any(s.endswith(".hip") for s in rec["sources"])
+        assert any(s.endswith("common.h") for s in rec["sources"])
+        for s in rec["sources"]:
+            assert os.path.exists(os.path.join(ROOT, s))
         assert rec["traffic_bytes_per_launch"] == rec["fetched_bytes"] + rec["written_bytes"]
 
 

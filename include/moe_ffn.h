@@ -34,14 +34,18 @@
  *   - Supported types: x/out float32 or bfloat16; expert weights float32
  *     (with float32 activations), bfloat16, OCP FP8 E4M3 with one float32
  *     scale per 128x128 block, or MXFP4 (E2M1 codes, one E8M0 scale byte per
- *     32 consecutive inputs; [AIS-12] "Quantize the experts first": gpt-oss
- *     ships its experts in MXFP4) - the last three with bfloat16
+ *     32 consecutive inputs, 2^(byte - 127), byte 255 = NaN; [AIS-12]
+ *     "Quantize the experts first": gpt-oss ships its experts in MXFP4) -
+ *     the last three with bfloat16
  *     activations.  The router weight, offset and bias are always float32.
  *   - Shape limits (else MOE_ERR_UNSUPPORTED): N <= 512, k <= 64;
  *     n_shared in {0,1}; bfloat16 weights need d_model % 32 == 0 and
  *     d_ff % 32 == 0; FP8 and MXFP4 weights need d_model % 128 == 0 and
- *     d_ff % 128 == 0; bfloat16 activations need d_model % 8 == 0.  MXFP4
- *     runs through the weight-streaming kernels at every batch size.
+ *     d_ff % 128 == 0; bfloat16 activations need d_model % 8 == 0.  bfloat16,
+ *     FP8 and MXFP4 experts run through the weight-streaming kernels at
+ *     small batches and through the tiled MFMA GEMM once the routed experts
+ *     average 64 rows or more (d_model % 256 == 0 and d_ff % 128 == 0; MXFP4
+ *     also needs its operands within 32-bit offsets, else it streams).
  *     float32 weights need n_tokens * top_k <= 1048560.  Invalid values
  *     (k < 1, k > N, negative sizes, ...) are MOE_ERR_INVALID_ARG.
  *     n_tokens == 0 is a valid no-op.
